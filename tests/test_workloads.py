@@ -1,0 +1,54 @@
+"""Host-side checks of the seeded input generator and the block tables."""
+
+import numpy as np
+
+import workloads
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5, 3.0e-3], dtype=np.float32)
+    bits = workloads.f32_to_bf16_bits(x)
+    back = (bits.astype(np.uint32) << 16).view(np.float32)
+    # 1+2^-8 is a tie between 1 and 1+2^-7: even mantissa wins (1.0)
+    assert back[0] == 1.0 and back[1] == 1.0 and back[2] == 1.0 + 2 ** -6 and back[3] == 1.0
+    assert back[4] == -2.5
+    assert abs(back[5] - 3.0e-3) <= 2 ** -8 * 3.0e-3      # half an ulp (2^-7 relative)
+
+
+def test_streams_are_deterministic_and_keyed():
+    w = workloads.make("v3_b32_h128_l16384", seed=3, B=3, L=100)
+    a = w.seq_cache(1)
+    b = w.seq_cache(1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert not np.array_equal(w.seq_cache(0)[0], a[0])
+    # a shorter draw is a prefix of a longer one (same stream)
+    assert np.array_equal(w.seq_cache(1, 40)[0], a[0][:40])
+
+
+def test_block_tables_are_disjoint_and_cover_pool():
+    for name in workloads.FULL_WORKLOADS:
+        w = workloads.make(name, seed=0)
+        used = []
+        for b in range(w.B):
+            n = -(-int(w.lens[b]) // 64)
+            row = w.block_table[b]
+            assert np.all(row[:n] >= 0) and np.all(row[n:] == -1)
+            used.append(row[:n])
+        used = np.concatenate(used)
+        assert len(np.unique(used)) == len(used) == w.num_blocks
+        assert used.min() == 0 and used.max() == w.num_blocks - 1
+
+
+def test_ragged_lengths_in_range():
+    w = workloads.make("ragged_b128_h128_l1to32768", seed=0)
+    assert w.lens.min() >= 1 and w.lens.max() <= 32768
+    assert abs(w.lens.mean() - 16384.5) < 3 * 32768 / np.sqrt(12 * 128)
+
+
+def test_query_positions_and_slots():
+    w = workloads.make("causal8_b16_h128_l65544", seed=0, B=2, L=100)
+    qp = w.query_positions()
+    assert list(qp[:8]) == list(range(92, 100))
+    s = w.slots(1, np.arange(100))
+    assert len(np.unique(s)) == 100
+    assert np.all(s // 64 == np.repeat(w.block_table[1, :2], 64)[:100])
