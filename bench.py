@@ -1,0 +1,243 @@
+"""Benchmark one absorbed-MLA decode step on one MI355X.
+
+A step is the whole hot path for one batch: mla_cache_append (the B*Lq new
+tokens) -> mla_absorb_q -> mla_decode_attn (split + combine) -> mla_out_up,
+with every input already resident in HBM. The default workload is the
+128-head, 16k-context decode (B=32, H=128, L=16384, Lq=1, block tables
+randomly permuted over the pool), the configuration the >=70 %-of-roofline
+target is stated on.
+
+Prints one JSON line: throughput (tokens/s), per-call times, the attention
+call's roofline (algorithmic bytes / HIP-event duration vs 8 TB/s HBM), and
+the fp64 oracle timed on the host cores on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+ROW_BYTES = 576 * 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="v3_b32_h128_l16384")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic(w):
+    """Algorithmic bytes and flops of one attention call (and of one step)."""
+    L = w.lens.astype(np.int64)
+    rows = w.Lq * w.H
+    cache = int(L.sum()) * ROW_BYTES
+    q_bytes = w.N * w.H * 576 * 2
+    olat_bytes = w.N * w.H * 512 * 2 + w.N * w.H * 4
+    attn_bytes = cache + q_bytes + olat_bytes
+    attn_flops = int((2 * rows * L * (576 + 512)).sum())
+    return dict(cache_bytes=cache, attn_bytes=attn_bytes, attn_flops=attn_flops)
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The fp64 oracle's absorbed path, as it stands, on whole sequences of the
+    same workload until about ``budget_s`` seconds of CPU work are done."""
+    from oracle import mla as orc
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in info}))
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads, blas = len(os.sched_getaffinity(0)), "unknown"
+    f = orc.bf16_bits_to_f64
+    q_nope, q_pe = w.queries(0)
+    wuk, wuv = (f(x) for x in w.weights())
+    done_tok, spent, seqs = 0, 0.0, 0
+    for b in range(w.B):
+        ckv, kpe = w.seq_cache(b)
+        sl = slice(b * w.Lq, (b + 1) * w.Lq)
+        args = (f(q_nope[sl]), f(q_pe[sl]), f(ckv), f(kpe), wuk, wuv)
+        t0 = time.perf_counter()
+        orc.absorbed_decode(*args)
+        spent += time.perf_counter() - t0
+        done_tok += w.Lq
+        seqs += 1
+        if spent >= budget_s:
+            break
+    return {"value": done_tok / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{seqs} of {w.B} sequences of {w.name} (fp64 NumPy absorbed path, BLAS {blas}), "
+                      f"{spent:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import workloads
+    from mla_latent_cache_append_amd import native as nat
+    from mla_latent_cache_append_amd.step import DecodeStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    nat.lib()
+    dev = torch.device("cuda")
+    w = workloads.make(args.workload, seed=args.seed)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- setup (untimed): weights, paged pool filled through mla_cache_append
+    wuk, wuv = w.weights()
+    pool = torch.empty((w.num_blocks, 64, 576), dtype=torch.bfloat16, device=dev)
+    block_table = torch.from_numpy(w.block_table).to(dev)
+    seq_lens = torch.from_numpy(w.lens.astype(np.int32)).to(dev)
+    step = DecodeStep(w.H, w.B, w.Lq, pool, block_table, seq_lens, to_dev(wuk), to_dev(wuv))
+    new_ckv = np.zeros((w.N, 512), np.uint16)
+    new_kpe = np.zeros((w.N, 64), np.uint16)
+    new_slot = np.zeros(w.N, np.int64)
+    fill_events = 0.0
+    t_fill = time.perf_counter()
+    for b in range(w.B):
+        L = int(w.lens[b])
+        ckv, kpe = w.seq_cache(b)
+        hist = L - w.Lq
+        for s0 in range(0, hist, 65536):
+            s1 = min(hist, s0 + 65536)
+            p = np.arange(s0, s1)
+            c, k = to_dev(ckv[s0:s1]), to_dev(kpe[s0:s1])
+            pos = torch.from_numpy(p.astype(np.int32)).to(dev)
+            sl = torch.from_numpy(w.slots(b, p)).to(dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step.append(c, k, pos, sl)
+            e1.record()
+            e1.synchronize()
+            fill_events += e0.elapsed_time(e1)
+        for i in range(w.Lq):
+            p = L - w.Lq + i
+            n = b * w.Lq + i
+            new_ckv[n], new_kpe[n], new_slot[n] = ckv[p], kpe[p], w.slots(b, [p])[0]
+        if b % 8 == 0:
+            print(f"[bench] filled sequence {b}/{w.B}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_fill = time.perf_counter() - t_fill
+    q_nope, q_pe = w.queries(0)
+    args_step = (to_dev(new_ckv), to_dev(new_kpe), to_dev(q_nope), to_dev(q_pe),
+                 torch.from_numpy(w.query_positions()).to(dev), torch.from_numpy(new_slot).to(dev))
+    ckv_n, kpe_n, qn, qp, qpos, slot_n = args_step
+
+    # ---- timed steps; HIP events around every call on the stream the kernels run on
+    names = ("append", "absorb_q", "decode_attn", "out_up")
+
+    def one_step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        step.append(ckv_n, kpe_n, qpos, slot_n)
+        if ev is not None:
+            ev[1].record()
+        nat.mla_absorb_q(step.dims, qn, qp, qpos, step.w_uk, step.q)
+        if ev is not None:
+            ev[2].record()
+        nat.mla_decode_attn(step.dims, step.q, step.pool, step.block_table, step.seq_lens, step.Lq,
+                            step.o_lat, step.lse, step.workspace)
+        if ev is not None:
+            ev[3].record()
+        nat.mla_out_up(step.dims, step.o_lat, step.w_uv, step.o)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [] for n in names}
+    for ev in evs:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # us
+    step_us = [evs[i][0].elapsed_time(evs[i][4]) * 1e3 for i in range(args.steps)]
+    ms_per_step = wall * 1e3 / args.steps
+    med = {n: float(np.median(v)) for n, v in per.items()}
+
+    alg = algorithmic(w)
+    attn_s = med["decode_attn"] * 1e-6
+    achieved_gbps = alg["attn_bytes"] / attn_s / 1e9
+    tflops = alg["attn_flops"] / attn_s / 1e12
+    traffic = None
+    tf = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_decode_attn.json")
+    if os.path.exists(tf):
+        try:
+            t = json.load(open(tf))
+            if t.get("workload") == w.name and t.get("kernel_source_hash") == kernel_hash():
+                traffic = t.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": "absorbed-MLA decode tokens/s + latent-cache GB/s & MFMA TFLOP/s (% roofline)",
+        "value": w.N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq,
+                   "keys_per_seq": int(w.lens.max()) if w.lens.min() == w.lens.max() else "ragged",
+                   "total_keys": int(w.lens.sum()), "block_table": w.table_kind, "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved_gbps / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "mla_decode_attn (attn_split_kernel + attn_combine_kernel)",
+                     "algorithmic_bytes_per_launch": alg["attn_bytes"],
+                     "avg_launch_us": med["decode_attn"]},
+        "latent_cache_GBps": alg["cache_bytes"] / attn_s / 1e9,
+        "mfma_TFLOPs": tflops,
+        "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+        "call_us_median": med,
+        "step_us_median_events": float(np.median(step_us)),
+        "fill": {"tokens": int(w.lens.sum()) - w.N, "append_kernel_s": fill_events * 1e-3,
+                 "wall_s_incl_host_generation": t_fill},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def kernel_hash() -> str:
+    """Hash of the attention kernel source, to tie stored counter data to it."""
+    import hashlib
+    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mla_latent_cache_append_amd", "csrc", "attn.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

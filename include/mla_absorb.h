@@ -1,0 +1,163 @@
+/*
+ * libmla_absorb — weight-absorbed Multi-head Latent Attention (MLA) decode
+ * over a paged bf16 latent cache, for AMD MI355X (gfx950).
+ *
+ * Sources, cited by title and section:
+ *   [AUDIT]  llm-atlas page "DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界"
+ *   [MLA80]  CSDN page "80 行 PyTorch 从零写 DeepSeek 的 MLA"
+ *   [TRACE]  llm-atlas page "DeepSeek-V2-Lite 真实权重执行审计"
+ *
+ * One decode step of one attention layer is four calls on one stream:
+ *   mla_cache_append  -> mla_absorb_q -> mla_decode_attn -> mla_out_up
+ *
+ * Conventions shared by every call
+ *   - bf16 tensors are passed as uint16_t bit patterns; every tensor is dense
+ *     row-major with the shape given at its argument.
+ *   - Every pointer named "device" is caller-owned device memory. The library
+ *     never allocates, frees or synchronises inside these calls; all work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream) in call order.
+ *   - Return value: MLA_OK (0) or a negative mla_status. Arguments are checked
+ *     on the host before anything is enqueued; on an error nothing is enqueued.
+ *     Device-resident values (positions, slots, block ids, lengths) cannot be
+ *     checked on the host: the kernels bound-check them as stated per call so
+ *     that a bad value never reads or writes outside the buffers.
+ *   - Cache layout: pool[num_blocks][block_size=64][576] bf16, one 1,152-byte row
+ *     per token: [c_kv (512) | RoPE(k_pe) (64)] ([AUDIT] §2.4 and §6.1 MQA mode
+ *     head_dim_k = 576; [TRACE] §3.1 the [B,T,576] projection).
+ *   - A token at absolute position p of sequence b lives at slot
+ *     block_table[b][p / 64] * 64 + p % 64.
+ */
+#ifndef MLA_ABSORB_H
+#define MLA_ABSORB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, bad dims value */
+  MLA_ERR_UNSUPPORTED = -2,   /* a dims value outside what the kernels implement */
+  MLA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than mla_decode_workspace_size */
+  MLA_ERR_LAUNCH = -4,        /* the HIP runtime reported an error at launch */
+} mla_status;
+
+/* Layer shape. The kernels implement d_c = 512, d_rope = 64, d_nope = 128,
+ * d_v = 128, block_size = 64 (V2-Lite / V2 / V3 attention: [TRACE] §1.2,
+ * [MLA80] §1) and 1 <= num_heads <= 128 with num_heads % 16 == 0 for the
+ * attention call. softmax_scale is 1/sqrt(d_nope + d_rope): the naive path
+ * attends over 192-wide heads with SDPA's default scale ([MLA80] §2
+ * MLA.forward). rope_base is 10000 ([MLA80] appendix A build_rope). */
+typedef struct mla_dims {
+  int32_t num_heads;
+  int32_t d_c;
+  int32_t d_rope;
+  int32_t d_nope;
+  int32_t d_v;
+  int32_t block_size;
+  float softmax_scale;
+  float rope_base;
+} mla_dims;
+
+/* Fills `d` with the defaults above for `num_heads` heads. */
+void mla_dims_default(mla_dims* d, int32_t num_heads);
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_str(int status);
+
+/*
+ * mla_cache_append — write T new tokens into the paged latent cache.
+ * For each token j: row = [c_kv[j] | RoPE(k_pe[j], pos[j])], stored at
+ * pool slot slot_mapping[j]. RoPE rotates interleaved pairs (2i, 2i+1) by
+ * pos * rope_base^(-2i/64) ([MLA80] appendix A); the rope key is shared by all
+ * heads and cached once per token ([MLA80] §2, [AUDIT] §2.4). It is rotated
+ * once here instead of at every step ([MLA80] §2 rotates the cached k_R each
+ * forward; the score is the same because the rotation depends only on the
+ * key's own position).
+ *   c_kv          device [T][512] bf16   latent of each new token
+ *   k_pe          device [T][64]  bf16   un-rotated rope key of each new token
+ *   pos           device [T]      int32  absolute position of each token
+ *   slot_mapping  device [T]      int64  destination slot; a slot outside
+ *                                        [0, num_blocks*64) is skipped (no write)
+ *   pool          device [num_blocks][64][576] bf16, updated in place
+ * The c_kv half is copied bit-exactly; the rope half is computed with an fp64
+ * angle and rotation and rounded once to bf16 (nearest even).
+ */
+int mla_cache_append(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                     const int32_t* pos, const int64_t* slot_mapping, uint16_t* pool,
+                     int64_t num_blocks, int32_t T, void* stream);
+
+/*
+ * mla_absorb_q — absorb W_UK into the query and rotate its rope part.
+ * q[n][h] = [ W_UK[h]^T q_nope[n][h] (512) | RoPE(q_pe[n][h], pos[n]) (64) ]
+ * ([AUDIT] §2.2: q^T (W_K c) = (W_K^T q)^T c; [MLA80] §4 Path B and §5).
+ *   q_nope  device [N][H][128] bf16
+ *   q_pe    device [N][H][64]  bf16 (un-rotated)
+ *   pos     device [N] int32   absolute position of each query token
+ *   w_uk    device [H][128][512] bf16  per-head [d_nope x d_c] up-projection
+ *                               (the head's rows of nn.Linear(d_c, H*d_nope).weight)
+ *   q_out   device [N][H][576] bf16
+ * The 128-long contraction accumulates in fp32 (bf16 MFMA) and is rounded once
+ * to bf16.
+ */
+int mla_absorb_q(const mla_dims* dims, const uint16_t* q_nope, const uint16_t* q_pe,
+                 const int32_t* pos, const uint16_t* w_uk, uint16_t* q_out, int32_t N,
+                 void* stream);
+
+/*
+ * mla_decode_workspace_size — bytes of device workspace mla_decode_attn needs
+ * for B sequences of Lq queries each (partial results of the key-range splits).
+ * Pure host arithmetic; depends only on its arguments.
+ */
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t Lq);
+
+/*
+ * mla_decode_attn — latent attention over the paged cache, split over the
+ * key range and merged.
+ * For query row (b, i, h), at absolute position p = seq_lens[b] - Lq + i:
+ *   s_t   = softmax_scale * (q[:512] . C_t[:512] + q[512:] . C_t[512:]),  t <= p
+ *   o_lat = sum_t softmax(s)_t C_t[:512],   lse = log sum_t exp(s_t)
+ * where C_t is cache row t of sequence b ([AUDIT] §2.2-2.3; [MLA80] §5:
+ * content score against the shared latent, rope score against the shared
+ * k_R broadcast to every head, context formed in the 512-wide latent).
+ * seq_lens counts keys including this step's appended tokens (append precedes
+ * attend: [MLA80] §2 concatenates the cache before attending), so query i sees
+ * itself and the earlier new tokens (causal among the Lq new tokens).
+ *   q            device [B*Lq][H][576] bf16 (row n = b*Lq + i; from mla_absorb_q)
+ *   pool         device [num_blocks][64][576] bf16
+ *   block_table  device [B][max_blocks_per_seq] int32
+ *   seq_lens     device [B] int32
+ *   o_lat        device [B*Lq][H][512] bf16
+ *   lse          device [B*Lq][H] float32, or NULL
+ *   workspace    device, at least mla_decode_workspace_size(dims, B, Lq) bytes
+ * Device-value handling: a length above max_blocks_per_seq*64 or a block id
+ * outside [0, num_blocks) makes that sequence's outputs NaN (never an
+ * out-of-bounds access); a length <= 0 gives zero outputs and lse = -inf, as
+ * does a row whose position is negative.
+ * Deterministic: the split plan depends only on seq_lens, B, Lq and H, and
+ * partials are merged in a fixed order without atomics.
+ */
+int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* pool,
+                    int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t B, int32_t Lq, uint16_t* o_lat, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_out_up — expand the latent context through W_UV per head.
+ * o[n][h] = W_UV[h] o_lat[n][h]   ([AUDIT] §2.3: sum_t p_t (W_V c_t) = W_V (sum_t p_t c_t))
+ *   o_lat  device [N][H][512] bf16
+ *   w_uv   device [H][128][512] bf16  (the head's rows of nn.Linear(d_c, H*d_v).weight)
+ *   o      device [N][H][128] bf16
+ * fp32 accumulation (bf16 MFMA), one rounding to bf16.
+ */
+int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o,
+               int32_t N, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_ABSORB_H */

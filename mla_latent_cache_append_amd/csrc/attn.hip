@@ -1,0 +1,682 @@
+// mla_decode_attn: split-KV flash-decode over the paged 576-wide latent cache.
+//
+// What is computed ([AUDIT] = llm-atlas page "DeepSeek MLA 吸收式缓存：真实权重
+// 执行与 FlashMLA 架构边界", §2.2-2.3; [MLA80] = CSDN page "80 行 PyTorch 从零写
+// DeepSeek 的 MLA", §5): for each query row (absorbed content query q_lat and
+// rotated rope query q_r, packed as 576 bf16) and the cache rows C_t =
+// [c_kv | k_r] of its sequence,
+//   s_t = scale * (q . C_t)              over all 576 features,
+//   o_lat = sum_t softmax(s)_t C_t[:512]
+// with causal visibility t <= position of the query.
+//
+// Design for gfx950:
+//  * One cache block (64 tokens x 1,152 B = 72 KiB, contiguous in HBM) is the
+//    tile. It is copied global -> LDS with direct 16-byte loads (no VGPR
+//    staging), double-buffered (144 KiB of the 160 KiB LDS), 1 KiB per wave
+//    instruction, fully coalesced.
+//  * Every query row that shares the sequence reuses each tile: the tile is the
+//    shared K (all 576 columns) and V (first 512 columns), one latent for all
+//    heads ([AUDIT] §2.4; [MLA80] §5 "共享 k_r 广播到各 head").
+//  * Scores are computed transposed, S^T = K Q^T, with the K tile as the MFMA A
+//    operand (8 consecutive features of one token: one 16-byte LDS read) and
+//    Q in registers. The S^T accumulator leaves each lane holding scores of
+//    one query row, so the softmax row statistics need only two cross-lane
+//    steps and the probabilities feed the PV product straight from registers.
+//  * The context is accumulated transposed, O^T = V^T P^T, with V^T read by
+//    ds_read_b64_tr_b16 from the same row-major tile, and the K dimension of
+//    the PV product permuted to match the token order the S^T layout gives.
+//  * LDS tile layout: row-major 72 chunks of 16 B per token, chunk index XOR
+//    ((token >> 1) & 7). Both the K reads and the transposed V reads are then
+//    free of bank conflicts.
+//  * Split-KV is stream-K style: the tiles of all sequences form one line that
+//    is cut into `width` equal ranges, one per workgroup, so ragged batches are
+//    balanced exactly. A range that covers a whole sequence writes the final
+//    o_lat; otherwise it writes (m, l, acc) partials that the combine kernel
+//    merges in a fixed order (deterministic, no atomics).
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+// ------------------------------------------------------------------ plan
+
+constexpr int TARGET_WGS = 256;   // one workgroup per CU on a 256-CU MI355X
+
+__device__ __forceinline__ int tiles_of(int L, int max_blocks) {
+  L = max(L, 0);
+  L = min(L, max_blocks * BLOCK);
+  return (L + BLOCK - 1) / BLOCK;
+}
+
+// Wave-uniform values made explicit (SGPRs, scalar branches).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
+// Total tiles over all sequences (wave-uniform).
+__device__ int64_t plan_total_tiles(const int32_t* seq_lens, int B, int max_blocks) {
+  const int lane = threadIdx.x & 63;
+  int64_t total = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    total += wave_sum_i(b < B ? tiles_of(seq_lens[b], max_blocks) : 0);
+  }
+  return uni64(total);
+}
+
+// First sequence b whose tile range [S_b, S_b + tiles_b) contains tile x.
+// Returns b (or B if none) and S_b (wave-uniform).
+__device__ void plan_find(const int32_t* seq_lens, int B, int max_blocks, int64_t x, int& b_out,
+                          int64_t& start_out) {
+  const int lane = threadIdx.x & 63;
+  int64_t base_sum = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    const int t = b < B ? tiles_of(seq_lens[b], max_blocks) : 0;
+    int incl = t;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const uint64_t hit = __ballot(b < B && base_sum + incl > x);
+    if (hit) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int incl_src = __shfl(incl, src);
+      const int t_src = __shfl(t, src);
+      b_out = uni(base + src);
+      start_out = uni64(base_sum + incl_src - t_src);
+      return;
+    }
+    base_sum += uni(__shfl(incl, 63));
+  }
+  b_out = B;
+  start_out = uni64(base_sum);
+}
+
+// Workgroup of range w (0..width-1) that holds tile x of the line of T tiles,
+// where range w is [floor(w T / width), floor((w+1) T / width)).
+__device__ __forceinline__ int plan_owner(int64_t x, int64_t T, int width) {
+  return (int)(((x + 1) * (int64_t)width - 1) / T);
+}
+
+// ------------------------------------------------------------------ kernel
+
+struct AttnArgs {
+  const uint16_t* q;            // [B*rows][576]   (row (b, r) = b*rows + r)
+  const uint16_t* pool;         // [num_blocks][64][576]
+  const int32_t* block_table;   // [B][max_blocks]
+  const int32_t* seq_lens;      // [B]
+  uint16_t* o_lat;              // [B*rows][512]
+  float* lse;                   // [B*rows] or null
+  float* ws_ml;                 // [slots][rows][2]
+  float* ws_acc;                // [slots][rows][512]
+  int64_t num_blocks;
+  int max_blocks;
+  int B, Lq, H, rows;
+  int n_rg, width;
+  float scale_log2;             // softmax scale * log2(e)
+};
+
+constexpr int TILE_BYTES = BLOCK_BYTES;          // 73,728
+constexpr int TILE_CHUNKS = BLOCK * ROW_CHUNKS;  // 4,608 sixteen-byte chunks
+constexpr int KSTEPS = D_K / 32;                 // 18 MFMA k-steps over 576 features
+constexpr float LN2 = 0.69314718055994530942f;
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// LDS tile layout (blocked): chunks of 16 B ordered [tg 8][cg 9][tl 8][cl 8] for
+// token t = 8 tg + tl and feature chunk c = 8 cg + cl (8 bf16 features), with
+// cl stored XOR swz(t). One 1-KiB direct-load instruction fills one
+// (tg, cg) block: 8 tokens x one 128-byte line each. swz spreads the 16 tokens
+// a 16-lane group reads over all 16 bank groups, so both the K reads and the
+// transposed V reads are conflict-free.
+__device__ __forceinline__ int swz(int t) { return ((t & 7) >> 1) | (((t >> 3) & 1) << 2); }
+
+__device__ __forceinline__ uint32_t lds_chunk_off(int t, int c) {
+  return (uint32_t)((((t >> 3) * 9 + (c >> 3)) * 64 + (t & 7) * 8 + ((c & 7) ^ swz(t))) * 16);
+}
+
+// Copy one cache block into an LDS tile buffer; wave w issues the 72 / NW
+// instructions j = w*72/NW .. (w+1)*72/NW - 1. Buffer loads with an LDS
+// destination: the per-lane offset is one of two VGPRs, the per-instruction
+// offset an SGPR, and the hardware bound-checks every lane against the
+// descriptor's size. The size covers only the block's first n_valid tokens:
+// rows past the end of the sequence (never written, arbitrary bits) arrive as
+// zeros, so a masked probability of 0 never meets a NaN in the PV product.
+template <int NW>
+__device__ __forceinline__ void load_tile(const uint16_t* pool, int blk, int n_valid, lds_char* dst,
+                                          int wave, const uint32_t (&goff_lane)[2]) {
+  constexpr int PER_WAVE = (BLOCK / 8) * 9 / NW;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)pool + (int64_t)blk * TILE_BYTES), (short)0, n_valid * ROW_BYTES, 0x00020000);
+#pragma unroll
+  for (int jj = 0; jj < PER_WAVE; ++jj) {
+    const int j = wave * PER_WAVE + jj;
+    const int tg = j / 9, cg = j - 9 * (j / 9);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + j * 1024), 16, goff_lane[tg & 1],
+                                             tg * 8 * ROW_BYTES + cg * 128, 0, 0);
+  }
+}
+
+// Rows are rescaled only when their running max grows by more than this many
+// log2 units, so probabilities stay below 2^8 (exact range for bf16 and fp32)
+// and the accumulators are touched outside the MFMAs only on rare tiles.
+constexpr float RESCALE_LOG2 = 8.f;
+
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Online-softmax update of RB row blocks from this tile's scores, given as the
+// 16 (NK = 2 k-blocks x 8) values per lane in PV k-slot order. Returns the
+// packed bf16 probabilities. NCB accumulators per row block are rescaled only
+// when some lane's max moved by more than RESCALE_LOG2.
+template <int RB, int NCB>
+__device__ __forceinline__ void softmax_update(float (&pv)[RB][2][8], float (&m_run)[RB],
+                                               float (&l_run)[RB], f32x4 (&o)[RB][NCB],
+                                               bf16x8 (&pf)[RB][2]) {
+  float mx[RB];
+  bool need = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float v = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v = fmaxf(v, pv[rb][kb][j]);
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    mx[rb] = v;
+    need |= v > m_run[rb] + RESCALE_LOG2;
+  }
+  if (__any(need)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (mx[rb] > m_run[rb] + RESCALE_LOG2) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - mx[rb]);  // 0 when m_run = -inf
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) o[rb][cb] *= alpha;
+        m_run[rb] = mx[rb];
+      }
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float m_ref = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 pk;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(pv[rb][kb][j] - m_ref);
+        psum += p;
+        pk[j] = (__bf16)p;
+      }
+      pf[rb][kb] = pk;
+    }
+    l_run[rb] += psum;
+  }
+}
+
+// O^T[col][row] += V^T[col][token] P^T[token][row] over the 64 tokens of the
+// tile for the column blocks cb0 .. cb0 + NCB - 1.
+template <int RB, int NCB>
+__device__ __forceinline__ void pv_product(lds_char* cur, const uint32_t (&vbase)[4], int cb0,
+                                           const bf16x8 (&pf)[RB][2], f32x4 (&o)[RB][NCB]) {
+  auto read_v = [&](int cbg, int kb) -> bf16x8 {
+    lds_char* vrow = cur + vbase[cbg & 3];
+    const i16x4 v0 = lds_read_tr16_b64(vrow, kb * 36864 + (cbg >> 2) * 1024);
+    const i16x4 v1 = lds_read_tr16_b64(vrow, kb * 36864 + 18432 + (cbg >> 2) * 1024);
+    return join_tr(v0, v1);
+  };
+  bf16x8 vn[2] = {read_v(cb0, 0), read_v(cb0, 1)};
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const bf16x8 vc[2] = {vn[0], vn[1]};
+    if (cb + 1 < NCB) {
+      vn[0] = read_v(cb0 + cb + 1, 0);
+      vn[1] = read_v(cb0 + cb + 1, 1);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][cb] = mfma16x16x32(vc[kb], pf[rb][kb], o[rb][cb]);
+    __builtin_amdgcn_sched_barrier(0);  // one column block of fragments in flight
+  }
+}
+
+// Scale scores to log2 units and, on tiles that reach past the first query's
+// position, mask keys beyond each row's limit. Score (rb, tb, i) belongs to
+// token 16 tok_block(tb) + 4g + i of the tile.
+template <int RB, int NTB, bool MASK>
+__device__ __forceinline__ void scale_mask(f32x4 (&s)[RB][NTB], float scale_log2, int key0,
+                                           int tok_block0, int g, const int (&lim)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = s[rb][tb][i] * scale_log2;
+        if (MASK && key0 + 16 * (tok_block0 + tb) + 4 * g + i > lim[rb]) v = -INFINITY;
+        s[rb][tb][i] = v;
+      }
+}
+
+// Row split, one tile: each wave scores its RB*16 rows against all 64 tokens
+// and accumulates all 512 columns.
+template <int RB, bool MASK>
+__device__ __forceinline__ void rows_tile(lds_char* cur, const bf16x8 (&qf)[RB][KSTEPS],
+                                          f32x4 (&o)[RB][32], float (&m_run)[RB],
+                                          float (&l_run)[RB], const int (&lim)[RB], int key0,
+                                          float scale_log2, const uint32_t (&kbase)[2],
+                                          const uint32_t (&vbase)[4], int g) {
+  f32x4 s[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) s[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // S^T = K Q^T, two token blocks at a time, K fragments prefetched one k-step ahead
+#pragma unroll
+  for (int tbp = 0; tbp < 2; ++tbp) {
+    u32x4 kn[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) kn[e] = lds_read_b128(cur + kbase[0], (2 * tbp + e) * 18432);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4 kc[2] = {kn[0], kn[1]};
+      if (ks + 1 < KSTEPS) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          kn[e] = lds_read_b128(cur + kbase[(ks + 1) & 1], (2 * tbp + e) * 18432 + ((ks + 1) >> 1) * 1024);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          s[rb][2 * tbp + e] = mfma16x16x32(as_bf16x8(kc[e]), qf[rb][ks], s[rb][2 * tbp + e]);
+      __builtin_amdgcn_sched_barrier(0);  // one k-step of fragments in flight
+    }
+  }
+  scale_mask<RB, 4, MASK>(s, scale_log2, key0, 0, g, lim);
+  float pv[RB][2][8];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[rb][kb][i] = s[rb][2 * kb][i];
+        pv[rb][kb][4 + i] = s[rb][2 * kb + 1][i];
+      }
+  bf16x8 pf[RB][2];
+  softmax_update<RB, 32>(pv, m_run, l_run, o, pf);
+  pv_product<RB, 32>(cur, vbase, 0, pf, o);
+}
+
+// Column split, one tile: wave w scores tokens 16w..16w+15 for all RB*16 rows,
+// shares the scores through LDS, and accumulates columns 128w..128w+127.
+template <int RB, bool MASK>
+__device__ __forceinline__ void cols_tile(lds_char* cur, __attribute__((address_space(3))) float* sbuf,
+                                          const bf16x8 (&qf)[RB][KSTEPS], f32x4 (&o)[RB][8],
+                                          float (&m_run)[RB], float (&l_run)[RB],
+                                          const int (&lim)[RB], int key0, float scale_log2,
+                                          const uint32_t (&kbase)[2], const uint32_t (&vbase)[4],
+                                          int wave, int g, int c16) {
+  constexpr int SB = 68;  // padded score-buffer row (floats)
+  f32x4 s[RB][1];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) s[rb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 kn = lds_read_b128(cur + kbase[0], 0);
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const u32x4 kc = kn;
+    if (ks + 1 < KSTEPS) kn = lds_read_b128(cur + kbase[(ks + 1) & 1], ((ks + 1) >> 1) * 1024);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s[rb][0] = mfma16x16x32(as_bf16x8(kc), qf[rb][ks], s[rb][0]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  scale_mask<RB, 1, MASK>(s, scale_log2, key0, wave, g, lim);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    *(__attribute__((address_space(3))) f32x4*)(sbuf + (rb * 16 + c16) * SB + 16 * wave + 4 * g) = s[rb][0];
+  __syncthreads();
+  float pv[RB][2][8];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(
+            sbuf + (rb * 16 + c16) * SB + 32 * kb + 16 * h2 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[rb][kb][4 * h2 + i] = v[i];
+      }
+  bf16x8 pf[RB][2];
+  softmax_update<RB, 8>(pv, m_run, l_run, o, pf);
+  pv_product<RB, 8>(cur, vbase, 8 * wave, pf, o);
+}
+
+// RB : 16-row MFMA blocks of query rows per wave.
+// CS : false = row split (4 waves x RB*16 rows, all tokens, all columns);
+//      true  = column split (4 waves share RB*16 rows; see cols_tile).
+template <int RB, bool CS>
+__global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
+  constexpr int NW = 4;
+  constexpr int RG = CS ? RB * 16 : NW * RB * 16;  // rows per workgroup
+  constexpr int NCB = CS ? 8 : 32;                 // 16-column blocks per wave
+  constexpr int SB_BYTES = CS ? RB * 16 * 68 * 4 : 0;
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_BYTES + SB_BYTES];
+  lds_char* tiles = (lds_char*)smem;
+  __attribute__((address_space(3))) float* sbuf =
+      (__attribute__((address_space(3))) float*)(tiles + 2 * TILE_BYTES);
+
+  const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+
+  // ---- which (row group, range) this workgroup owns
+  int unit = blockIdx.x;
+  if (a.n_rg > 1) {
+    // Put the row groups of one range on one XCD (workgroup ids are dealt to
+    // the 8 XCDs round-robin) so their reads of the same tiles share its L2.
+    const int full = (int)(gridDim.x / 64) * 64;
+    if (unit < full) {
+      const int loc = unit & 63;
+      unit = (unit & ~63) + (loc & 7) * 8 + (loc >> 3);
+    }
+  }
+  const int w = unit / a.n_rg;
+  const int rg = unit - w * a.n_rg;
+
+  const int64_t T = plan_total_tiles(a.seq_lens, a.B, a.max_blocks);
+  if (T == 0) return;
+  const int64_t x_begin = (int64_t)w * T / a.width;
+  const int64_t x_end = (int64_t)(w + 1) * T / a.width;
+  if (x_begin >= x_end) return;
+
+  int b;
+  int64_t seq_start;
+  plan_find(a.seq_lens, a.B, a.max_blocks, x_begin, b, seq_start);
+
+  const int row_base = rg * RG + (CS ? 0 : wave * RB * 16);  // first row of this wave
+
+  // Per-lane parts of every LDS / global tile offset; the rest are immediates.
+  uint32_t goff_lane[2];
+#pragma unroll
+  for (int odd = 0; odd < 2; ++odd) {
+    const int tl = lane >> 3;
+    goff_lane[odd] = (uint32_t)(tl * ROW_BYTES + ((lane & 7) ^ ((tl >> 1) | (odd << 2))) * 16);
+  }
+  // K fragment (token 16 tb + c16, chunk 4 ks + g) = kbase[ks & 1] + tb*18432 + (ks >> 1)*1024
+  const int ktok = c16 + (CS ? 16 * wave : 0);
+  const uint32_t kbase[2] = {lds_chunk_off(ktok, g), lds_chunk_off(ktok, 4 + g)};
+  // V^T fragment (token 32 kb + 16 h + 4g + c16/4, column 16 cb + 4 (c16 % 4)) =
+  //   vbase[cb & 3] + kb*36864 + h*18432 + (cb >> 2)*1024
+  uint32_t vbase[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+    vbase[q4] = lds_chunk_off(4 * g + (c16 >> 2), 2 * q4 + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
+
+  int64_t x = x_begin;
+  while (x < x_end && b < a.B) {
+    const int L = uni(a.seq_lens[b]);
+    const int ntiles = tiles_of(L, a.max_blocks);
+    const int64_t seg_end = min(x_end, seq_start + ntiles);
+    const int k_first = (int)(x - seq_start);
+    const int k_last = (int)(seg_end - seq_start);  // exclusive
+    const bool whole = (x == seq_start) && (seg_end == seq_start + ntiles);
+    bool bad = L > a.max_blocks * BLOCK;
+    const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks;
+    {
+      const int blk = uni(bt[k_first]);
+      if (blk < 0 || blk >= a.num_blocks) bad = true;
+      else load_tile<NW>(a.pool, blk, min(BLOCK, L - k_first * BLOCK), tiles, wave, goff_lane);
+    }
+
+    // ---- query fragments: B operand of S^T (lane: row c16, features 32ks + 8g .. +7)
+    bf16x8 qf[RB][KSTEPS];
+    int lim[RB];
+    float m_run[RB], l_run[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = row_base + rb * 16 + c16;
+      const bool valid = r < a.rows;
+      const uint16_t* qrow = a.q + ((int64_t)b * a.rows + (valid ? r : 0)) * D_K + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        u32x4 v = *(const u32x4*)(qrow + 32 * ks);
+        if (!valid) v = u32x4{0u, 0u, 0u, 0u};
+        qf[rb][ks] = as_bf16x8(v);
+      }
+      // query i of this row sits at position L - Lq + i and sees keys <= it
+      lim[rb] = valid ? L - a.Lq + r / a.H : -1;
+      m_run[rb] = -INFINITY;
+      l_run[rb] = 0.f;
+    }
+    f32x4 o[RB][NCB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) o[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Tiles [k_first, k_mask) hold only keys every row may see; later tiles
+    // need the causal / length mask. Two loops keep the mask out of the main one.
+    const int k_mask = max(k_first, min(k_last, max(0, L - a.Lq + 1) / BLOCK));
+    auto step = [&](int k) -> lds_char* {
+      wait_vmem();
+      __syncthreads();
+      if (k + 1 < k_last) {
+        const int blk = uni(bt[k + 1]);
+        if (blk < 0 || blk >= a.num_blocks) bad = true;
+        else
+          load_tile<NW>(a.pool, blk, min(BLOCK, L - (k + 1) * BLOCK),
+                        tiles + ((k + 1 - k_first) & 1) * TILE_BYTES, wave, goff_lane);
+      }
+      return tiles + ((k - k_first) & 1) * TILE_BYTES;
+    };
+    for (int k = k_first; k < k_mask; ++k) {
+      lds_char* cur = step(k);
+      if constexpr (CS)
+        cols_tile<RB, false>(cur, sbuf, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, wave, g, c16);
+      else
+        rows_tile<RB, false>(cur, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, g);
+    }
+    for (int k = k_mask; k < k_last; ++k) {
+      lds_char* cur = step(k);
+      if constexpr (CS)
+        cols_tile<RB, true>(cur, sbuf, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, wave, g, c16);
+      else
+        rows_tile<RB, true>(cur, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, g);
+    }
+
+    // ---- finish the segment: row sums across the 4 lanes of each row
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      l_run[rb] += __shfl_xor(l_run[rb], 16);
+      l_run[rb] += __shfl_xor(l_run[rb], 32);
+    }
+    const int slot = w + b;
+    const int cb0 = CS ? wave * NCB : 0;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = row_base + rb * 16 + c16;
+      if (r >= a.rows) continue;
+      const int64_t orow = (int64_t)b * a.rows + r;
+      if (whole) {
+        const float inv = l_run[rb] > 0.f ? 1.f / l_run[rb] : 0.f;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          f32x4 v = o[rb][cb] * inv;
+          if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+          const u32x2 out = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *(u32x2*)(a.o_lat + orow * D_C + 16 * (cb0 + cb) + 4 * g) = out;
+        }
+        if (a.lse && g == 0 && (!CS || wave == 0)) {
+          float lv = l_run[rb] > 0.f ? (m_run[rb] + __log2f(l_run[rb])) * LN2 : -INFINITY;
+          if (bad) lv = NAN;
+          a.lse[orow] = lv;
+        }
+      } else {
+        const int64_t prow = (int64_t)slot * a.rows + r;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          f32x4 v = o[rb][cb];
+          if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+          *(f32x4*)(a.ws_acc + prow * D_C + 16 * (cb0 + cb) + 4 * g) = v;
+        }
+        if (g == 0 && (!CS || wave == 0)) {
+          a.ws_ml[prow * 2 + 0] = bad ? NAN : m_run[rb];
+          a.ws_ml[prow * 2 + 1] = bad ? NAN : l_run[rb];
+        }
+      }
+    }
+
+    // ---- next sequence with tiles
+    x = seg_end;
+    seq_start += ntiles;
+    ++b;
+    while (b < a.B && tiles_of(uni(a.seq_lens[b]), a.max_blocks) == 0) ++b;
+    __syncthreads();  // every wave is done with the tile buffers and sbuf
+  }
+}
+
+// Merge the partials of each query row in range order. One wave per row,
+// 8 output columns per lane.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x;
+  const int r = blockIdx.y * 4 + wave;
+  if (r >= a.rows) return;
+  const int64_t T = plan_total_tiles(a.seq_lens, a.B, a.max_blocks);
+  const int ntiles = tiles_of(a.seq_lens[b], a.max_blocks);
+  const int64_t orow = (int64_t)b * a.rows + r;
+  uint16_t* out = a.o_lat + orow * D_C + 8 * lane;
+  if (ntiles == 0) {
+    *(u32x4*)out = u32x4{0u, 0u, 0u, 0u};
+    if (a.lse && lane == 0) a.lse[orow] = -INFINITY;
+    return;
+  }
+  // start of sequence b on the tile line: tiles of sequences before it
+  int64_t start = 0;
+  for (int base = 0; base < b; base += 64) {
+    const int bb = base + lane;
+    start += wave_sum_i(bb < b ? tiles_of(a.seq_lens[bb], a.max_blocks) : 0);
+  }
+  const int w_lo = plan_owner(start, T, a.width);
+  const int w_hi = plan_owner(start + ntiles - 1, T, a.width);
+  if (w_lo == w_hi) return;  // one range held the whole sequence and wrote it
+
+  // Ranges between w_lo and w_hi all lie inside sequence b, except empty ones
+  // (more workgroups than tiles), which wrote nothing and are skipped.
+  auto empty = [&](int w) { return (int64_t)w * T / a.width == (int64_t)(w + 1) * T / a.width; };
+  float M = -INFINITY;
+  for (int w = w_lo; w <= w_hi; ++w)
+    if (!empty(w)) M = fmaxf(M, a.ws_ml[((int64_t)(w + b) * a.rows + r) * 2]);
+  const float Mref = M == -INFINITY ? 0.f : M;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int w = w_lo; w <= w_hi; ++w) {
+    if (empty(w)) continue;
+    const int64_t prow = (int64_t)(w + b) * a.rows + r;
+    const float m_k = a.ws_ml[prow * 2], l_k = a.ws_ml[prow * 2 + 1];
+    const float wt = __builtin_amdgcn_exp2f(m_k - Mref);
+    l += wt * l_k;
+    const f32x4* src = (const f32x4*)(a.ws_acc + prow * D_C + 8 * lane);
+    const f32x4 v0 = src[0], v1 = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] += wt * v0[i];
+      acc[4 + i] += wt * v1[i];
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  *(u32x4*)out = o;
+  if (a.lse && lane == 0) a.lse[orow] = l > 0.f ? (M + __log2f(l)) * LN2 : (l != l ? NAN : -INFINITY);
+}
+
+// ------------------------------------------------------------------ host side
+
+enum { V_ROWS128 = 0, V_ROWS64 = 1, V_COLS32 = 2, V_COLS16 = 3 };
+
+AttnPlan plan_attention(int32_t B, int32_t Lq, int32_t H) {
+  (void)B;
+  AttnPlan p;
+  const int rows = Lq * H;
+  if (rows >= 48) { p.variant = V_ROWS64; p.rg_rows = 64; }
+  else if (rows >= 32) { p.variant = V_COLS32; p.rg_rows = 32; }
+  else { p.variant = V_COLS16; p.rg_rows = 16; }
+  p.n_rg = (rows + p.rg_rows - 1) / p.rg_rows;
+  p.width = (TARGET_WGS + p.n_rg - 1) / p.n_rg;
+  return p;
+}
+
+size_t attention_workspace_bytes(int32_t B, int32_t Lq, int32_t H) {
+  const AttnPlan p = plan_attention(B, Lq, H);
+  const size_t slots = (size_t)p.width + (size_t)B;
+  const size_t rows = (size_t)Lq * (size_t)H;
+  return slots * rows * (2 + D_C) * sizeof(float);
+}
+
+hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t num_blocks,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
+                              float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
+                              hipStream_t stream) {
+  const AttnPlan p = plan_attention(B, Lq, H);
+  AttnArgs a;
+  a.q = q;
+  a.pool = pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o_lat = o_lat;
+  a.lse = lse;
+  const size_t slots = (size_t)p.width + (size_t)B;
+  a.ws_ml = (float*)workspace;
+  a.ws_acc = a.ws_ml + slots * (size_t)Lq * H * 2;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks;
+  a.B = B;
+  a.Lq = Lq;
+  a.H = H;
+  a.rows = Lq * H;
+  a.n_rg = p.n_rg;
+  a.width = p.width;
+  a.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  const dim3 grid(p.width * p.n_rg);
+  switch (p.variant) {
+    case V_ROWS64:
+      hipLaunchKernelGGL((attn_split_kernel<1, false>), grid, dim3(256), 0, stream, a);
+      break;
+    case V_COLS32:
+      hipLaunchKernelGGL((attn_split_kernel<2, true>), grid, dim3(256), 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((attn_split_kernel<1, true>), grid, dim3(256), 0, stream, a);
+      break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(B, (a.rows + 3) / 4), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

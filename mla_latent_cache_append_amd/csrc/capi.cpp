@@ -1,0 +1,107 @@
+// C ABI of libmla_absorb: argument checks on the host, then kernel launches on
+// the caller's stream. Declarations and their contracts: include/mla_absorb.h.
+#include "../../include/mla_absorb.h"
+
+#include <math.h>
+
+#include "kernels.h"
+
+namespace {
+
+int check_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_INVALID_ARG;
+  if (d->num_heads <= 0 || !(d->softmax_scale > 0.f) || !isfinite(d->softmax_scale) ||
+      !(d->rope_base > 1.f) || !isfinite(d->rope_base))
+    return MLA_ERR_INVALID_ARG;
+  if (d->d_c != mla::D_C || d->d_rope != mla::D_ROPE || d->d_nope != mla::D_NOPE ||
+      d->d_v != mla::D_V || d->block_size != mla::BLOCK || d->num_heads > 128)
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+void mla_dims_default(mla_dims* d, int32_t num_heads) {
+  if (!d) return;
+  d->num_heads = num_heads;
+  d->d_c = mla::D_C;
+  d->d_rope = mla::D_ROPE;
+  d->d_nope = mla::D_NOPE;
+  d->d_v = mla::D_V;
+  d->block_size = mla::BLOCK;
+  d->softmax_scale = (float)(1.0 / sqrt((double)(mla::D_NOPE + mla::D_ROPE)));
+  d->rope_base = 10000.f;
+}
+
+const char* mla_status_str(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dimensions";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mla_cache_append(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                     const int32_t* pos, const int64_t* slot_mapping, uint16_t* pool,
+                     int64_t num_blocks, int32_t T, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!c_kv || !k_pe || !pos || !slot_mapping || !pool || num_blocks <= 0 || T <= 0)
+    return MLA_ERR_INVALID_ARG;
+  return launch_status(mla::launch_cache_append(c_kv, k_pe, pos, slot_mapping, pool, num_blocks, T,
+                                                (double)dims->rope_base, (hipStream_t)stream));
+}
+
+int mla_absorb_q(const mla_dims* dims, const uint16_t* q_nope, const uint16_t* q_pe,
+                 const int32_t* pos, const uint16_t* w_uk, uint16_t* q_out, int32_t N,
+                 void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !q_pe || !pos || !w_uk || !q_out || N <= 0) return MLA_ERR_INVALID_ARG;
+  return launch_status(mla::launch_absorb_q(q_nope, q_pe, pos, w_uk, q_out, N, dims->num_heads,
+                                            (double)dims->rope_base, (hipStream_t)stream));
+}
+
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t Lq) {
+  if (check_dims(dims) != MLA_OK || B <= 0 || Lq <= 0) return 0;
+  return mla::attention_workspace_bytes(B, Lq, dims->num_heads);
+}
+
+int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* pool,
+                    int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t B, int32_t Lq, uint16_t* o_lat, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (dims->num_heads % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  if (!q || !pool || !block_table || !seq_lens || !o_lat || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || B <= 0 || Lq <= 0)
+    return MLA_ERR_INVALID_ARG;
+  // rows of one sequence index 32-bit offsets inside the kernels
+  if ((int64_t)Lq * dims->num_heads > (1 << 20) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
+    return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla::attention_workspace_bytes(B, Lq, dims->num_heads);
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  return launch_status(mla::launch_decode_attn(q, pool, num_blocks, block_table, max_blocks_per_seq,
+                                               seq_lens, B, Lq, dims->num_heads,
+                                               dims->softmax_scale, o_lat, lse, workspace,
+                                               (hipStream_t)stream));
+}
+
+int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o,
+               int32_t N, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!o_lat || !w_uv || !o || N <= 0) return MLA_ERR_INVALID_ARG;
+  return launch_status(
+      mla::launch_out_up(o_lat, w_uv, o, N, dims->num_heads, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Device-side helpers shared by the libmla_absorb kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned int))));
+typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp64 -> bf16 with a single rounding (nearest even) for normal-range values:
+// round the 52-bit mantissa to 7 bits in the double itself, after which the
+// value is exact in fp32 and its top 16 bits are the bf16 pattern.
+__device__ __forceinline__ uint16_t f64_to_bf16(double d) {
+  uint64_t u = (uint64_t)__double_as_longlong(d);
+  if ((u & 0x7fffffffffffffffull) > 0x7ff0000000000000ull) return 0x7fc0u;
+  const uint64_t lsb = (u >> 45) & 1ull;
+  u += 0x00000fffffffffffull + lsb;
+  u &= ~((1ull << 45) - 1ull);
+  const float f = (float)__longlong_as_double((long long)u);
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- MFMA
+//
+// v_mfma_f32_16x16x32_bf16, lane l, g = l / 16, c = l % 16:
+//   A (16x32, MxK): a[j] = A[c][8g + j]      j = 0..7
+//   B (32x16, KxN): b[j] = B[8g + j][c]
+//   D (16x16):      d[i] = D[4g + i][c]      i = 0..3
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- LDS
+
+// 16 bytes from LDS at a byte offset of an LDS base pointer.
+__device__ __forceinline__ u32x4 lds_read_b128(const __attribute__((address_space(3))) char* base,
+                                               uint32_t off) {
+  return *(const __attribute__((address_space(3))) u32x4*)(base + off);
+}
+
+// Transposing 64-bit LDS read (ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane i supplies the address of 4 consecutive 16-bit elements; lane n
+// of the group receives element n % 4 of the loads of lanes n / 4, 4 + n / 4,
+// 8 + n / 4 and 12 + n / 4. With lane i loading row i / 4, columns 4 (i % 4)
+// .. +3 of a row-major [row][16 col] block, lane n receives column n of rows
+// 0..3: the transpose an MFMA operand needs when its K dimension is the
+// row-major one.
+__device__ __forceinline__ i16x4 lds_read_tr16_b64(const __attribute__((address_space(3))) char* base,
+                                                   uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + off));
+}
+
+// Global -> LDS direct copy of 16 bytes per lane: lane l's 16 bytes land at
+// lds_wave_base + 16 * l (lds_wave_base is wave-uniform).
+__device__ __forceinline__ void global_load_lds_16(const void* gptr, lds_void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gptr, lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+}  // namespace mla

@@ -1,0 +1,53 @@
+// Host-side launch entry points of the libmla_absorb kernels. Each function
+// enqueues its kernel(s) on `stream` and returns hipGetLastError(); the C ABI
+// (capi.cpp) validates arguments before calling them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Fixed layer dimensions the kernels implement (V2-Lite / V2 / V3 attention).
+constexpr int D_C = 512;           // KV latent width
+constexpr int D_ROPE = 64;         // decoupled rope key width
+constexpr int D_K = D_C + D_ROPE;  // 576: one cache row
+constexpr int D_NOPE = 128;
+constexpr int D_V = 128;
+constexpr int BLOCK = 64;          // tokens per cache block
+constexpr int ROW_BYTES = D_K * 2;              // 1,152
+constexpr int BLOCK_BYTES = BLOCK * ROW_BYTES;  // 73,728
+constexpr int ROW_CHUNKS = ROW_BYTES / 16;      // 72 sixteen-byte chunks per row
+
+hipError_t launch_cache_append(const uint16_t* c_kv, const uint16_t* k_pe, const int32_t* pos,
+                               const int64_t* slot_mapping, uint16_t* pool, int64_t num_blocks,
+                               int32_t T, double rope_base, hipStream_t stream);
+
+hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                           const uint16_t* w_uk, uint16_t* q_out, int32_t N, int32_t H,
+                           double rope_base, hipStream_t stream);
+
+hipError_t launch_out_up(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int32_t N,
+                         int32_t H, hipStream_t stream);
+
+// Split-KV plan shared by the host (workspace sizing, grid) and the kernels.
+struct AttnPlan {
+  int variant;    // kernel shape, see attn.hip
+  int rg_rows;    // query rows per workgroup (row group)
+  int n_rg;       // row groups per sequence
+  int width;      // workgroups per row group (stream-K width)
+};
+
+AttnPlan plan_attention(int32_t B, int32_t Lq, int32_t H);
+
+// Partial-result slots of one call: width + B (one per (workgroup, sequence) pair).
+size_t attention_workspace_bytes(int32_t B, int32_t Lq, int32_t H);
+
+hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t num_blocks,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
+                              float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
+                              hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,88 @@
+"""Host-only checks of the C ABI library: it loads, exports every symbol the
+header declares, and its host-side argument checks return the documented
+status codes without touching a device (no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_absorb.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(mla_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def nat():
+    from mla_latent_cache_append_amd import native
+    if not os.path.exists(native.LIB_PATH):
+        from mla_latent_cache_append_amd import build
+        build.build()
+    native.lib()
+    return native
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("mla_cache_append", "mla_absorb_q", "mla_decode_attn", "mla_out_up",
+              "mla_decode_workspace_size", "mla_status_str", "mla_dims_default"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(nat):
+    lib = nat.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_defaults(nat):
+    assert nat.mla_status_str(0) == "ok"
+    assert nat.mla_status_str(-3).startswith("workspace")
+    d = nat.mla_dims_default(128)
+    assert (d.num_heads, d.d_c, d.d_rope, d.d_nope, d.d_v, d.block_size) == (128, 512, 64, 128, 128, 64)
+    assert abs(d.softmax_scale - 192 ** -0.5) < 1e-7 and d.rope_base == 10000.0
+
+
+def test_workspace_size_is_host_arithmetic(nat):
+    d = nat.mla_dims_default(128)
+    s1 = nat.mla_decode_workspace_size(d, 32, 1)
+    s8 = nat.mla_decode_workspace_size(d, 16, 8)
+    assert s1 > 0 and s8 > 0 and s1 % 4 == 0
+    # (range slots + sequences) x rows x (m, l, 512 accumulators) x 4 bytes
+    assert s1 % (128 * 514 * 4) == 0
+    bad = nat.mla_dims_default(128)
+    bad.d_c = 256
+    assert nat.mla_decode_workspace_size(bad, 32, 1) == 0
+
+
+def test_invalid_arguments_return_status(nat):
+    lib = nat.lib()
+    d = nat.mla_dims_default(16)
+    P = ctypes.c_void_p
+    fake = P(0x1000)   # never dereferenced: the host checks fail first
+    null = P(0)
+    assert lib.mla_cache_append(ctypes.byref(d), null, fake, fake, fake, fake, 4, 1, null) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(ctypes.byref(d), fake, fake, fake, fake, fake, 4, 0, null) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(ctypes.byref(d), fake, fake, fake, fake, null, 3, null) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_out_up(ctypes.byref(d), fake, fake, fake, -1, null) == nat.MLA_ERR_INVALID_ARG
+    # workspace smaller than required
+    assert lib.mla_decode_attn(ctypes.byref(d), fake, fake, 4, fake, 2, fake, 2, 1, fake, null,
+                               fake, 16, null) == nat.MLA_ERR_WORKSPACE
+    assert lib.mla_decode_attn(ctypes.byref(d), fake, fake, 4, fake, 2, fake, 2, 1, fake, null,
+                               null, 1 << 30, null) == nat.MLA_ERR_WORKSPACE
+    # unsupported shapes
+    d24 = nat.mla_dims_default(24)
+    assert lib.mla_decode_attn(ctypes.byref(d24), fake, fake, 4, fake, 2, fake, 2, 1, fake, null,
+                               fake, 1 << 30, null) == nat.MLA_ERR_UNSUPPORTED
+    d.block_size = 32
+    assert lib.mla_cache_append(ctypes.byref(d), fake, fake, fake, fake, fake, 4, 1, null) == nat.MLA_ERR_UNSUPPORTED
+    d = nat.mla_dims_default(16)
+    d.softmax_scale = 0.0
+    assert lib.mla_out_up(ctypes.byref(d), fake, fake, fake, 1, null) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(None, fake, fake, fake, fake, fake, 4, 1, null) == nat.MLA_ERR_INVALID_ARG
