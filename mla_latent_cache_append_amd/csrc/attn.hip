@@ -157,14 +157,12 @@ template <int NW>
 __device__ __forceinline__ void load_tile(const uint16_t* pool, int blk, int n_valid, lds_char* dst,
                                           int wave, const uint32_t (&goff_lane)[2]) {
   constexpr int PER_WAVE = (BLOCK / 8) * 9 / NW;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)pool + (int64_t)blk * TILE_BYTES), (short)0, n_valid * ROW_BYTES, 0x00020000);
+  const sgpr_x4 rsrc = buffer_rsrc((const char*)pool + (int64_t)blk * TILE_BYTES, n_valid * ROW_BYTES);
 #pragma unroll
   for (int jj = 0; jj < PER_WAVE; ++jj) {
     const int j = wave * PER_WAVE + jj;
     const int tg = j / 9, cg = j - 9 * (j / 9);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + j * 1024), 16, goff_lane[tg & 1],
-                                             tg * 8 * ROW_BYTES + cg * 128, 0, 0);
+    buffer_load_lds_16(rsrc, goff_lane[tg & 1], tg * 8 * ROW_BYTES + cg * 128, lds_addr(dst + j * 1024));
   }
 }
 
@@ -277,57 +275,6 @@ __device__ __forceinline__ void scale_mask(f32x4 (&s)[RB][NTB], float scale_log2
       }
 }
 
-// Row split, one tile: each wave scores its RB*16 rows against all 64 tokens
-// and accumulates all 512 columns.
-template <int RB, bool MASK>
-__device__ __forceinline__ void rows_tile(lds_char* cur, const bf16x8 (&qf)[RB][KSTEPS],
-                                          f32x4 (&o)[RB][32], float (&m_run)[RB],
-                                          float (&l_run)[RB], const int (&lim)[RB], int key0,
-                                          float scale_log2, const uint32_t (&kbase)[2],
-                                          const uint32_t (&vbase)[4], int g) {
-  f32x4 s[RB][4];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) s[rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // S^T = K Q^T, two token blocks at a time, K fragments prefetched one k-step ahead
-#pragma unroll
-  for (int tbp = 0; tbp < 2; ++tbp) {
-    u32x4 kn[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) kn[e] = lds_read_b128(cur + kbase[0], (2 * tbp + e) * 18432);
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const u32x4 kc[2] = {kn[0], kn[1]};
-      if (ks + 1 < KSTEPS) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          kn[e] = lds_read_b128(cur + kbase[(ks + 1) & 1], (2 * tbp + e) * 18432 + ((ks + 1) >> 1) * 1024);
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          s[rb][2 * tbp + e] = mfma16x16x32(as_bf16x8(kc[e]), qf[rb][ks], s[rb][2 * tbp + e]);
-      __builtin_amdgcn_sched_barrier(0);  // one k-step of fragments in flight
-    }
-  }
-  scale_mask<RB, 4, MASK>(s, scale_log2, key0, 0, g, lim);
-  float pv[RB][2][8];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[rb][kb][i] = s[rb][2 * kb][i];
-        pv[rb][kb][4 + i] = s[rb][2 * kb + 1][i];
-      }
-  bf16x8 pf[RB][2];
-  softmax_update<RB, 32>(pv, m_run, l_run, o, pf);
-  pv_product<RB, 32>(cur, vbase, 0, pf, o);
-}
-
 // Column split, one tile: wave w scores tokens 16w..16w+15 for all RB*16 rows,
 // shares the scores through LDS, and accumulates columns 128w..128w+127.
 template <int RB, bool MASK>
@@ -372,15 +319,15 @@ __device__ __forceinline__ void cols_tile(lds_char* cur, __attribute__((address_
   pv_product<RB, 8>(cur, vbase, 8 * wave, pf, o);
 }
 
-// RB : 16-row MFMA blocks of query rows per wave.
-// CS : false = row split (4 waves x RB*16 rows, all tokens, all columns);
-//      true  = column split (4 waves share RB*16 rows; see cols_tile).
-template <int RB, bool CS>
-__global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
+// Few rows per sequence (16 or 32, e.g. 16 heads): the 4 waves of a
+// workgroup share the same RB*16 rows (RB = 16-row MFMA blocks); see cols_tile.
+template <int RB>
+__global__ __launch_bounds__(256, 1) void attn_cols_kernel(AttnArgs a) {
+  constexpr bool CS = true;
   constexpr int NW = 4;
-  constexpr int RG = CS ? RB * 16 : NW * RB * 16;  // rows per workgroup
-  constexpr int NCB = CS ? 8 : 32;                 // 16-column blocks per wave
-  constexpr int SB_BYTES = CS ? RB * 16 * 68 * 4 : 0;
+  constexpr int RG = RB * 16;   // rows per workgroup
+  constexpr int NCB = 8;        // 16-column blocks per wave
+  constexpr int SB_BYTES = RB * 16 * 68 * 4;
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_BYTES + SB_BYTES];
   lds_char* tiles = (lds_char*)smem;
@@ -442,9 +389,11 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     const int k_last = (int)(seg_end - seq_start);  // exclusive
     const bool whole = (x == seq_start) && (seg_end == seq_start + ntiles);
     bool bad = L > a.max_blocks * BLOCK;
-    const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks;
+    // scalar loads (lgkmcnt): reading a block id never waits on the tile loads
+    const __attribute__((address_space(4))) int32_t* bt =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)b * a.max_blocks);
     {
-      const int blk = uni(bt[k_first]);
+      const int blk = bt[k_first];
       if (blk < 0 || blk >= a.num_blocks) bad = true;
       else load_tile<NW>(a.pool, blk, min(BLOCK, L - k_first * BLOCK), tiles, wave, goff_lane);
     }
@@ -480,9 +429,9 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     const int k_mask = max(k_first, min(k_last, max(0, L - a.Lq + 1) / BLOCK));
     auto step = [&](int k) -> lds_char* {
       wait_vmem();
-      __syncthreads();
+      lds_barrier();
       if (k + 1 < k_last) {
-        const int blk = uni(bt[k + 1]);
+        const int blk = bt[k + 1];
         if (blk < 0 || blk >= a.num_blocks) bad = true;
         else
           load_tile<NW>(a.pool, blk, min(BLOCK, L - (k + 1) * BLOCK),
@@ -492,17 +441,11 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     };
     for (int k = k_first; k < k_mask; ++k) {
       lds_char* cur = step(k);
-      if constexpr (CS)
-        cols_tile<RB, false>(cur, sbuf, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, wave, g, c16);
-      else
-        rows_tile<RB, false>(cur, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, g);
+      cols_tile<RB, false>(cur, sbuf, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, wave, g, c16);
     }
     for (int k = k_mask; k < k_last; ++k) {
       lds_char* cur = step(k);
-      if constexpr (CS)
-        cols_tile<RB, true>(cur, sbuf, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, wave, g, c16);
-      else
-        rows_tile<RB, true>(cur, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, g);
+      cols_tile<RB, true>(cur, sbuf, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, wave, g, c16);
     }
 
     // ---- finish the segment: row sums across the 4 lanes of each row
@@ -553,6 +496,330 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     ++b;
     while (b < a.B && tiles_of(uni(a.seq_lens[b]), a.max_blocks) == 0) ++b;
     __syncthreads();  // every wave is done with the tile buffers and sbuf
+  }
+}
+
+
+// ================================================================== pair kernel
+//
+// Rows >= 48 per sequence (e.g. 128 heads): a workgroup owns 64 query rows of
+// one key range, as 2 row groups of 32 rows x 2 halves. Wave (rg2, hf) holds
+// Q[32 rows][features 288 hf .. +288] (72 VGPRs) and accumulates
+// O[32 rows][columns 256 hf .. +256] (128 AGPRs), so the whole state fits one
+// wave per SIMD without spills. Per 32-token half tile each wave forms its
+// partial scores S_hf^T = K[:, half] Q[:, half]^T, the two waves of a pair
+// swap partials through LDS and add them, both run the same online softmax,
+// and each accumulates its column half of O^T = V^T P^T. All products are
+// v_mfma_f32_32x32x16_bf16:
+//   A (32x16): a[j] = A[l % 32][8 (l / 32) + j]
+//   B (16x32): b[j] = B[8 (l / 32) + j][l % 32]
+//   D (32x32): d[i] = D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]
+// Half tiles (32 tokens, 36 KiB, contiguous in HBM) stream through 4 LDS
+// stages, three in flight, by buffer-to-LDS DMA.
+
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int HT_TOK = 32;                      // tokens per half tile
+constexpr int HT_BYTES = HT_TOK * ROW_BYTES;    // 36,864
+constexpr int NSTAGE = 4;
+constexpr int XB_BYTES = 4 * 4 * 64 * 16;       // 4 waves x [4][64 lanes] x 16 B = 16 KiB
+constexpr int KSTEPS_HALF = 18;                 // 288 features / 16
+
+// Half-tile LDS layout: 16-byte chunks ordered [tg 4][cg 9][tl 8][cl 8] for
+// token t = 8 tg + tl, feature chunk c = 8 cg + cl, with cl stored XOR
+// swz2(t). swz2 makes both the 16 tokens of a K read and the 8 tokens x 4
+// chunks of a transposed V read land on distinct bank groups.
+__device__ __forceinline__ int swz2(int t) {
+  const int tl = t & 7;
+  return ((tl >> 1) & 1) | (((tl >> 2) & 1) << 2) | (((t >> 3) & 1) << 1);
+}
+__device__ __forceinline__ uint32_t ht_off(int t, int c) {
+  return (uint32_t)((((t >> 3) * 9 + (c >> 3)) * 64 + (t & 7) * 8 + ((c & 7) ^ swz2(t))) * 16);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Partial scores of one half tile over this wave's 288 features:
+// S_hf^T[token][row], as two MFMA chains over alternating k-steps (the PV
+// MFMAs issued alongside provide further independent chains).
+__device__ __forceinline__ f32x16 pair_partial(lds_char* stage, const bf16x8 (&qf)[KSTEPS_HALF],
+                                               const uint32_t (&kbase)[4]) {
+  f32x16 acc[2] = {};
+  u32x4 kn = lds_read_b128(stage + kbase[0], 0);
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS_HALF; ++ks) {
+    const u32x4 kc = kn;
+    if (ks + 1 < KSTEPS_HALF) kn = lds_read_b128(stage + kbase[(ks + 1) & 3], ((ks + 1) >> 2) * 1024);
+    acc[ks & 1] = mfma32x32x16(as_bf16x8(kc), qf[ks], acc[ks & 1]);
+  }
+  return acc[0] + acc[1];
+}
+
+// xbuf slot of a wave: [4 j][64 lanes] x 16 B, value i of a lane at (i / 4, lane).
+__device__ __forceinline__ void xbuf_put(__attribute__((address_space(3))) char* xb, int wave, int lane,
+                                         const f32x16& s) {
+  __attribute__((address_space(3))) f32x4* mine = (__attribute__((address_space(3))) f32x4*)(xb + wave * 4096);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mine[j * 64 + lane] = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+}
+__device__ __forceinline__ void xbuf_add(const __attribute__((address_space(3))) char* xb, int wave, int lane,
+                                         f32x16& s) {
+  const __attribute__((address_space(3))) f32x4* theirs =
+      (const __attribute__((address_space(3))) f32x4*)(xb + wave * 4096);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 v = theirs[j * 64 + lane];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s[4 * j + u] += v[u];
+  }
+}
+
+// Online-softmax step for one half tile of full scores (unscaled; value i is
+// token key0 + 8 (i / 4) + 4 h + i % 4). Masks keys past the row's position
+// when `tail`, updates (m_run, l_run), rescales O when the running max grew
+// by more than RESCALE_LOG2, and returns the probabilities as the PV B operand:
+//   k-slot 8h + u   <- token 16 kk + 4h + u      (value 8 kk + u)
+//   k-slot 8h + 4+u <- token 16 kk + 8 + 4h + u  (value 8 kk + 4 + u)
+__device__ __forceinline__ void pair_softmax(f32x16 s, bool tail, int key0, int h, int lim,
+                                             float scale_log2, float& m_run, float& l_run,
+                                             f32x16 (&o)[8], bf16x8 (&pf)[2]) {
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (key0 + 8 * (i >> 2) + 4 * h + (i & 3) > lim) s[i] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;   // scale > 0: max commutes with it
+  if (__any(mx > m_run + RESCALE_LOG2)) {
+    if (mx > m_run + RESCALE_LOG2) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) o[cb] *= alpha;
+      m_run = mx;
+    }
+  }
+  const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    bf16x8 pk;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + u], scale_log2, -m_ref));
+      l_run += p;
+      pk[u] = (__bf16)p;
+    }
+    pf[kk] = pk;
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void attn_pair_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * HT_BYTES + XB_BYTES];
+  lds_char* stages = (lds_char*)smem;
+  __attribute__((address_space(3))) char* xb = (__attribute__((address_space(3))) char*)smem + NSTAGE * HT_BYTES;
+
+  const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int rg2 = wave & 1, hf = wave >> 1;
+  const int c32 = lane & 31, h = lane >> 5;
+
+  int unit = blockIdx.x;
+  if (a.n_rg > 1) {
+    const int full = (int)(gridDim.x / 64) * 64;
+    if (unit < full) {
+      const int loc = unit & 63;
+      unit = (unit & ~63) + (loc & 7) * 8 + (loc >> 3);
+    }
+  }
+  const int w = unit / a.n_rg;
+  const int rg = unit - w * a.n_rg;
+  const int64_t T = plan_total_tiles(a.seq_lens, a.B, a.max_blocks);
+  if (T == 0) return;
+  const int64_t x_begin = (int64_t)w * T / a.width;
+  const int64_t x_end = (int64_t)(w + 1) * T / a.width;
+  if (x_begin >= x_end) return;
+  int b;
+  int64_t seq_start;
+  plan_find(a.seq_lens, a.B, a.max_blocks, x_begin, b, seq_start);
+
+  const int r = rg * 64 + rg2 * 32 + c32;   // this lane's query row within the sequence
+  // per-lane offset parts (see ht_off): K reads, V^T reads, DMA
+  uint32_t kbase[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) kbase[q] = ht_off(c32, 36 * hf + 2 * q + h);
+  uint32_t vbase[2][2];
+  {
+    const int i16 = lane & 15, q = lane >> 4;
+    const int tl = 4 * (q >> 1) + (i16 >> 2);
+    const int e = 2 * (q & 1) + ((i16 & 3) >> 1);
+#pragma unroll
+    for (int c1 = 0; c1 < 2; ++c1)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+        vbase[c1][rr] = ht_off(8 * rr + tl, 32 * hf + 4 * c1 + e) - (uint32_t)(rr * 9 * 1024) + 8 * (i16 & 1);
+  }
+  const uint32_t goff = (uint32_t)((lane >> 3) * ROW_BYTES + ((lane & 7) ^ swz2(8 * wave + (lane >> 3))) * 16);
+
+  int64_t x = x_begin;
+  while (x < x_end && b < a.B) {
+    const int L = uni(a.seq_lens[b]);
+    const int ntiles = tiles_of(L, a.max_blocks);
+    const int64_t seg_end = min(x_end, seq_start + ntiles);
+    const int k_first = (int)(x - seq_start);
+    const int k_last = (int)(seg_end - seq_start);
+    const bool whole = (x == seq_start) && (seg_end == seq_start + ntiles);
+    bool bad = L > a.max_blocks * BLOCK;
+    const int key_end = min(k_last * BLOCK, L);
+    const int e0 = 2 * k_first, e1 = (key_end + HT_TOK - 1) / HT_TOK;
+
+    // ---- query fragments (B operand of S^T): row r, features 288 hf + 16 ks + 8 h .. +7
+    bf16x8 qf[KSTEPS_HALF];
+    {
+      const bool valid = r < a.rows;
+      const uint16_t* qrow = a.q + ((int64_t)b * a.rows + (valid ? r : 0)) * D_K + 288 * hf + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS_HALF; ++ks) {
+        u32x4 v = *(const u32x4*)(qrow + 16 * ks);
+        if (!valid) v = u32x4{0u, 0u, 0u, 0u};
+        qf[ks] = as_bf16x8(v);
+      }
+    }
+    const int lim = r < a.rows ? L - a.Lq + r / a.H : -1;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 o[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) o[cb] = f32x16{};
+
+    // Block ids come through scalar loads (lgkmcnt, not vmcnt, so reading one
+    // never drains the tile loads in flight), one tile ahead of their use.
+    const __attribute__((address_space(4))) int32_t* bt =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)b * a.max_blocks);
+    int kq = k_first;
+    int blk_q = bt[kq];
+    int blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
+    auto issue = [&](int e) {
+      const int k = e >> 1;
+      if (k != kq) {   // tiles advance one at a time
+        kq = k;
+        blk_q = blk_q1;
+        blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
+      }
+      const int blk = blk_q;
+      if (blk < 0 || blk >= a.num_blocks) {
+        bad = true;
+        return;
+      }
+      const int n_valid = min(HT_TOK, L - e * HT_TOK);
+      const sgpr_x4 rsrc =
+          buffer_rsrc((const char*)a.pool + (int64_t)blk * TILE_BYTES + (e & 1) * HT_BYTES, n_valid * ROW_BYTES);
+      const uint32_t dst = lds_addr(stages + (e % NSTAGE) * HT_BYTES + wave * 9 * 1024);
+#pragma unroll
+      for (int cg = 0; cg < 9; ++cg)
+        buffer_load_lds_16(rsrc, goff, wave * 8 * ROW_BYTES + cg * 128, dst + cg * 1024);
+    };
+    for (int e = e0; e < min(e1, e0 + NSTAGE - 1); ++e) issue(e);
+
+    // Software pipeline over half tiles: iteration e holds the full scores of
+    // e (exchanged in the previous iteration) and
+    //   (1) waits for stage e+1 and issues the load of e+3,
+    //   (2) runs the score MFMAs of e+1, the softmax of e (VALU) and the PV
+    //       MFMAs of e as one region, so the two MFMA streams interleave and
+    //       the VALU work runs under them,
+    //   (3) swaps the partial scores of e+1 with the partner wave.
+    // Stage e (V) and e+1 (K) are read; e+2 and e+3 are in flight.
+    const int tail_from = max(0, L - a.Lq + 1) / HT_TOK;   // first half tile needing the mask
+    f32x16 s_cur;
+    {
+      if (e1 - e0 >= 3) wait_vmem_n<18>();
+      else if (e1 - e0 == 2) wait_vmem_n<9>();
+      else wait_vmem_n<0>();
+      lds_barrier();
+      s_cur = pair_partial(stages + (e0 % NSTAGE) * HT_BYTES, qf, kbase);
+      xbuf_put(xb, wave, lane, s_cur);
+      lds_barrier();
+      xbuf_add(xb, wave ^ 2, lane, s_cur);
+    }
+    for (int e = e0; e < e1; ++e) {
+      const bool more = e + 1 < e1;
+      if (more) {
+        // stage e+1 complete; only the load of e+2 was issued after it (e+3
+        // is issued below), so at most one stage (9 loads per wave) may remain
+        if (e + 2 < e1) wait_vmem_n<9>();
+        else wait_vmem_n<0>();
+      }
+      lds_barrier();
+      if (e + NSTAGE - 1 < e1) issue(e + NSTAGE - 1);
+      bf16x8 pf[2];
+      pair_softmax(s_cur, e >= tail_from, e * HT_TOK, h, lim, a.scale_log2, m_run, l_run, o, pf);
+      // One branch-free region: the score MFMAs of e+1 (on the last half tile
+      // they rerun on stage e and are discarded) and the PV MFMAs of e,
+      // O^T[col][row] += V^T[col][token] P^T[token][row] for this wave's 256 columns.
+      lds_char* stage = stages + (e % NSTAGE) * HT_BYTES;
+      f32x16 s_next = pair_partial(stages + ((more ? e + 1 : e) % NSTAGE) * HT_BYTES, qf, kbase);
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const i16x4 v0 = lds_read_tr16_b64(stage + vbase[cb & 1][0], kk * 18432 + (cb >> 1) * 1024);
+          const i16x4 v1 = lds_read_tr16_b64(stage + vbase[cb & 1][1], kk * 18432 + 9216 + (cb >> 1) * 1024);
+          o[cb] = mfma32x32x16(join_tr(v0, v1), pf[kk], o[cb]);
+        }
+      }
+      xbuf_put(xb, wave, lane, s_next);
+      lds_barrier();
+      xbuf_add(xb, wave ^ 2, lane, s_next);
+      s_cur = s_next;
+    }
+
+    // ---- finish the segment
+    l_run += __shfl_xor(l_run, 32);
+    if (r < a.rows) {
+      const int64_t orow = (int64_t)b * a.rows + r;
+      if (whole) {
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float v0 = o[cb][4 * j] * inv, v1 = o[cb][4 * j + 1] * inv;
+            float v2 = o[cb][4 * j + 2] * inv, v3 = o[cb][4 * j + 3] * inv;
+            if (bad) v0 = v1 = v2 = v3 = NAN;
+            const u32x2 out = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            *(u32x2*)(a.o_lat + orow * D_C + 256 * hf + 32 * cb + 8 * j + 4 * h) = out;
+          }
+        if (a.lse && hf == 0 && h == 0) {
+          float lv = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
+          a.lse[orow] = bad ? NAN : lv;
+        }
+      } else {
+        const int64_t prow = (int64_t)(w + b) * a.rows + r;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f32x4 v = {o[cb][4 * j], o[cb][4 * j + 1], o[cb][4 * j + 2], o[cb][4 * j + 3]};
+            if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+            *(f32x4*)(a.ws_acc + prow * D_C + 256 * hf + 32 * cb + 8 * j + 4 * h) = v;
+          }
+        if (hf == 0 && h == 0) {
+          a.ws_ml[prow * 2 + 0] = bad ? NAN : m_run;
+          a.ws_ml[prow * 2 + 1] = bad ? NAN : l_run;
+        }
+      }
+    }
+    x = seg_end;
+    seq_start += ntiles;
+    ++b;
+    while (b < a.B && tiles_of(uni(a.seq_lens[b]), a.max_blocks) == 0) ++b;
+    __syncthreads();
   }
 }
 
@@ -615,13 +882,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-enum { V_ROWS128 = 0, V_ROWS64 = 1, V_COLS32 = 2, V_COLS16 = 3 };
+enum { V_PAIR64 = 0, V_COLS32 = 2, V_COLS16 = 3 };
 
 AttnPlan plan_attention(int32_t B, int32_t Lq, int32_t H) {
   (void)B;
   AttnPlan p;
   const int rows = Lq * H;
-  if (rows >= 48) { p.variant = V_ROWS64; p.rg_rows = 64; }
+  if (rows >= 48) { p.variant = V_PAIR64; p.rg_rows = 64; }
   else if (rows >= 32) { p.variant = V_COLS32; p.rg_rows = 32; }
   else { p.variant = V_COLS16; p.rg_rows = 16; }
   p.n_rg = (rows + p.rg_rows - 1) / p.rg_rows;
@@ -663,14 +930,14 @@ hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t n
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
   const dim3 grid(p.width * p.n_rg);
   switch (p.variant) {
-    case V_ROWS64:
-      hipLaunchKernelGGL((attn_split_kernel<1, false>), grid, dim3(256), 0, stream, a);
+    case V_PAIR64:
+      hipLaunchKernelGGL(attn_pair_kernel, grid, dim3(256), 0, stream, a);
       break;
     case V_COLS32:
-      hipLaunchKernelGGL((attn_split_kernel<2, true>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attn_cols_kernel<2>), grid, dim3(256), 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((attn_split_kernel<1, true>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attn_cols_kernel<1>), grid, dim3(256), 0, stream, a);
       break;
   }
   hipError_t e = hipGetLastError();

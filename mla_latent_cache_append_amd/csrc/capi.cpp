@@ -1,6 +1,6 @@
 // C ABI of libmla_absorb: argument checks on the host, then kernel launches on
 // the caller's stream. Declarations and their contracts: include/mla_absorb.h.
-#include "../../include/mla_absorb.h"
+#include "mla_absorb.h"
 
 #include <math.h>
 

@@ -81,12 +81,47 @@ __device__ __forceinline__ i16x4 lds_read_tr16_b64(const __attribute__((address_
       (__attribute__((address_space(3))) i16x4*)(base + off));
 }
 
-// Global -> LDS direct copy of 16 bytes per lane: lane l's 16 bytes land at
-// lds_wave_base + 16 * l (lds_wave_base is wave-uniform).
-__device__ __forceinline__ void global_load_lds_16(const void* gptr, lds_void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gptr, lds_wave_base, 16, 0, 0);
+// Buffer resource (V#) for raw 16-byte loads of `bytes` bytes at `base`:
+// lanes whose offset + 16 exceeds `bytes` read zeros.
+typedef unsigned int sgpr_x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ sgpr_x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return sgpr_x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// Buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane
+// l reads rsrc + voff + soff and its 16 bytes land at LDS byte address
+// lds_wave_base + 16 l (lds_wave_base is wave-uniform, taken from M0).
+//
+// Issued as inline asm on purpose: the compiler's wait-count pass cannot tell
+// these LDS writes apart from the transposing LDS reads (ds_read_b64_tr_b16)
+// and would drain every load in flight before each such read. The kernels
+// order these copies themselves: s_waitcnt vmcnt(N) for the stage about to
+// be read, then a barrier. M0 is set right before each copy; no compiled code
+// in these kernels reads M0.
+__device__ __forceinline__ void buffer_load_lds_16(sgpr_x4 rsrc, uint32_t voff, uint32_t soff,
+                                                   uint32_t lds_wave_base) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_wave_base)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const __attribute__((address_space(3))) void* p) {
+  return (uint32_t)(uintptr_t)p;
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier for LDS traffic only: this wave's LDS writes complete,
+// then s_barrier. Unlike __syncthreads() it does not wait for outstanding
+// global / buffer loads, so tile loads stay in flight across it. (Data that
+// buffer-to-LDS loads deliver is waited for separately with vmcnt.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 }  // namespace mla
