@@ -500,39 +500,30 @@ __global__ __launch_bounds__(256, 1) void attn_cols_kernel(AttnArgs a) {
 }
 
 
-// ================================================================== pair kernel
+// ================================================================== rows kernel
 //
-// Rows >= 48 per sequence (e.g. 128 heads): a workgroup owns 64 query rows of
-// one key range, as 2 row groups of 32 rows x 2 halves. Wave (rg2, hf) holds
-// Q[32 rows][features 288 hf .. +288] (72 VGPRs) and accumulates
-// O[32 rows][columns 256 hf .. +256] (128 AGPRs), so the whole state fits one
-// wave per SIMD without spills. Per 32-token half tile each wave forms its
-// partial scores S_hf^T = K[:, half] Q[:, half]^T, the two waves of a pair
-// swap partials through LDS and add them, both run the same online softmax,
-// and each accumulates its column half of O^T = V^T P^T. All products are
-// v_mfma_f32_32x32x16_bf16:
-//   A (32x16): a[j] = A[l % 32][8 (l / 32) + j]
-//   B (16x32): b[j] = B[8 (l / 32) + j][l % 32]
-//   D (32x32): d[i] = D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]
-// Half tiles (32 tokens, 36 KiB, contiguous in HBM) stream through 4 LDS
-// stages, three in flight, by buffer-to-LDS DMA.
-
-typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
-
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+// Rows >= 48 per sequence (e.g. 128 heads): a workgroup owns 64 * NH query
+// rows of one key range, as NH halves of 4 waves. In half hw, wave r (0..3)
+//   * scores rows 64 hw + 16 r .. +15 against each 32-token half tile with
+//     the full 576-wide query (S^T = K Q^T, Q in 72 VGPRs), runs their online
+//     softmax, and writes the bf16 probabilities P^T to LDS;
+//   * accumulates columns 128 r .. +127 of O for all 64 rows of its half
+//     (O^T = V^T P^T, 128 AGPRs), reading the half's four P blocks from LDS.
+// The whole key range's cache is read from HBM once per workgroup (all heads
+// of the sequence on one CU), every wave stays within 256 registers (two
+// waves per SIMD), and no score is computed twice. Iteration e scores half
+// tile e+1 and accumulates half tile e, two independent MFMA streams; one
+// barrier per half tile publishes both the next stage and the probabilities.
+// Products use v_mfma_f32_16x16x32_bf16 (layout at mfma16x16x32).
 
 constexpr int HT_TOK = 32;                      // tokens per half tile
 constexpr int HT_BYTES = HT_TOK * ROW_BYTES;    // 36,864
-constexpr int NSTAGE = 4;
-constexpr int XB_BYTES = 4 * 4 * 64 * 16;       // 4 waves x [4][64 lanes] x 16 B = 16 KiB
-constexpr int KSTEPS_HALF = 18;                 // 288 features / 16
+constexpr int RSTAGE = 3;                       // LDS stages of half tiles
 
 // Half-tile LDS layout: 16-byte chunks ordered [tg 4][cg 9][tl 8][cl 8] for
-// token t = 8 tg + tl, feature chunk c = 8 cg + cl, with cl stored XOR
-// swz2(t). swz2 makes both the 16 tokens of a K read and the 8 tokens x 4
-// chunks of a transposed V read land on distinct bank groups.
+// token t = 8 tg + tl, feature chunk c = 8 cg + cl, cl stored XOR swz2(t).
+// For any 16 consecutive tokens and one chunk (K reads) and for any 16 tokens
+// x 2 chunks (transposed V reads) the accesses cover all 16 bank groups.
 __device__ __forceinline__ int swz2(int t) {
   const int tl = t & 7;
   return ((tl >> 1) & 1) | (((tl >> 2) & 1) << 2) | (((t >> 3) & 1) << 1);
@@ -546,90 +537,23 @@ __device__ __forceinline__ void wait_vmem_n() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Partial scores of one half tile over this wave's 288 features:
-// S_hf^T[token][row], as two MFMA chains over alternating k-steps (the PV
-// MFMAs issued alongside provide further independent chains).
-__device__ __forceinline__ f32x16 pair_partial(lds_char* stage, const bf16x8 (&qf)[KSTEPS_HALF],
-                                               const uint32_t (&kbase)[4]) {
-  f32x16 acc[2] = {};
-  u32x4 kn = lds_read_b128(stage + kbase[0], 0);
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS_HALF; ++ks) {
-    const u32x4 kc = kn;
-    if (ks + 1 < KSTEPS_HALF) kn = lds_read_b128(stage + kbase[(ks + 1) & 3], ((ks + 1) >> 2) * 1024);
-    acc[ks & 1] = mfma32x32x16(as_bf16x8(kc), qf[ks], acc[ks & 1]);
-  }
-  return acc[0] + acc[1];
-}
-
-// xbuf slot of a wave: [4 j][64 lanes] x 16 B, value i of a lane at (i / 4, lane).
-__device__ __forceinline__ void xbuf_put(__attribute__((address_space(3))) char* xb, int wave, int lane,
-                                         const f32x16& s) {
-  __attribute__((address_space(3))) f32x4* mine = (__attribute__((address_space(3))) f32x4*)(xb + wave * 4096);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) mine[j * 64 + lane] = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
-}
-__device__ __forceinline__ void xbuf_add(const __attribute__((address_space(3))) char* xb, int wave, int lane,
-                                         f32x16& s) {
-  const __attribute__((address_space(3))) f32x4* theirs =
-      (const __attribute__((address_space(3))) f32x4*)(xb + wave * 4096);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f32x4 v = theirs[j * 64 + lane];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) s[4 * j + u] += v[u];
-  }
-}
-
-// Online-softmax step for one half tile of full scores (unscaled; value i is
-// token key0 + 8 (i / 4) + 4 h + i % 4). Masks keys past the row's position
-// when `tail`, updates (m_run, l_run), rescales O when the running max grew
-// by more than RESCALE_LOG2, and returns the probabilities as the PV B operand:
-//   k-slot 8h + u   <- token 16 kk + 4h + u      (value 8 kk + u)
-//   k-slot 8h + 4+u <- token 16 kk + 8 + 4h + u  (value 8 kk + 4 + u)
-__device__ __forceinline__ void pair_softmax(f32x16 s, bool tail, int key0, int h, int lim,
-                                             float scale_log2, float& m_run, float& l_run,
-                                             f32x16 (&o)[8], bf16x8 (&pf)[2]) {
-  if (tail) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (key0 + 8 * (i >> 2) + 4 * h + (i & 3) > lim) s[i] = -INFINITY;
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;   // scale > 0: max commutes with it
-  if (__any(mx > m_run + RESCALE_LOG2)) {
-    if (mx > m_run + RESCALE_LOG2) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
-      l_run *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) o[cb] *= alpha;
-      m_run = mx;
-    }
-  }
-  const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    bf16x8 pk;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + u], scale_log2, -m_ref));
-      l_run += p;
-      pk[u] = (__bf16)p;
-    }
-    pf[kk] = pk;
-  }
-}
-
-__global__ __launch_bounds__(256, 1) void attn_pair_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * HT_BYTES + XB_BYTES];
+template <int NH>
+__global__ __launch_bounds__(256 * NH, 1) void attn_rows_kernel(AttnArgs a) {
+  constexpr int NWAVE = 4 * NH;
+  constexpr int PB_BYTES = NH * 4 * 64 * 16;       // P^T blocks of one half tile
+  constexpr int QR_BYTES = NWAVE * 2 * 64 * 16;     // rope part of Q (2 k-steps) per wave
+  __shared__ __attribute__((aligned(1024))) char smem[RSTAGE * HT_BYTES + 2 * PB_BYTES + QR_BYTES +
+                                                       2 * NH * 64 * 4 * 2];
   lds_char* stages = (lds_char*)smem;
-  __attribute__((address_space(3))) char* xb = (__attribute__((address_space(3))) char*)smem + NSTAGE * HT_BYTES;
+  lds_char* pbase = stages + RSTAGE * HT_BYTES;                       // [2][NH][4 rb][64 lanes] x 16 B
+  lds_char* qrope = pbase + 2 * PB_BYTES;                               // [wave][2 ks][64 lanes] x 16 B
+  __attribute__((address_space(3))) float* abase =
+      (__attribute__((address_space(3))) float*)(qrope + QR_BYTES);      // [2][NH][64 rows] rescale factors
+  __attribute__((address_space(3))) float* stat = abase + 2 * NH * 64;   // [NH][64 rows][2] (m, l)
 
   const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int rg2 = wave & 1, hf = wave >> 1;
-  const int c32 = lane & 31, h = lane >> 5;
+  const int hw = wave >> 2, r4 = wave & 3;
+  const int g = lane >> 4, c16 = lane & 15;
 
   int unit = blockIdx.x;
   if (a.n_rg > 1) {
@@ -650,23 +574,22 @@ __global__ __launch_bounds__(256, 1) void attn_pair_kernel(AttnArgs a) {
   int64_t seq_start;
   plan_find(a.seq_lens, a.B, a.max_blocks, x_begin, b, seq_start);
 
-  const int r = rg * 64 + rg2 * 32 + c32;   // this lane's query row within the sequence
-  // per-lane offset parts (see ht_off): K reads, V^T reads, DMA
-  uint32_t kbase[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) kbase[q] = ht_off(c32, 36 * hf + 2 * q + h);
-  uint32_t vbase[2][2];
+  const int half_row0 = rg * 64 * NH + hw * 64;     // first row of this wave's half
+  const int r_s = half_row0 + 16 * r4 + c16;        // row this lane scores
+  // K fragment (token 16 tb + c16, chunk 4 ks + g) = kbase[ks & 1] + tb*18432 + (ks >> 1)*1024
+  const uint32_t kbase[2] = {ht_off(c16, g), ht_off(c16, 4 + g)};
+  // V^T fragment of column block cb (cols 128 r4 + 16 cb ..), first / second read:
+  //   vbase[cb & 3] + (cb >> 2)*1024 (+ 18432 for tokens 16..31)
+  uint32_t vbase[4];
   {
-    const int i16 = lane & 15, q = lane >> 4;
-    const int tl = 4 * (q >> 1) + (i16 >> 2);
-    const int e = 2 * (q & 1) + ((i16 & 3) >> 1);
+    const int t = 4 * g + (c16 >> 2);                // token of this lane's 4-element load
+    const int e = (c16 & 3) >> 1;
 #pragma unroll
-    for (int c1 = 0; c1 < 2; ++c1)
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr)
-        vbase[c1][rr] = ht_off(8 * rr + tl, 32 * hf + 4 * c1 + e) - (uint32_t)(rr * 9 * 1024) + 8 * (i16 & 1);
+    for (int q = 0; q < 4; ++q)
+      vbase[q] = ht_off(t, 16 * r4 + 2 * q + e) + 8 * (c16 & 1);   // chunk 16 r4 = column 128 r4
   }
-  const uint32_t goff = (uint32_t)((lane >> 3) * ROW_BYTES + ((lane & 7) ^ swz2(8 * wave + (lane >> 3))) * 16);
+  const uint32_t goff = (uint32_t)((lane >> 3) * ROW_BYTES + ((lane & 7) ^ swz2(8 * r4 + (lane >> 3))) * 16);
+  const bool dma_wave = hw == 0;                    // half 0's four waves copy the tiles
 
   int64_t x = x_begin;
   while (x < x_end && b < a.B) {
@@ -680,26 +603,31 @@ __global__ __launch_bounds__(256, 1) void attn_pair_kernel(AttnArgs a) {
     const int key_end = min(k_last * BLOCK, L);
     const int e0 = 2 * k_first, e1 = (key_end + HT_TOK - 1) / HT_TOK;
 
-    // ---- query fragments (B operand of S^T): row r, features 288 hf + 16 ks + 8 h .. +7
-    bf16x8 qf[KSTEPS_HALF];
+    // query fragments: B operand of S^T (lane: row r_s, features 32 ks + 8 g .. +7);
+    // the 16 latent k-steps stay in registers, the 2 rope k-steps in LDS
+    constexpr int KS_REG = D_C / 32;
+    bf16x8 qf[KS_REG];
+    lds_char* qr = qrope + wave * 2048 + lane * 16;
     {
-      const bool valid = r < a.rows;
-      const uint16_t* qrow = a.q + ((int64_t)b * a.rows + (valid ? r : 0)) * D_K + 288 * hf + 8 * h;
+      const bool valid = r_s < a.rows;
+      const uint16_t* qrow = a.q + ((int64_t)b * a.rows + (valid ? r_s : 0)) * D_K + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS_HALF; ++ks) {
-        u32x4 v = *(const u32x4*)(qrow + 16 * ks);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        u32x4 v = *(const u32x4*)(qrow + 32 * ks);
         if (!valid) v = u32x4{0u, 0u, 0u, 0u};
-        qf[ks] = as_bf16x8(v);
+        if (ks < KS_REG) qf[ks] = as_bf16x8(v);
+        else *(__attribute__((address_space(3))) u32x4*)(qr + (ks - KS_REG) * 1024) = v;
       }
     }
-    const int lim = r < a.rows ? L - a.Lq + r / a.H : -1;
+    const int lim = r_s < a.rows ? L - a.Lq + r_s / a.H : -1;
     float m_run = -INFINITY, l_run = 0.f;
-    f32x16 o[8];
+    f32x4 o[4][8];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) o[cb] = f32x16{};
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) o[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Block ids come through scalar loads (lgkmcnt, not vmcnt, so reading one
-    // never drains the tile loads in flight), one tile ahead of their use.
+    // block ids through scalar loads, one tile ahead
     const __attribute__((address_space(4))) int32_t* bt =
         (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)b * a.max_blocks);
     int kq = k_first;
@@ -707,7 +635,7 @@ __global__ __launch_bounds__(256, 1) void attn_pair_kernel(AttnArgs a) {
     int blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
     auto issue = [&](int e) {
       const int k = e >> 1;
-      if (k != kq) {   // tiles advance one at a time
+      if (k != kq) {
         kq = k;
         blk_q = blk_q1;
         blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
@@ -717,101 +645,160 @@ __global__ __launch_bounds__(256, 1) void attn_pair_kernel(AttnArgs a) {
         bad = true;
         return;
       }
+      if (!dma_wave) return;
       const int n_valid = min(HT_TOK, L - e * HT_TOK);
       const sgpr_x4 rsrc =
           buffer_rsrc((const char*)a.pool + (int64_t)blk * TILE_BYTES + (e & 1) * HT_BYTES, n_valid * ROW_BYTES);
-      const uint32_t dst = lds_addr(stages + (e % NSTAGE) * HT_BYTES + wave * 9 * 1024);
+      const uint32_t dst = lds_addr(stages + (e % RSTAGE) * HT_BYTES + r4 * 9 * 1024);
 #pragma unroll
       for (int cg = 0; cg < 9; ++cg)
-        buffer_load_lds_16(rsrc, goff, wave * 8 * ROW_BYTES + cg * 128, dst + cg * 1024);
+        buffer_load_lds_16(rsrc, goff, r4 * 8 * ROW_BYTES + cg * 128, dst + cg * 1024);
     };
-    for (int e = e0; e < min(e1, e0 + NSTAGE - 1); ++e) issue(e);
 
-    // Software pipeline over half tiles: iteration e holds the full scores of
-    // e (exchanged in the previous iteration) and
-    //   (1) waits for stage e+1 and issues the load of e+3,
-    //   (2) runs the score MFMAs of e+1, the softmax of e (VALU) and the PV
-    //       MFMAs of e as one region, so the two MFMA streams interleave and
-    //       the VALU work runs under them,
-    //   (3) swaps the partial scores of e+1 with the partner wave.
-    // Stage e (V) and e+1 (K) are read; e+2 and e+3 are in flight.
-    const int tail_from = max(0, L - a.Lq + 1) / HT_TOK;   // first half tile needing the mask
-    f32x16 s_cur;
-    {
-      if (e1 - e0 >= 3) wait_vmem_n<18>();
-      else if (e1 - e0 == 2) wait_vmem_n<9>();
-      else wait_vmem_n<0>();
-      lds_barrier();
-      s_cur = pair_partial(stages + (e0 % NSTAGE) * HT_BYTES, qf, kbase);
-      xbuf_put(xb, wave, lane, s_cur);
-      lds_barrier();
-      xbuf_add(xb, wave ^ 2, lane, s_cur);
-    }
-    for (int e = e0; e < e1; ++e) {
-      const bool more = e + 1 < e1;
-      if (more) {
-        // stage e+1 complete; only the load of e+2 was issued after it (e+3
-        // is issued below), so at most one stage (9 loads per wave) may remain
-        if (e + 2 < e1) wait_vmem_n<9>();
-        else wait_vmem_n<0>();
+    // Scores of half tile e for this wave's 16 rows, online softmax, and P^T /
+    // rescale factors into buffer (e & 1). Scores value i of token block tb is
+    // token 16 tb + 4 g + i of the half tile.
+    auto scores = [&](int e) {
+      lds_char* st = stages + (e % RSTAGE) * HT_BYTES;
+      f32x4 s[2] = {};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        // no register prefetch: the other wave on the SIMD covers LDS latency
+        u32x4 kc[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) kc[tb] = lds_read_b128(st + kbase[ks & 1], tb * 18432 + (ks >> 1) * 1024);
+        const bf16x8 qk = ks < KS_REG ? qf[ks < KS_REG ? ks : 0]
+                                      : as_bf16x8(lds_read_b128(qr, (ks - KS_REG) * 1024));
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) s[tb] = mfma16x16x32(as_bf16x8(kc[tb]), qk, s[tb]);
       }
-      lds_barrier();
-      if (e + NSTAGE - 1 < e1) issue(e + NSTAGE - 1);
-      bf16x8 pf[2];
-      pair_softmax(s_cur, e >= tail_from, e * HT_TOK, h, lim, a.scale_log2, m_run, l_run, o, pf);
-      // One branch-free region: the score MFMAs of e+1 (on the last half tile
-      // they rerun on stage e and are discarded) and the PV MFMAs of e,
-      // O^T[col][row] += V^T[col][token] P^T[token][row] for this wave's 256 columns.
-      lds_char* stage = stages + (e % NSTAGE) * HT_BYTES;
-      f32x16 s_next = pair_partial(stages + ((more ? e + 1 : e) % NSTAGE) * HT_BYTES, qf, kbase);
+      const int key0 = e * HT_TOK;
+      if (key0 + HT_TOK - 1 > L - a.Lq) {       // some key past some row's position
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (key0 + 16 * tb + 4 * g + i > lim) s[tb][i] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx *= a.scale_log2;                        // scale > 0: max commutes with it
+      float alpha = 1.f;
+      if (mx > m_run + RESCALE_LOG2) {           // rare: the running max moved a lot
+        alpha = __builtin_amdgcn_exp2f(m_run - mx);   // 0 when m_run = -inf
+        l_run *= alpha;
+        m_run = mx;
+      }
+      __attribute__((address_space(3))) float* ab = abase + ((e & 1) * NH + hw) * 64;
+      if (g == 0) ab[16 * r4 + c16] = alpha;
+      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+      bf16x8 pk;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][i], a.scale_log2, -m_ref));
+          l_run += p;
+          pk[4 * tb + i] = (__bf16)p;
+        }
+      *(__attribute__((address_space(3))) u32x4*)(pbase + (((e & 1) * NH + hw) * 4 + r4) * 1024 + lane * 16) =
+          as_u32x4(pk);
+    };
+
+    // O^T[col][row] += V^T[col][token] P^T[token][row] over half tile e for
+    // columns 128 r4 .. +127 and the half's 64 rows, after applying the
+    // rows' rescale factors published with P.
+    auto accumulate = [&](int e) {
+      const __attribute__((address_space(3))) float* ab = abase + ((e & 1) * NH + hw) * 64;
+      float al[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) al[rb] = ab[16 * rb + c16];
+      bool any = false;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) any |= al[rb] != 1.f;
+      if (__any(any)) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb) o[rb][cb] *= al[rb];
+      }
+      lds_char* st = stages + (e % RSTAGE) * HT_BYTES;
+      const lds_char* pb = pbase + ((e & 1) * NH + hw) * 4 * 1024 + lane * 16;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) pf[rb] = as_bf16x8(lds_read_b128(pb, rb * 1024));
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
+        const i16x4 v0 = lds_read_tr16_b64(st + vbase[cb & 3], (cb >> 2) * 1024);
+        const i16x4 v1 = lds_read_tr16_b64(st + vbase[cb & 3], 18432 + (cb >> 2) * 1024);
+        const bf16x8 vf = join_tr(v0, v1);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const i16x4 v0 = lds_read_tr16_b64(stage + vbase[cb & 1][0], kk * 18432 + (cb >> 1) * 1024);
-          const i16x4 v1 = lds_read_tr16_b64(stage + vbase[cb & 1][1], kk * 18432 + 9216 + (cb >> 1) * 1024);
-          o[cb] = mfma32x32x16(join_tr(v0, v1), pf[kk], o[cb]);
-        }
+        for (int rb = 0; rb < 4; ++rb) o[rb][cb] = mfma16x16x32(vf, pf[rb], o[rb][cb]);
       }
-      xbuf_put(xb, wave, lane, s_next);
-      lds_barrier();
-      xbuf_add(xb, wave ^ 2, lane, s_next);
-      s_cur = s_next;
+    };
+
+    // ---- pipeline: prologue loads e0, e0+1; stage e+2 is loaded during iteration e
+    for (int e = e0; e < min(e1, e0 + 2); ++e) issue(e);
+    if (dma_wave) {
+      if (e1 - e0 >= 2) wait_vmem_n<9>();
+      else wait_vmem_n<0>();
+    }
+    lds_barrier();
+    scores(e0);
+    for (int e = e0; e < e1; ++e) {
+      // stage e+1 complete (only e+2, not yet issued, would be newer)
+      if (dma_wave) wait_vmem_n<0>();
+      lds_barrier();                 // stage e+1 and P / factors of e visible
+      if (e + 2 < e1) issue(e + 2);  // into the stage of e-1, free after the barrier
+      if (e + 1 < e1) scores(e + 1);
+      accumulate(e);
     }
 
-    // ---- finish the segment
+    // ---- finish the segment: row sums; publish (m, l) for the column owners
+    l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-    if (r < a.rows) {
+    lds_barrier();
+    if (g == 0) {
+      stat[(hw * 64 + 16 * r4 + c16) * 2 + 0] = m_run;
+      stat[(hw * 64 + 16 * r4 + c16) * 2 + 1] = l_run;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = half_row0 + 16 * rb + c16;       // row of o[rb][*] in this lane
+      if (r >= a.rows) continue;
+      const float mr = stat[(hw * 64 + 16 * rb + c16) * 2 + 0];
+      const float lr = stat[(hw * 64 + 16 * rb + c16) * 2 + 1];
       const int64_t orow = (int64_t)b * a.rows + r;
       if (whole) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        const float inv = lr > 0.f ? 1.f / lr : 0.f;
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float v0 = o[cb][4 * j] * inv, v1 = o[cb][4 * j + 1] * inv;
-            float v2 = o[cb][4 * j + 2] * inv, v3 = o[cb][4 * j + 3] * inv;
-            if (bad) v0 = v1 = v2 = v3 = NAN;
-            const u32x2 out = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            *(u32x2*)(a.o_lat + orow * D_C + 256 * hf + 32 * cb + 8 * j + 4 * h) = out;
-          }
-        if (a.lse && hf == 0 && h == 0) {
-          float lv = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
+        for (int cb = 0; cb < 8; ++cb) {
+          f32x4 v = o[rb][cb] * inv;
+          if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+          const u32x2 out = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *(u32x2*)(a.o_lat + orow * D_C + 128 * r4 + 16 * cb + 4 * g) = out;
+        }
+        if (a.lse && r4 == 0 && g == 0) {
+          const float lv = lr > 0.f ? (mr + __log2f(lr)) * LN2 : -INFINITY;
           a.lse[orow] = bad ? NAN : lv;
         }
       } else {
         const int64_t prow = (int64_t)(w + b) * a.rows + r;
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            f32x4 v = {o[cb][4 * j], o[cb][4 * j + 1], o[cb][4 * j + 2], o[cb][4 * j + 3]};
-            if (bad) v = f32x4{NAN, NAN, NAN, NAN};
-            *(f32x4*)(a.ws_acc + prow * D_C + 256 * hf + 32 * cb + 8 * j + 4 * h) = v;
-          }
-        if (hf == 0 && h == 0) {
-          a.ws_ml[prow * 2 + 0] = bad ? NAN : m_run;
-          a.ws_ml[prow * 2 + 1] = bad ? NAN : l_run;
+        for (int cb = 0; cb < 8; ++cb) {
+          f32x4 v = o[rb][cb];
+          if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+          *(f32x4*)(a.ws_acc + prow * D_C + 128 * r4 + 16 * cb + 4 * g) = v;
+        }
+        if (r4 == 0 && g == 0) {
+          a.ws_ml[prow * 2 + 0] = bad ? NAN : mr;
+          a.ws_ml[prow * 2 + 1] = bad ? NAN : lr;
         }
       }
     }
@@ -819,7 +806,7 @@ __global__ __launch_bounds__(256, 1) void attn_pair_kernel(AttnArgs a) {
     seq_start += ntiles;
     ++b;
     while (b < a.B && tiles_of(uni(a.seq_lens[b]), a.max_blocks) == 0) ++b;
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -882,13 +869,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-enum { V_PAIR64 = 0, V_COLS32 = 2, V_COLS16 = 3 };
+enum { V_ROWS128 = 0, V_ROWS64 = 1, V_COLS32 = 2, V_COLS16 = 3 };
 
 AttnPlan plan_attention(int32_t B, int32_t Lq, int32_t H) {
   (void)B;
   AttnPlan p;
   const int rows = Lq * H;
-  if (rows >= 48) { p.variant = V_PAIR64; p.rg_rows = 64; }
+  if (rows >= 96) { p.variant = V_ROWS128; p.rg_rows = 128; }
+  else if (rows >= 48) { p.variant = V_ROWS64; p.rg_rows = 64; }
   else if (rows >= 32) { p.variant = V_COLS32; p.rg_rows = 32; }
   else { p.variant = V_COLS16; p.rg_rows = 16; }
   p.n_rg = (rows + p.rg_rows - 1) / p.rg_rows;
@@ -930,8 +918,11 @@ hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t n
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
   const dim3 grid(p.width * p.n_rg);
   switch (p.variant) {
-    case V_PAIR64:
-      hipLaunchKernelGGL(attn_pair_kernel, grid, dim3(256), 0, stream, a);
+    case V_ROWS128:
+      hipLaunchKernelGGL(attn_rows_kernel<2>, grid, dim3(512), 0, stream, a);
+      break;
+    case V_ROWS64:
+      hipLaunchKernelGGL(attn_rows_kernel<1>, grid, dim3(256), 0, stream, a);
       break;
     case V_COLS32:
       hipLaunchKernelGGL((attn_cols_kernel<2>), grid, dim3(256), 0, stream, a);

@@ -21,6 +21,8 @@ constexpr int AQ_COLS = 64;                  // latent columns per absorb workgr
 constexpr int AQ_CHUNKS = D_C / AQ_COLS;     // 8 workgroups per head
 constexpr int AQ_LDS_STRIDE = D_NOPE + 8;    // padded row of the transposed W tile
 
+// Blocks 0..N-1 rotate q_pe (one token each, dispatched first); the others
+// each compute a [N x 64] column slice of q_lat for one head.
 // W_UK[h] is stored [128 j][512 c] (rows of nn.Linear(d_c, H*d_nope).weight);
 // the contraction runs over j, so each workgroup stages a [128 x 64] slice
 // transposed into LDS as wt[c][j], making each MFMA A fragment (8 consecutive
@@ -30,21 +32,25 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
     const int32_t* __restrict__ pos, const uint16_t* __restrict__ w_uk,
     uint16_t* __restrict__ q_out, int N, int H, double base) {
   __shared__ __attribute__((aligned(16))) uint16_t wt[AQ_COLS * AQ_LDS_STRIDE];
-  const int n_gemm = H * AQ_CHUNKS;
-  if ((int)blockIdx.x >= n_gemm) {
-    // rope of one query token, all heads: q_out[n][h][512 + 2i .. +1]
-    const int n = blockIdx.x - n_gemm;
-    const int p = pos[n];
+  __shared__ double rot[D_ROPE / 2][2];
+  if ((int)blockIdx.x < N) {
+    // rope of one query token, all heads: q_out[n][h][512 + 2i .. +1]. The 32
+    // (cos, sin) pairs depend only on the position: computed once, shared by
+    // every head.
+    const int n = blockIdx.x;
+    if (threadIdx.x < D_ROPE / 2) rope_cos_sin(pos[n], threadIdx.x, base, rot[threadIdx.x][0], rot[threadIdx.x][1]);
+    __syncthreads();
     for (int k = threadIdx.x; k < H * (D_ROPE / 2); k += blockDim.x) {
       const int h = k / (D_ROPE / 2), i = k % (D_ROPE / 2);
       const int64_t rowq = (int64_t)n * H + h;
       const uint32_t x = *(const uint32_t*)(q_pe + rowq * D_ROPE + 2 * i);
-      *(uint32_t*)(q_out + rowq * D_K + D_C + 2 * i) = rope_pair_bf16(x, p, i, base);
+      *(uint32_t*)(q_out + rowq * D_K + D_C + 2 * i) = rope_rotate_bf16(x, rot[i][0], rot[i][1]);
     }
     return;
   }
-  const int h = blockIdx.x / AQ_CHUNKS;
-  const int c0 = (blockIdx.x % AQ_CHUNKS) * AQ_COLS;
+  const int gb = blockIdx.x - N;
+  const int h = gb / AQ_CHUNKS;
+  const int c0 = (gb % AQ_CHUNKS) * AQ_COLS;
   const uint16_t* w = w_uk + (int64_t)h * D_NOPE * D_C;
   for (int k = threadIdx.x; k < D_NOPE * (AQ_COLS / 8); k += blockDim.x) {
     const int j = k / (AQ_COLS / 8);
@@ -101,13 +107,15 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
   for (int n0 = 0; n0 < N; n0 += 16) {
     const int n = n0 + c;
     const uint16_t* src = o_lat + ((int64_t)n * H + h) * D_C + 8 * g;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // four independent accumulator chains keep the MFMA pipe busy
+    f32x4 acc4[4] = {};
 #pragma unroll
     for (int ks = 0; ks < D_C / 32; ++ks) {
       u32x4 bv = {0u, 0u, 0u, 0u};
       if (n < N) bv = *(const u32x4*)(src + 32 * ks);
-      acc = mfma16x16x32(af[ks], as_bf16x8(bv), acc);
+      acc4[ks & 3] = mfma16x16x32(af[ks], as_bf16x8(bv), acc4[ks & 3]);
     }
+    const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
     if (n < N) {
       u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
       *(u32x2*)(o + ((int64_t)n * H + h) * D_V + j0 + 4 * g) = out;

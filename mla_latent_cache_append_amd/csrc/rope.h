@@ -15,15 +15,25 @@
 
 namespace mla {
 
-__device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t x_pair, int pos, int i, double base) {
+// (cos, sin) of theta_i = pos * base^(-2i/64), fp64.
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, double base, double& c, double& s) {
+  const double theta = (double)pos * pow(base, -2.0 * (double)i / (double)D_ROPE);
+  sincos(theta, &s, &c);
+}
+
+// Rotate the bf16 pair packed in x_pair by (c, s); one rounding to bf16 each.
+__device__ __forceinline__ uint32_t rope_rotate_bf16(uint32_t x_pair, double c, double s) {
   const double x0 = (double)bf16_to_f32((uint16_t)(x_pair & 0xffffu));
   const double x1 = (double)bf16_to_f32((uint16_t)(x_pair >> 16));
-  const double theta = (double)pos * pow(base, -2.0 * (double)i / (double)D_ROPE);
-  double s, c;
-  sincos(theta, &s, &c);
   const double y0 = x0 * c - x1 * s;
   const double y1 = x1 * c + x0 * s;
   return (uint32_t)f64_to_bf16(y0) | ((uint32_t)f64_to_bf16(y1) << 16);
+}
+
+__device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t x_pair, int pos, int i, double base) {
+  double c, s;
+  rope_cos_sin(pos, i, base, c, s);
+  return rope_rotate_bf16(x_pair, c, s);
 }
 
 }  // namespace mla
