@@ -62,7 +62,7 @@ def traffic_from(fetch_dir: str, write_dir: str, workload: str) -> dict:
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            key = ("split" if "attn_pair" in name or "attn_cols" in name else
+            key = ("split" if any(k in name for k in ("attn_own", "attn_rows", "attn_cols")) else
                    "combine" if "attn_combine" in name else
                    "copy" if "copyBuffer" in name else None)
             if key:

@@ -19,6 +19,13 @@ HIPCC_FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
+    # the attention kernel includes instruction sequences written by a generator
+    sys.path.insert(0, CSRC)
+    try:
+        import gen_own_asm
+    finally:
+        sys.path.pop(0)
+    gen_own_asm.main()
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]

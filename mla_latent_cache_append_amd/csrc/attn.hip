@@ -35,6 +35,7 @@
 //    merges in a fixed order (deterministic, no atomics).
 #include "common.h"
 #include "kernels.h"
+#include "own_asm.inc"
 
 namespace mla {
 
@@ -170,12 +171,6 @@ __device__ __forceinline__ void load_tile(const uint16_t* pool, int blk, int n_v
 // log2 units, so probabilities stay below 2^8 (exact range for bf16 and fp32)
 // and the accumulators are touched outside the MFMAs only on rare tiles.
 constexpr float RESCALE_LOG2 = 8.f;
-
-__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
-  typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
-  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 // Online-softmax update of RB row blocks from this tile's scores, given as the
 // 16 (NK = 2 k-blocks x 8) values per lane in PV k-slot order. Returns the
@@ -522,11 +517,12 @@ constexpr int RSTAGE = 3;                       // LDS stages of half tiles
 
 // Half-tile LDS layout: 16-byte chunks ordered [tg 4][cg 9][tl 8][cl 8] for
 // token t = 8 tg + tl, feature chunk c = 8 cg + cl, cl stored XOR swz2(t).
-// For any 16 consecutive tokens and one chunk (K reads) and for any 16 tokens
-// x 2 chunks (transposed V reads) the accesses cover all 16 bank groups.
+// With 64 banks of 4 bytes (16 groups of 16 bytes), the 16 consecutive tokens
+// of one chunk (a K read) land on 16 distinct groups, and so do the 4 tokens
+// x 4 aligned chunks that 32 lanes of a transposed V read cover.
 __device__ __forceinline__ int swz2(int t) {
   const int tl = t & 7;
-  return ((tl >> 1) & 1) | (((tl >> 2) & 1) << 2) | (((t >> 3) & 1) << 1);
+  return (((tl >> 1) & 1) << 2) | ((tl >> 2) & 1) | (((t >> 3) & 1) << 1);
 }
 __device__ __forceinline__ uint32_t ht_off(int t, int c) {
   return (uint32_t)((((t >> 3) * 9 + (c >> 3)) * 64 + (t & 7) * 8 + ((c & 7) ^ swz2(t))) * 16);
@@ -810,6 +806,268 @@ __global__ __launch_bounds__(256 * NH, 1) void attn_rows_kernel(AttnArgs a) {
   }
 }
 
+// =================================================================== own kernel
+//
+// Rows >= 96 per sequence (e.g. 128 heads): a workgroup owns 128 query rows
+// of one key range with one wave per SIMD, and wave w owns rows 32 w .. +31
+// end to end. It holds their whole query (576 features, 144 VGPRs) and their
+// whole output accumulator (O^T, 512 columns, 256 AGPRs), forms the scores
+// S^T = K Q^T, runs the online softmax in registers and accumulates
+// O^T += V^T P^T with the probabilities taken straight from the score
+// registers. Waves share only the half tiles in LDS: one barrier per half
+// tile. Iteration e accumulates half tile e and scores half tile e+1 in one
+// branch-free region (two independent MFMA streams, the softmax VALU work
+// under them). Products are v_mfma_f32_32x32x16_bf16:
+//   A (32x16): a[j] = A[l % 32][8 (l / 32) + j]
+//   B (16x32): b[j] = B[8 (l / 32) + j][l % 32]
+//   D (32x32): d[i] = D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]
+// so score value i of lane l is token 8 (i / 4) + 4 (l / 32) + i % 4 of the
+// half tile for row l % 32, and values 8 kk .. 8 kk + 7 are exactly the PV
+// B operand of token block kk (k-slot 8 (l / 32) + u <-> token 16 kk +
+// 8 (u / 4) + 4 (l / 32) + u % 4), with V^T read in the same token order.
+
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Maximum over lanes l and l ^ 32 by the gfx950 lane-swap instruction (VALU,
+// no LDS round trip). With both operands equal, the two results hold the
+// wave's two halves in opposite order, so their maximum is the same either way.
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+}
+
+constexpr int OSTAGE = 4;                 // LDS stages: two read per iteration, two in flight
+constexpr int KSTEPS16 = D_K / 16;        // k-steps of 16 features
+
+// Scale an accumulator held in AGPRs. The empty asm statements pin the value
+// to the AGPR class on both sides of the multiply, so that this rarely taken
+// path does not lead the register allocator to move every accumulator of the
+// kernel into VGPRs.
+__device__ __forceinline__ void scale_acc(f32x16& acc, float f) {
+  f32x16 t = acc;
+  asm volatile("" : "+a"(t));
+  t *= f;
+  acc = t;
+  asm volatile("" : "+a"(acc));
+}
+
+__global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[OSTAGE * HT_BYTES];
+  lds_char* stages = (lds_char*)smem;
+
+  const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int c32 = lane & 31, h = lane >> 5;
+
+  int unit = blockIdx.x;
+  if (a.n_rg > 1) {
+    const int full = (int)(gridDim.x / 64) * 64;
+    if (unit < full) {
+      const int loc = unit & 63;
+      unit = (unit & ~63) + (loc & 7) * 8 + (loc >> 3);
+    }
+  }
+  const int w = unit / a.n_rg;
+  const int rg = unit - w * a.n_rg;
+  const int64_t T = plan_total_tiles(a.seq_lens, a.B, a.max_blocks);
+  if (T == 0) return;
+  const int64_t x_begin = (int64_t)w * T / a.width;
+  const int64_t x_end = (int64_t)(w + 1) * T / a.width;
+  if (x_begin >= x_end) return;
+  int b;
+  int64_t seq_start;
+  plan_find(a.seq_lens, a.B, a.max_blocks, x_begin, b, seq_start);
+
+  const int r = rg * 128 + 32 * wave + c32;   // this lane's query row within the sequence
+  // K fragment of k-step ks (token c32, chunk 2 ks + h) sits at
+  // (stage + kbase) ^ ((ks & 3) << 5), plus (ks >> 2) * 1024: within a group
+  // of 8 chunks the chunk index only enters the swizzled slot bits 5..6, and
+  // stage bases are multiples of 128 bytes.
+  const uint32_t kbase = ht_off(c32, h);
+  // V^T fragment of column block cb (columns 32 cb .. +31) and token block kk:
+  //   tr(((stage + vbase[0]) ^ ((cb & 1) << 6)) + kk * 18432 + (cb >> 1) * 1024)          tokens 16 kk + 4 h .. +3
+  //   tr(((stage + vbase[1]) ^ ((cb & 1) << 6)) + kk * 18432 + 9216 + (cb >> 1) * 1024)   tokens 16 kk + 8 + 4 h .. +3
+  uint32_t vbase[2];
+  {
+    const int i16 = lane & 15, q = lane >> 4;
+    const int tl = 4 * (q >> 1) + (i16 >> 2);
+    const int e = 2 * (q & 1) + ((i16 & 3) >> 1);
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+      vbase[rr] = ht_off(8 * rr + tl, e) - (uint32_t)(rr * 9216) + 8 * (i16 & 1);
+  }
+  const uint32_t goff = (uint32_t)((lane >> 3) * ROW_BYTES + ((lane & 7) ^ swz2(8 * wave + (lane >> 3))) * 16);
+
+  int64_t x = x_begin;
+  while (x < x_end && b < a.B) {
+    const int L = uni(a.seq_lens[b]);
+    const int ntiles = tiles_of(L, a.max_blocks);
+    const int64_t seg_end = min(x_end, seq_start + ntiles);
+    const int k_first = (int)(x - seq_start);
+    const int k_last = (int)(seg_end - seq_start);
+    const bool whole = (x == seq_start) && (seg_end == seq_start + ntiles);
+    bool bad = L > a.max_blocks * BLOCK;
+    const int key_end = min(k_last * BLOCK, L);
+    const int e0 = 2 * k_first, e1 = (key_end + HT_TOK - 1) / HT_TOK;
+
+    // query fragments (B operand of S^T): row r, features 16 ks + 8 h .. +7
+    u32x4 qf[KSTEPS16];
+    {
+      const bool valid = r < a.rows;
+      const uint16_t* qrow = a.q + ((int64_t)b * a.rows + (valid ? r : 0)) * D_K + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS16; ++ks) {
+        u32x4 v = *(const u32x4*)(qrow + 16 * ks);
+        if (!valid) v = u32x4{0u, 0u, 0u, 0u};
+        qf[ks] = v;
+      }
+    }
+    const int lim = r < a.rows ? L - a.Lq + r / a.H : -1;   // last key row r sees
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 o[16];
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
+
+    // Block ids come through scalar loads (lgkmcnt, not vmcnt, so reading one
+    // never drains the tile loads in flight), one tile ahead of their use.
+    const __attribute__((address_space(4))) int32_t* bt =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)b * a.max_blocks);
+    int kq = k_first;
+    int blk_q = bt[kq];
+    int blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
+    auto issue = [&](int e) {
+      const int k = e >> 1;
+      if (k != kq) {   // tiles advance one at a time
+        kq = k;
+        blk_q = blk_q1;
+        blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
+      }
+      const int blk = blk_q;
+      if (blk < 0 || blk >= a.num_blocks) {
+        bad = true;
+        return;
+      }
+      const int n_valid = min(HT_TOK, L - e * HT_TOK);
+      const sgpr_x4 rsrc =
+          buffer_rsrc((const char*)a.pool + (int64_t)blk * TILE_BYTES + (e & 1) * HT_BYTES, n_valid * ROW_BYTES);
+      const uint32_t dst = lds_addr(stages + (e % OSTAGE) * HT_BYTES + wave * 9 * 1024);
+#pragma unroll
+      for (int cg = 0; cg < 9; ++cg)
+        buffer_load_lds_16(rsrc, goff, wave * 8 * ROW_BYTES + cg * 128, dst + cg * 1024);
+    };
+
+    // LDS addresses of the K fragments (stage of half tile e) and of the V^T
+    // fragments (stage of half tile e), as the instruction sequences take them
+    uint32_t ka[4], va[4];
+    auto k_addr = [&](int e) {
+      const uint32_t sb = lds_addr(stages + (e % OSTAGE) * HT_BYTES) + kbase;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ka[q] = sb ^ (uint32_t)(q << 5);
+    };
+    auto v_addr = [&](int e) {
+      const uint32_t sb = lds_addr(stages + (e % OSTAGE) * HT_BYTES);
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int c1 = 0; c1 < 2; ++c1) va[c1 + 2 * rr] = (sb + vbase[rr]) ^ (uint32_t)(c1 << 6);
+    };
+
+    // ---- pipeline: iteration e reads stage e (V) and e+1 (K); e+2 and e+3 in flight.
+    // The instruction sequences (own_asm.inc) per iteration:
+    //   A: online softmax of half tile e from its scores (mask, row max,
+    //      probabilities, alpha, l) under the score MFMAs of e+1, k-steps 0..17;
+    //   B: score MFMAs of e+1, k-steps 18..35, with the PV MFMAs of e,
+    //      O^T[col][row] += V^T[col][token] P^T[token][row].
+    // On the last half tile the scores rerun on stage e and are discarded.
+    for (int e = e0; e < min(e1, e0 + OSTAGE - 1); ++e) issue(e);
+    if (e1 - e0 >= 3) wait_vmem_n<18>();
+    else if (e1 - e0 == 2) wait_vmem_n<9>();
+    else wait_vmem_n<0>();
+    lds_barrier();
+    f32x16 sn;
+    u32x4 kb[4];
+    k_addr(e0);
+    asm volatile(OWN_ASM_PRO : [sn] "=&v"(sn), OWN_OPS_KB_OUT : OWN_OPS_Q0_35, OWN_OPS_KA : "memory");
+    for (int e = e0; e < e1; ++e) {
+      const bool more = e + 1 < e1;
+      if (more) {
+        // stage e+1 complete; only the load of e+2 was issued after it
+        if (e + 2 < e1) wait_vmem_n<9>();
+        else wait_vmem_n<0>();
+      }
+      lds_barrier();                       // stage e+1 visible; stage e-1 free
+      if (e + OSTAGE - 1 < e1) issue(e + OSTAGE - 1);
+      k_addr(more ? e + 1 : e);
+      v_addr(e);
+      const int lr = lim - (e * HT_TOK + 4 * h);
+      float s[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = sn[i];
+      float alpha;
+      uint32_t p[8];
+      asm volatile(OWN_ASM_A
+                   : OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "=&v"(alpha), OWN_OPS_P,
+                     [sn] "=&v"(sn), OWN_OPS_KB_OUT
+                   : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "v"(a.scale_log2)
+                   : OWN_CLOB_A, "vcc", "memory");
+      if (e > e0 && __any(alpha != 1.f)) {
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
+      }
+      const u32x4 pf0 = {p[0], p[1], p[2], p[3]}, pf1 = {p[4], p[5], p[6], p[7]};
+      asm volatile(OWN_ASM_B
+                   : OWN_OPS_O, [sn] "+v"(sn), OWN_OPS_KB_INOUT
+                   : OWN_OPS_Q18_35, OWN_OPS_KA, OWN_OPS_VA, [pf0] "v"(pf0), [pf1] "v"(pf1)
+                   : OWN_CLOB_B, "memory");
+    }
+
+    // ---- finish the segment
+    l_run += __shfl_xor(l_run, 32);
+    if (r < a.rows) {
+      const int64_t orow = (int64_t)b * a.rows + r;
+      if (whole) {
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float v0 = o[cb][4 * j] * inv, v1 = o[cb][4 * j + 1] * inv;
+            float v2 = o[cb][4 * j + 2] * inv, v3 = o[cb][4 * j + 3] * inv;
+            if (bad) v0 = v1 = v2 = v3 = NAN;
+            const u32x2 out = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            *(u32x2*)(a.o_lat + orow * D_C + 32 * cb + 8 * j + 4 * h) = out;
+          }
+        if (a.lse && h == 0) {
+          const float lv = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
+          a.lse[orow] = bad ? NAN : lv;
+        }
+      } else {
+        const int64_t prow = (int64_t)(w + b) * a.rows + r;
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f32x4 v = {o[cb][4 * j], o[cb][4 * j + 1], o[cb][4 * j + 2], o[cb][4 * j + 3]};
+            if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+            *(f32x4*)(a.ws_acc + prow * D_C + 32 * cb + 8 * j + 4 * h) = v;
+          }
+        if (h == 0) {
+          a.ws_ml[prow * 2 + 0] = bad ? NAN : m_run;
+          a.ws_ml[prow * 2 + 1] = bad ? NAN : l_run;
+        }
+      }
+    }
+    x = seg_end;
+    seq_start += ntiles;
+    ++b;
+    while (b < a.B && tiles_of(uni(a.seq_lens[b]), a.max_blocks) == 0) ++b;
+    lds_barrier();
+  }
+}
+
 // Merge the partials of each query row in range order. One wave per row,
 // 8 output columns per lane.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
@@ -919,7 +1177,7 @@ hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t n
   const dim3 grid(p.width * p.n_rg);
   switch (p.variant) {
     case V_ROWS128:
-      hipLaunchKernelGGL(attn_rows_kernel<2>, grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL(attn_own_kernel, grid, dim3(256), 0, stream, a);
       break;
     case V_ROWS64:
       hipLaunchKernelGGL(attn_rows_kernel<1>, grid, dim3(256), 0, stream, a);

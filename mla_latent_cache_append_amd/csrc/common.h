@@ -81,6 +81,13 @@ __device__ __forceinline__ i16x4 lds_read_tr16_b64(const __attribute__((address_
       (__attribute__((address_space(3))) i16x4*)(base + off));
 }
 
+// Two transposing reads (4 rows each) joined into one 8-element MFMA operand.
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Buffer resource (V#) for raw 16-byte loads of `bytes` bytes at `base`:
 // lanes whose offset + 16 exceeds `bytes` read zeros.
 typedef unsigned int sgpr_x4 __attribute__((ext_vector_type(4)));

@@ -17,21 +17,26 @@
 
 namespace mla {
 
-constexpr int AQ_COLS = 64;                  // latent columns per absorb workgroup
-constexpr int AQ_CHUNKS = D_C / AQ_COLS;     // 8 workgroups per head
-constexpr int AQ_LDS_STRIDE = D_NOPE + 8;    // padded row of the transposed W tile
+constexpr int AQ_COLS = 128;                 // latent columns per absorb workgroup
+constexpr int AQ_CHUNKS = D_C / AQ_COLS;     // 4 workgroups per head
+
+// The [128 j][128 c] slice of W_UK[h] sits in LDS row-major (256 bytes per
+// row) with 16-byte chunk k of row j stored at k ^ aq_swz(j): the 32 lanes of
+// one transposing read cycle (rows 4i .. 4i+3 and 4i+8 .. 4i+11, two chunks
+// each) then hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int aq_swz(int j) { return 2 * (j & 3) + 8 * ((j >> 3) & 1); }
 
 // Blocks 0..N-1 rotate q_pe (one token each, dispatched first); the others
-// each compute a [N x 64] column slice of q_lat for one head.
-// W_UK[h] is stored [128 j][512 c] (rows of nn.Linear(d_c, H*d_nope).weight);
-// the contraction runs over j, so each workgroup stages a [128 x 64] slice
-// transposed into LDS as wt[c][j], making each MFMA A fragment (8 consecutive
-// j of one c) a 16-byte LDS read.
+// each compute a [N x 128] column slice of q_lat for one head.
+// W_UK[h] is stored [128 j][512 c] (rows of nn.Linear(d_c, H*d_nope).weight)
+// and the contraction runs over j, its row index: the MFMA A operand
+// (8 consecutive j of one column c) comes from two transposing LDS reads
+// (ds_read_b64_tr_b16) of the row-major slice.
 __global__ __launch_bounds__(256) void absorb_q_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const int32_t* __restrict__ pos, const uint16_t* __restrict__ w_uk,
     uint16_t* __restrict__ q_out, int N, int H, double base) {
-  __shared__ __attribute__((aligned(16))) uint16_t wt[AQ_COLS * AQ_LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) char wl[D_NOPE * AQ_COLS * 2];
   __shared__ double rot[D_ROPE / 2][2];
   if ((int)blockIdx.x < N) {
     // rope of one query token, all heads: q_out[n][h][512 + 2i .. +1]. The 32
@@ -40,48 +45,88 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
     const int n = blockIdx.x;
     if (threadIdx.x < D_ROPE / 2) rope_cos_sin(pos[n], threadIdx.x, base, rot[threadIdx.x][0], rot[threadIdx.x][1]);
     __syncthreads();
-    for (int k = threadIdx.x; k < H * (D_ROPE / 2); k += blockDim.x) {
-      const int h = k / (D_ROPE / 2), i = k % (D_ROPE / 2);
-      const int64_t rowq = (int64_t)n * H + h;
-      const uint32_t x = *(const uint32_t*)(q_pe + rowq * D_ROPE + 2 * i);
-      *(uint32_t*)(q_out + rowq * D_K + D_C + 2 * i) = rope_rotate_bf16(x, rot[i][0], rot[i][1]);
+    // pair k = (head k / 32, pair k % 32); eight pairs per thread per pass, all
+    // loads issued before the first rotation
+    constexpr int U = 8;
+    const int npairs = H * (D_ROPE / 2);
+    for (int k0 = 0; k0 < npairs; k0 += U * 256) {
+      uint32_t x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + u * 256 + threadIdx.x;
+        x[u] = k < npairs ? *(const uint32_t*)(q_pe + (int64_t)n * H * D_ROPE + 2 * k) : 0u;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + u * 256 + threadIdx.x;
+        if (k < npairs) {
+          const int h = k / (D_ROPE / 2), i = k % (D_ROPE / 2);
+          *(uint32_t*)(q_out + ((int64_t)n * H + h) * D_K + D_C + 2 * i) =
+              rope_rotate_bf16(x[u], rot[i][0], rot[i][1]);
+        }
+      }
     }
     return;
   }
   const int gb = blockIdx.x - N;
   const int h = gb / AQ_CHUNKS;
   const int c0 = (gb % AQ_CHUNKS) * AQ_COLS;
-  const uint16_t* w = w_uk + (int64_t)h * D_NOPE * D_C;
-  for (int k = threadIdx.x; k < D_NOPE * (AQ_COLS / 8); k += blockDim.x) {
-    const int j = k / (AQ_COLS / 8);
-    const int cc = (k % (AQ_COLS / 8)) * 8;
-    const u32x4 v = *(const u32x4*)(w + (int64_t)j * D_C + c0 + cc);
+  const uint16_t* w = w_uk + (int64_t)h * D_NOPE * D_C + c0;
+  __attribute__((address_space(3))) char* wls = (__attribute__((address_space(3))) char*)wl;
+  {
+    // 2048 chunks of 16 bytes, eight per thread: all loads in flight before the LDS writes
+    constexpr int PER = D_NOPE * (AQ_COLS / 8) / 256;
+    u32x4 v[PER];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      wt[(cc + e) * AQ_LDS_STRIDE + j] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    for (int u = 0; u < PER; ++u) {
+      const int k = u * 256 + threadIdx.x, j = k >> 4, ch = k & 15;
+      v[u] = *(const u32x4*)(w + (int64_t)j * D_C + ch * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int k = u * 256 + threadIdx.x, j = k >> 4, ch = k & 15;
+      *(__attribute__((address_space(3))) u32x4*)(wls + j * 256 + ((ch ^ aq_swz(j)) << 4)) = v[u];
+    }
   }
   __syncthreads();
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
-  // A = W^T[M = column][K = j]: this wave's 16 columns, 4 k-steps of 32.
-  bf16x8 af[D_NOPE / 32];
+  // A = W^T[M = column][K = j]: this wave's two 16-column blocks
+  // (c0 + 32 wave + 16 cb + c), k-step ks covers j = 32 ks .. +31 and lane
+  // group g its rows 32 ks + 8 g .. +7.
+  bf16x8 af[2][D_NOPE / 32];
 #pragma unroll
-  for (int ks = 0; ks < D_NOPE / 32; ++ks)
-    af[ks] = as_bf16x8(*(const u32x4*)&wt[(16 * wave + c) * AQ_LDS_STRIDE + 32 * ks + 8 * g]);
-  for (int n0 = 0; n0 < N; n0 += 16) {
-    const int n = n0 + c;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < 2; ++cb) {
+    const int col = 32 * wave + 16 * cb + 4 * (c & 3);   // first column of this lane's 8-byte piece
+    const int ch = col >> 3, half = (col >> 2) & 1;
 #pragma unroll
     for (int ks = 0; ks < D_NOPE / 32; ++ks) {
-      u32x4 bv = {0u, 0u, 0u, 0u};
-      if (n < N) bv = *(const u32x4*)(q_nope + ((int64_t)n * H + h) * D_NOPE + 32 * ks + 8 * g);
-      acc = mfma16x16x32(af[ks], as_bf16x8(bv), acc);
+      const int r0 = 32 * ks + 8 * g + (c >> 2), r1 = r0 + 4;
+      const i16x4 v0 = lds_read_tr16_b64(wls, r0 * 256 + ((ch ^ aq_swz(r0)) << 4) + 8 * half);
+      const i16x4 v1 = lds_read_tr16_b64(wls, r1 * 256 + ((ch ^ aq_swz(r1)) << 4) + 8 * half);
+      af[cb][ks] = join_tr(v0, v1);
     }
-    if (n < N) {
-      // lane holds columns c0 + 16 wave + 4g + i (i = 0..3) of token n
-      u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-      *(u32x2*)(q_out + ((int64_t)n * H + h) * D_K + c0 + 16 * wave + 4 * g) = out;
+  }
+  for (int n0 = 0; n0 < N; n0 += 16) {
+    const int n = n0 + c;
+    // lanes past the last token load a valid row; their columns are not stored
+    const uint16_t* src = q_nope + ((int64_t)min(n, N - 1) * H + h) * D_NOPE + 8 * g;
+    bf16x8 bq[D_NOPE / 32];
+#pragma unroll
+    for (int ks = 0; ks < D_NOPE / 32; ++ks) bq[ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
+    __builtin_amdgcn_sched_barrier(0);   // every load in flight before the first product
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D_NOPE / 32; ++ks) acc = mfma16x16x32(af[cb][ks], bq[ks], acc);
+      if (n < N) {
+        // lane holds columns c0 + 32 wave + 16 cb + 4 g + i (i = 0..3) of token n
+        const u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        *(u32x2*)(q_out + ((int64_t)n * H + h) * D_K + c0 + 32 * wave + 16 * cb + 4 * g) = out;
+      }
     }
   }
 }
@@ -106,15 +151,16 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
   for (int ks = 0; ks < D_C / 32; ++ks) af[ks] = as_bf16x8(*(const u32x4*)(w + 32 * ks + 8 * g));
   for (int n0 = 0; n0 < N; n0 += 16) {
     const int n = n0 + c;
-    const uint16_t* src = o_lat + ((int64_t)n * H + h) * D_C + 8 * g;
+    // lanes past the last token load a valid row; their outputs are not stored
+    const uint16_t* src = o_lat + ((int64_t)min(n, N - 1) * H + h) * D_C + 8 * g;
+    bf16x8 bv[D_C / 32];
+#pragma unroll
+    for (int ks = 0; ks < D_C / 32; ++ks) bv[ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
+    __builtin_amdgcn_sched_barrier(0);   // every load in flight before the first product
     // four independent accumulator chains keep the MFMA pipe busy
     f32x4 acc4[4] = {};
 #pragma unroll
-    for (int ks = 0; ks < D_C / 32; ++ks) {
-      u32x4 bv = {0u, 0u, 0u, 0u};
-      if (n < N) bv = *(const u32x4*)(src + 32 * ks);
-      acc4[ks & 3] = mfma16x16x32(af[ks], as_bf16x8(bv), acc4[ks & 3]);
-    }
+    for (int ks = 0; ks < D_C / 32; ++ks) acc4[ks & 3] = mfma16x16x32(af[ks], bv[ks], acc4[ks & 3]);
     const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
     if (n < N) {
       u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};

@@ -1,0 +1,214 @@
+"""Writes own_asm.inc: the instruction sequences of the 128-row attention
+kernel's inner loop (attn_own_kernel in attn.hip), as inline-asm templates.
+
+The loop body is emitted instruction by instruction so that the schedule is
+exactly the one intended: LDS operand reads issued several MFMAs ahead of
+their use with exact lgkmcnt waits, the softmax VALU work interleaved with the
+score MFMAs, and no register traffic between the accumulators and VGPRs.
+Register allocation stays with the compiler through named operands; only a
+few short-lived temporaries are fixed registers (declared as clobbers).
+
+Three templates:
+  OWN_ASM_PRO  scores of the first half tile of a segment (36 k-steps)
+  OWN_ASM_A    softmax of half tile e (from its scores) interleaved with the
+               score MFMAs of half tile e+1, k-steps 0..17; leaves the K
+               fragments of k-steps 18..21 loaded
+  OWN_ASM_B    score MFMAs of half tile e+1, k-steps 18..35, interleaved with
+               the 32 PV MFMAs of half tile e (V^T fragments read transposed)
+
+Operand names and layouts are those of attn_own_kernel; the MFMA is
+v_mfma_f32_32x32x16_bf16 throughout. Run: python gen_own_asm.py (the build
+runs it before compiling).
+"""
+
+import os
+
+KSTEPS = 36          # 576 features / 16
+A_STEPS = 18         # score k-steps in template A
+PF = 4               # K / V fragments in flight
+NEG_INF = "0xff800000"
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+# fixed temporaries (clobbered): A uses TA, B uses the V ring
+TA = ["v%d" % r for r in range(250, 256)]
+VRING = [("v[%d:%d]" % (240 + 4 * i, 240 + 4 * i + 1), "v[%d:%d]" % (240 + 4 * i + 2, 240 + 4 * i + 3),
+          "v[%d:%d]" % (240 + 4 * i, 240 + 4 * i + 3)) for i in range(PF)]
+GUARD = ["s_nop 7", "s_nop 7", "s_nop 7"]   # MFMA results settle before the compiler's code reads them
+
+
+class Seq:
+    """Instruction list with a model of the in-order LDS counter (lgkmcnt)."""
+
+    def __init__(self):
+        self.lines = []
+        self.pending = []          # tags of LDS reads not yet waited for, in issue order
+
+    def op(self, s):
+        self.lines.append(s)
+
+    def lds(self, s, tag):
+        assert len(self.pending) < 15, "too many LDS reads in flight for lgkmcnt"
+        self.lines.append(s)
+        self.pending.append(tag)
+
+    def need(self, tag):
+        if tag not in self.pending:
+            return
+        i = max(k for k, t in enumerate(self.pending) if t == tag)
+        self.lines.append("s_waitcnt lgkmcnt(%d)" % (len(self.pending) - i - 1))
+        self.pending = self.pending[i + 1:]
+
+    def drain(self):
+        if self.pending:
+            self.lines.append("s_waitcnt lgkmcnt(0)")
+            self.pending = []
+
+    def text(self):
+        return "".join(l + "\\n\\t" for l in self.lines)
+
+
+def kread(seq, ks):
+    """K fragment of k-step ks into ring slot ks % 4 (16 bytes per lane)."""
+    seq.lds("ds_read_b128 %%[kb%d], %%[ka%d] offset:%d" % (ks % PF, ks & 3, (ks >> 2) * 1024), "K%d" % ks)
+
+
+def score_mfma(seq, ks, first):
+    seq.need("K%d" % ks)
+    seq.op("v_mfma_f32_32x32x16_bf16 %%[sn], %%[kb%d], %%[q%d], %s" % (ks % PF, ks, "0" if first else "%[sn]"))
+
+
+def vread(seq, j):
+    """V^T fragment of PV step j (column block j / 2, token block j % 2): two
+    transposing reads into the two halves of ring slot j % 4."""
+    cb, kk = j >> 1, j & 1
+    lo, hi, _ = VRING[j % PF]
+    seq.lds("ds_read_b64_tr_b16 %s, %%[va%d] offset:%d" % (lo, cb & 1, kk * 18432 + (cb >> 1) * 1024), "V%da" % j)
+    seq.lds("ds_read_b64_tr_b16 %s, %%[va%d] offset:%d" % (hi, 2 + (cb & 1), kk * 18432 + 9216 + (cb >> 1) * 1024),
+            "V%db" % j)
+
+
+def gen_pro():
+    s = Seq()
+    s.op("s_nop 1")
+    for ks in range(PF):
+        kread(s, ks)
+    for ks in range(KSTEPS):
+        score_mfma(s, ks, ks == 0)
+        if ks + PF < KSTEPS:
+            kread(s, ks + PF)
+    s.lines += GUARD
+    return s.text()
+
+
+def softmax_valu():
+    """Online softmax of one half tile for the lane's row, on operands s0..s15
+    (score value i = token 8 (i / 4) + 4 h + i % 4 of the half tile; lr = last
+    visible key minus the token of value 0). Returns the VALU instructions."""
+    t0, t1, t2, t3, t4, ninf = TA
+    # v_cndmask reads VCC over the constant bus, so -inf comes from a register
+    v = ["v_mov_b32 %s, %s" % (ninf, NEG_INF)]
+    for i in range(16):   # keys past the row's position -> -inf
+        off = 8 * (i >> 2) + (i & 3)
+        v.append("v_cmp_le_i32 vcc, %d, %%[lr]" % off)
+        v.append("v_cndmask_b32 %%[s%d], %s, %%[s%d], vcc" % (i, ninf, i))
+    v.append("v_max3_f32 %s, %%[s0], %%[s1], %%[s2]" % t0)
+    for i in range(3, 15, 2):
+        v.append("v_max3_f32 %s, %s, %%[s%d], %%[s%d]" % (t0, t0, i, i + 1))
+    v.append("v_max_f32 %s, %s, %%[s15]" % (t0, t0))
+    v.append("v_mov_b32 %s, %s" % (t1, t0))
+    v.append("s_nop 1")
+    v.append("v_permlane32_swap_b32 %s, %s" % (t0, t1))      # halves of the wave swapped
+    v.append("v_max_f32 %s, %s, %s" % (t0, t0, t1))            # row max over both halves
+    v.append("v_mul_f32 %s, %s, %%[scale]" % (t0, t0))        # in log2 units
+    v.append("v_add_f32 %s, 0x41000000, %%[mrun]" % t1)       # running max + 8
+    v.append("v_cmp_gt_f32 vcc, %s, %s" % (t0, t1))
+    v.append("v_cndmask_b32 %s, %%[mrun], %s, vcc" % (t2, t0))  # new max
+    v.append("v_sub_f32 %s, %%[mrun], %s" % (t1, t2))
+    v.append("v_exp_f32 %s, %s" % (t1, t1))
+    v.append("v_cmp_neq_f32 vcc, %s, %%[mrun]" % t2)
+    v.append("v_cndmask_b32 %%[alpha], 1.0, %s, vcc" % t1)     # 1 unless the max moved
+    v.append("v_mov_b32 %%[mrun], %s" % t2)
+    v.append("v_cmp_neq_f32 vcc, %s, %s" % (NEG_INF, t2))
+    v.append("v_cndmask_b32 %s, 0, %s, vcc" % (t3, t2))        # reference: 0 while nothing is visible
+    for i in range(16):
+        v.append("v_fma_f32 %%[s%d], %%[s%d], %%[scale], -%s" % (i, i, t3))
+        v.append("v_exp_f32 %%[s%d], %%[s%d]" % (i, i))
+    v.append("v_add_f32 %s, %%[s0], %%[s1]" % t4)
+    for i in range(2, 16):
+        v.append("v_add_f32 %s, %s, %%[s%d]" % (t4, t4, i))
+    for j in range(8):
+        v.append("v_cvt_pk_bf16_f32 %%[p%d], %%[s%d], %%[s%d]" % (j, 2 * j, 2 * j + 1))
+    v.append("v_fma_f32 %%[lrun], %%[lrun], %%[alpha], %s" % t4)
+    return v
+
+
+def gen_a():
+    s = Seq()
+    s.op("s_nop 1")
+    for ks in range(PF):
+        kread(s, ks)
+    valu = softmax_valu()
+    per = (len(valu) + A_STEPS - 1) // A_STEPS
+    for ks in range(A_STEPS):
+        score_mfma(s, ks, ks == 0)
+        kread(s, ks + PF)                 # up to k-step 21: the first four of template B
+        for ins in valu[ks * per:(ks + 1) * per]:
+            s.op(ins)
+    s.drain()
+    s.lines += GUARD
+    return s.text()
+
+
+def gen_b():
+    s = Seq()
+    s.op("s_nop 1")
+    for j in range(PF):
+        vread(s, j)
+    for j in range(32):
+        if j < KSTEPS - A_STEPS:
+            ks = A_STEPS + j
+            score_mfma(s, ks, False)
+            if ks + PF < KSTEPS:
+                kread(s, ks + PF)
+        s.need("V%db" % j)
+        s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %%[pf%d], %%[o%d]" % (j >> 1, VRING[j % PF][2], j & 1, j >> 1))
+        if j + PF < 32:
+            vread(s, j + PF)
+    s.drain()
+    s.lines += GUARD
+    return s.text()
+
+
+def main():
+    out = os.path.join(HERE, "own_asm.inc")
+    body = ["// Generated by gen_own_asm.py; do not edit.", ""]
+    for name, text in (("OWN_ASM_PRO", gen_pro()), ("OWN_ASM_A", gen_a()), ("OWN_ASM_B", gen_b())):
+        body.append('#define %s "%s"' % (name, text))
+        body.append("")
+    # operand lists (names of attn_own_kernel's variables)
+    ops = {
+        "OWN_OPS_Q0_17": ", ".join('[q%d] "v"(qf[%d])' % (i, i) for i in range(A_STEPS)),
+        "OWN_OPS_Q18_35": ", ".join('[q%d] "v"(qf[%d])' % (i, i) for i in range(A_STEPS, KSTEPS)),
+        "OWN_OPS_Q0_35": ", ".join('[q%d] "v"(qf[%d])' % (i, i) for i in range(KSTEPS)),
+        "OWN_OPS_KA": ", ".join('[ka%d] "v"(ka[%d])' % (i, i) for i in range(4)),
+        "OWN_OPS_VA": ", ".join('[va%d] "v"(va[%d])' % (i, i) for i in range(4)),
+        "OWN_OPS_KB_OUT": ", ".join('[kb%d] "=&v"(kb[%d])' % (i, i) for i in range(PF)),
+        "OWN_OPS_KB_INOUT": ", ".join('[kb%d] "+v"(kb[%d])' % (i, i) for i in range(PF)),
+        "OWN_OPS_S": ", ".join('[s%d] "+v"(s[%d])' % (i, i) for i in range(16)),
+        "OWN_OPS_P": ", ".join('[p%d] "=&v"(p[%d])' % (i, i) for i in range(8)),
+        "OWN_OPS_O": ", ".join('[o%d] "+a"(o[%d])' % (i, i) for i in range(16)),
+        "OWN_CLOB_A": ", ".join('"%s"' % r for r in TA),
+        "OWN_CLOB_B": ", ".join('"v%d"' % r for r in range(240, 256)),
+    }
+    for name, text in ops.items():
+        body.append("#define %s %s" % (name, text))
+    body.append("")
+    new = "\n".join(body)
+    if not os.path.exists(out) or open(out).read() != new:
+        with open(out, "w") as f:
+            f.write(new)
+    return out
+
+
+if __name__ == "__main__":
+    print(main())
