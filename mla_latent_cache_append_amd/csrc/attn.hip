@@ -57,6 +57,16 @@ __device__ __forceinline__ int64_t uni64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
@@ -119,8 +129,8 @@ struct AttnArgs {
   const int32_t* seq_lens;      // [B]
   uint16_t* o_lat;              // [B*rows][512]
   float* lse;                   // [B*rows] or null
-  float* ws_ml;                 // [slots][rows][2]
-  float* ws_acc;                // [slots][rows][512]
+  float* ws_ml;                 // [slots][rows][2]: (m, l) of each partial, fp32
+  uint16_t* ws_acc;             // [slots][rows][512]: partial o_lat normalized by its l, bf16
   int64_t num_blocks;
   int max_blocks;
   int B, Lq, H, rows;
@@ -472,11 +482,13 @@ __global__ __launch_bounds__(256, 1) void attn_cols_kernel(AttnArgs a) {
         }
       } else {
         const int64_t prow = (int64_t)slot * a.rows + r;
+        const float inv = l_run[rb] > 0.f ? 1.f / l_run[rb] : 0.f;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          f32x4 v = o[rb][cb];
+          f32x4 v = o[rb][cb] * inv;
           if (bad) v = f32x4{NAN, NAN, NAN, NAN};
-          *(f32x4*)(a.ws_acc + prow * D_C + 16 * (cb0 + cb) + 4 * g) = v;
+          const u32x2 out = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *(u32x2*)(a.ws_acc + prow * D_C + 16 * (cb0 + cb) + 4 * g) = out;
         }
         if (g == 0 && (!CS || wave == 0)) {
           a.ws_ml[prow * 2 + 0] = bad ? NAN : m_run[rb];
@@ -786,11 +798,13 @@ __global__ __launch_bounds__(256 * NH, 1) void attn_rows_kernel(AttnArgs a) {
         }
       } else {
         const int64_t prow = (int64_t)(w + b) * a.rows + r;
+        const float inv = lr > 0.f ? 1.f / lr : 0.f;
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
-          f32x4 v = o[rb][cb];
+          f32x4 v = o[rb][cb] * inv;
           if (bad) v = f32x4{NAN, NAN, NAN, NAN};
-          *(f32x4*)(a.ws_acc + prow * D_C + 128 * r4 + 16 * cb + 4 * g) = v;
+          const u32x2 out = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *(u32x2*)(a.ws_acc + prow * D_C + 128 * r4 + 16 * cb + 4 * g) = out;
         }
         if (r4 == 0 && g == 0) {
           a.ws_ml[prow * 2 + 0] = bad ? NAN : mr;
@@ -913,18 +927,6 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     const int key_end = min(k_last * BLOCK, L);
     const int e0 = 2 * k_first, e1 = (key_end + HT_TOK - 1) / HT_TOK;
 
-    // query fragments (B operand of S^T): row r, features 16 ks + 8 h .. +7
-    u32x4 qf[KSTEPS16];
-    {
-      const bool valid = r < a.rows;
-      const uint16_t* qrow = a.q + ((int64_t)b * a.rows + (valid ? r : 0)) * D_K + 8 * h;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS16; ++ks) {
-        u32x4 v = *(const u32x4*)(qrow + 16 * ks);
-        if (!valid) v = u32x4{0u, 0u, 0u, 0u};
-        qf[ks] = v;
-      }
-    }
     const int lim = r < a.rows ? L - a.Lq + r / a.H : -1;   // last key row r sees
     float m_run = -INFINITY, l_run = 0.f;
     f32x16 o[16];
@@ -982,13 +984,29 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     //   B: score MFMAs of e+1, k-steps 18..35, with the PV MFMAs of e,
     //      O^T[col][row] += V^T[col][token] P^T[token][row].
     // On the last half tile the scores rerun on stage e and are discarded.
-    for (int e = e0; e < min(e1, e0 + OSTAGE - 1); ++e) issue(e);
-    if (e1 - e0 >= 3) wait_vmem_n<18>();
-    else if (e1 - e0 == 2) wait_vmem_n<9>();
-    else wait_vmem_n<0>();
+    // Stage e0 and the query go out together; the query's arrival is awaited
+    // (which also completes stage e0) before the next two stages are issued,
+    // so the first scores wait for one stage rather than three.
+    issue(e0);
+    // query fragments (B operand of S^T): row r, features 16 ks + 8 h .. +7
+    u32x4 qf[KSTEPS16];
+    {
+      const bool valid = r < a.rows;
+      const uint16_t* qrow = a.q + ((int64_t)b * a.rows + (valid ? r : 0)) * D_K + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS16; ++ks) {
+        u32x4 v = *(const u32x4*)(qrow + 16 * ks);
+        if (!valid) v = u32x4{0u, 0u, 0u, 0u};
+        qf[ks] = v;
+      }
+    }
+    // an empty statement reading every fragment: the compiler's wait for the
+    // query loads lands here, before the next copies are issued
+    asm volatile("" ::OWN_OPS_Q0_35);
+    for (int e = e0 + 1; e < min(e1, e0 + OSTAGE - 1); ++e) issue(e);
     lds_barrier();
     f32x16 sn;
-    u32x4 kb[4];
+    u32x4 kb[OWN_PF_K];
     k_addr(e0);
     asm volatile(OWN_ASM_PRO : [sn] "=&v"(sn), OWN_OPS_KB_OUT : OWN_OPS_Q0_35, OWN_OPS_KA : "memory");
     for (int e = e0; e < e1; ++e) {
@@ -1046,13 +1064,16 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
         }
       } else {
         const int64_t prow = (int64_t)(w + b) * a.rows + r;
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
         for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            f32x4 v = {o[cb][4 * j], o[cb][4 * j + 1], o[cb][4 * j + 2], o[cb][4 * j + 3]};
-            if (bad) v = f32x4{NAN, NAN, NAN, NAN};
-            *(f32x4*)(a.ws_acc + prow * D_C + 32 * cb + 8 * j + 4 * h) = v;
+            float v0 = o[cb][4 * j] * inv, v1 = o[cb][4 * j + 1] * inv;
+            float v2 = o[cb][4 * j + 2] * inv, v3 = o[cb][4 * j + 3] * inv;
+            if (bad) v0 = v1 = v2 = v3 = NAN;
+            const u32x2 out = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            *(u32x2*)(a.ws_acc + prow * D_C + 32 * cb + 8 * j + 4 * h) = out;
           }
         if (h == 0) {
           a.ws_ml[prow * 2 + 0] = bad ? NAN : m_run;
@@ -1095,26 +1116,48 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   if (w_lo == w_hi) return;  // one range held the whole sequence and wrote it
 
   // Ranges between w_lo and w_hi all lie inside sequence b, except empty ones
-  // (more workgroups than tiles), which wrote nothing and are skipped.
+  // (more workgroups than tiles), which wrote nothing and are skipped. They are
+  // taken 64 at a time: lane k reads (m, l) of range c + k, the wave reduces,
+  // and the partial rows are loaded eight at a time before their products.
   auto empty = [&](int w) { return (int64_t)w * T / a.width == (int64_t)(w + 1) * T / a.width; };
   float M = -INFINITY;
-  for (int w = w_lo; w <= w_hi; ++w)
-    if (!empty(w)) M = fmaxf(M, a.ws_ml[((int64_t)(w + b) * a.rows + r) * 2]);
+  for (int c = w_lo; c <= w_hi; c += 64) {
+    const int w = c + lane;
+    const float m = (w <= w_hi && !empty(w)) ? a.ws_ml[((int64_t)(w + b) * a.rows + r) * 2] : -INFINITY;
+    M = fmaxf(M, wave_max_f(m));
+  }
   const float Mref = M == -INFINITY ? 0.f : M;
+  // partial k holds o_k / l_k: weight it by l_k 2^(m_k - M)
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
-  for (int w = w_lo; w <= w_hi; ++w) {
-    if (empty(w)) continue;
-    const int64_t prow = (int64_t)(w + b) * a.rows + r;
-    const float m_k = a.ws_ml[prow * 2], l_k = a.ws_ml[prow * 2 + 1];
-    const float wt = __builtin_amdgcn_exp2f(m_k - Mref);
-    l += wt * l_k;
-    const f32x4* src = (const f32x4*)(a.ws_acc + prow * D_C + 8 * lane);
-    const f32x4 v0 = src[0], v1 = src[1];
+  for (int c = w_lo; c <= w_hi; c += 64) {
+    const int w = c + lane;
+    float wt = 0.f;
+    if (w <= w_hi && !empty(w)) {
+      const int64_t prow = (int64_t)(w + b) * a.rows + r;
+      wt = __builtin_amdgcn_exp2f(a.ws_ml[prow * 2] - Mref) * a.ws_ml[prow * 2 + 1];
+    }
+    l += wave_sum_f(wt);
+    const int cnt = min(64, w_hi - c + 1);
+    for (int k0 = 0; k0 < cnt; k0 += 8) {
+      u32x4 v[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] += wt * v0[i];
-      acc[4 + i] += wt * v1[i];
+      for (int u = 0; u < 8; ++u) {
+        // ranges past the last one read row c (in bounds); their weight is 0
+        const int k = k0 + u < cnt ? k0 + u : 0;
+        v[u] = *(const u32x4*)(a.ws_acc + ((int64_t)(c + k + b) * a.rows + r) * D_C + 8 * lane);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wk = k0 + u < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), k0 + u)) : 0.f;
+        if (wk != 0.f) {   // empty ranges hold no data
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += wk * bf16_to_f32((uint16_t)(v[u][i] & 0xffffu));
+            acc[2 * i + 1] += wk * bf16_to_f32((uint16_t)(v[u][i] >> 16));
+          }
+        }
+      }
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -1142,11 +1185,19 @@ AttnPlan plan_attention(int32_t B, int32_t Lq, int32_t H) {
   return p;
 }
 
+// Workspace: (m, l) of every partial in fp32, then the partials themselves
+// in bf16, normalized by their l, starting on a 256-byte boundary.
+static size_t ws_slots(int32_t B, int32_t Lq, int32_t H) {
+  return (size_t)plan_attention(B, Lq, H).width + (size_t)B;
+}
+static size_t ws_ml_bytes(int32_t B, int32_t Lq, int32_t H) {
+  const size_t bytes = ws_slots(B, Lq, H) * (size_t)Lq * (size_t)H * 2 * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
 size_t attention_workspace_bytes(int32_t B, int32_t Lq, int32_t H) {
   const AttnPlan p = plan_attention(B, Lq, H);
-  const size_t slots = (size_t)p.width + (size_t)B;
-  const size_t rows = (size_t)Lq * (size_t)H;
-  return slots * rows * (2 + D_C) * sizeof(float);
+  return ws_ml_bytes(B, Lq, H) + ws_slots(B, Lq, H) * (size_t)Lq * (size_t)H * D_C * sizeof(uint16_t);
 }
 
 hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t num_blocks,
@@ -1162,9 +1213,8 @@ hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t n
   a.seq_lens = seq_lens;
   a.o_lat = o_lat;
   a.lse = lse;
-  const size_t slots = (size_t)p.width + (size_t)B;
   a.ws_ml = (float*)workspace;
-  a.ws_acc = a.ws_ml + slots * (size_t)Lq * H * 2;
+  a.ws_acc = (uint16_t*)((char*)workspace + ws_ml_bytes(B, Lq, H));
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks;
   a.B = B;

@@ -109,23 +109,31 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
       af[cb][ks] = join_tr(v0, v1);
     }
   }
-  for (int n0 = 0; n0 < N; n0 += 16) {
-    const int n = n0 + c;
-    // lanes past the last token load a valid row; their columns are not stored
-    const uint16_t* src = q_nope + ((int64_t)min(n, N - 1) * H + h) * D_NOPE + 8 * g;
-    bf16x8 bq[D_NOPE / 32];
+  // two 16-token blocks per pass, all their loads in flight before the products
+  for (int n0 = 0; n0 < N; n0 += 32) {
+    bf16x8 bq[2][D_NOPE / 32];
 #pragma unroll
-    for (int ks = 0; ks < D_NOPE / 32; ++ks) bq[ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
-    __builtin_amdgcn_sched_barrier(0);   // every load in flight before the first product
+    for (int tb = 0; tb < 2; ++tb) {
+      // lanes past the last token load a valid row; their columns are not stored
+      const int n = min(n0 + 16 * tb + c, N - 1);
+      const uint16_t* src = q_nope + ((int64_t)n * H + h) * D_NOPE + 8 * g;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < D_NOPE / 32; ++ks) bq[tb][ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < D_NOPE / 32; ++ks) acc = mfma16x16x32(af[cb][ks], bq[ks], acc);
-      if (n < N) {
-        // lane holds columns c0 + 32 wave + 16 cb + 4 g + i (i = 0..3) of token n
-        const u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-        *(u32x2*)(q_out + ((int64_t)n * H + h) * D_K + c0 + 32 * wave + 16 * cb + 4 * g) = out;
+    for (int tb = 0; tb < 2; ++tb) {
+      const int n = n0 + 16 * tb + c;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D_NOPE / 32; ++ks) acc = mfma16x16x32(af[cb][ks], bq[tb][ks], acc);
+        if (n < N) {
+          // lane holds columns c0 + 32 wave + 16 cb + 4 g + i (i = 0..3) of token n
+          const u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+          *(u32x2*)(q_out + ((int64_t)n * H + h) * D_K + c0 + 32 * wave + 16 * cb + 4 * g) = out;
+        }
       }
     }
   }
@@ -149,22 +157,30 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
   bf16x8 af[D_C / 32];
 #pragma unroll
   for (int ks = 0; ks < D_C / 32; ++ks) af[ks] = as_bf16x8(*(const u32x4*)(w + 32 * ks + 8 * g));
-  for (int n0 = 0; n0 < N; n0 += 16) {
-    const int n = n0 + c;
-    // lanes past the last token load a valid row; their outputs are not stored
-    const uint16_t* src = o_lat + ((int64_t)min(n, N - 1) * H + h) * D_C + 8 * g;
-    bf16x8 bv[D_C / 32];
+  // two 16-token blocks per pass, all their loads in flight before the products
+  for (int n0 = 0; n0 < N; n0 += 32) {
+    bf16x8 bv[2][D_C / 32];
 #pragma unroll
-    for (int ks = 0; ks < D_C / 32; ++ks) bv[ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
-    __builtin_amdgcn_sched_barrier(0);   // every load in flight before the first product
-    // four independent accumulator chains keep the MFMA pipe busy
-    f32x4 acc4[4] = {};
+    for (int tb = 0; tb < 2; ++tb) {
+      // lanes past the last token load a valid row; their outputs are not stored
+      const int n = min(n0 + 16 * tb + c, N - 1);
+      const uint16_t* src = o_lat + ((int64_t)n * H + h) * D_C + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < D_C / 32; ++ks) acc4[ks & 3] = mfma16x16x32(af[ks], bv[ks], acc4[ks & 3]);
-    const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-    if (n < N) {
-      u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-      *(u32x2*)(o + ((int64_t)n * H + h) * D_V + j0 + 4 * g) = out;
+      for (int ks = 0; ks < D_C / 32; ++ks) bv[tb][ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int n = n0 + 16 * tb + c;
+      // four independent accumulator chains keep the MFMA pipe busy
+      f32x4 acc4[4] = {};
+#pragma unroll
+      for (int ks = 0; ks < D_C / 32; ++ks) acc4[ks & 3] = mfma16x16x32(af[ks], bv[tb][ks], acc4[ks & 3]);
+      const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+      if (n < N) {
+        u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        *(u32x2*)(o + ((int64_t)n * H + h) * D_V + j0 + 4 * g) = out;
+      }
     }
   }
 }

@@ -25,14 +25,17 @@ import os
 
 KSTEPS = 36          # 576 features / 16
 A_STEPS = 18         # score k-steps in template A
-PF = 4               # K / V fragments in flight
+PF_K = int(os.environ.get("OWN_PF_K", "5"))   # K fragments in flight
+PF_V = int(os.environ.get("OWN_PF_V", "5"))   # V^T fragments in flight (two reads each)
+assert PF_K + 2 * PF_V <= 15, "LDS reads in flight must fit lgkmcnt"
 NEG_INF = "0xff800000"
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # fixed temporaries (clobbered): A uses TA, B uses the V ring
 TA = ["v%d" % r for r in range(250, 256)]
-VRING = [("v[%d:%d]" % (240 + 4 * i, 240 + 4 * i + 1), "v[%d:%d]" % (240 + 4 * i + 2, 240 + 4 * i + 3),
-          "v[%d:%d]" % (240 + 4 * i, 240 + 4 * i + 3)) for i in range(PF)]
+VR0 = 256 - 4 * PF_V
+VRING = [("v[%d:%d]" % (VR0 + 4 * i, VR0 + 4 * i + 1), "v[%d:%d]" % (VR0 + 4 * i + 2, VR0 + 4 * i + 3),
+          "v[%d:%d]" % (VR0 + 4 * i, VR0 + 4 * i + 3)) for i in range(PF_V)]
 GUARD = ["s_nop 7", "s_nop 7", "s_nop 7"]   # MFMA results settle before the compiler's code reads them
 
 
@@ -68,20 +71,20 @@ class Seq:
 
 
 def kread(seq, ks):
-    """K fragment of k-step ks into ring slot ks % 4 (16 bytes per lane)."""
-    seq.lds("ds_read_b128 %%[kb%d], %%[ka%d] offset:%d" % (ks % PF, ks & 3, (ks >> 2) * 1024), "K%d" % ks)
+    """K fragment of k-step ks into ring slot ks % PF_K (16 bytes per lane)."""
+    seq.lds("ds_read_b128 %%[kb%d], %%[ka%d] offset:%d" % (ks % PF_K, ks & 3, (ks >> 2) * 1024), "K%d" % ks)
 
 
 def score_mfma(seq, ks, first):
     seq.need("K%d" % ks)
-    seq.op("v_mfma_f32_32x32x16_bf16 %%[sn], %%[kb%d], %%[q%d], %s" % (ks % PF, ks, "0" if first else "%[sn]"))
+    seq.op("v_mfma_f32_32x32x16_bf16 %%[sn], %%[kb%d], %%[q%d], %s" % (ks % PF_K, ks, "0" if first else "%[sn]"))
 
 
 def vread(seq, j):
     """V^T fragment of PV step j (column block j / 2, token block j % 2): two
-    transposing reads into the two halves of ring slot j % 4."""
+    transposing reads into the two halves of ring slot j % PF_V."""
     cb, kk = j >> 1, j & 1
-    lo, hi, _ = VRING[j % PF]
+    lo, hi, _ = VRING[j % PF_V]
     seq.lds("ds_read_b64_tr_b16 %s, %%[va%d] offset:%d" % (lo, cb & 1, kk * 18432 + (cb >> 1) * 1024), "V%da" % j)
     seq.lds("ds_read_b64_tr_b16 %s, %%[va%d] offset:%d" % (hi, 2 + (cb & 1), kk * 18432 + 9216 + (cb >> 1) * 1024),
             "V%db" % j)
@@ -90,12 +93,12 @@ def vread(seq, j):
 def gen_pro():
     s = Seq()
     s.op("s_nop 1")
-    for ks in range(PF):
+    for ks in range(PF_K):
         kread(s, ks)
     for ks in range(KSTEPS):
         score_mfma(s, ks, ks == 0)
-        if ks + PF < KSTEPS:
-            kread(s, ks + PF)
+        if ks + PF_K < KSTEPS:
+            kread(s, ks + PF_K)
     s.lines += GUARD
     return s.text()
 
@@ -145,13 +148,13 @@ def softmax_valu():
 def gen_a():
     s = Seq()
     s.op("s_nop 1")
-    for ks in range(PF):
+    for ks in range(PF_K):
         kread(s, ks)
     valu = softmax_valu()
     per = (len(valu) + A_STEPS - 1) // A_STEPS
     for ks in range(A_STEPS):
         score_mfma(s, ks, ks == 0)
-        kread(s, ks + PF)                 # up to k-step 21: the first four of template B
+        kread(s, ks + PF_K)               # the last PF_K of these are template B's first k-steps
         for ins in valu[ks * per:(ks + 1) * per]:
             s.op(ins)
     s.drain()
@@ -162,18 +165,18 @@ def gen_a():
 def gen_b():
     s = Seq()
     s.op("s_nop 1")
-    for j in range(PF):
+    for j in range(PF_V):
         vread(s, j)
     for j in range(32):
         if j < KSTEPS - A_STEPS:
             ks = A_STEPS + j
             score_mfma(s, ks, False)
-            if ks + PF < KSTEPS:
-                kread(s, ks + PF)
+            if ks + PF_K < KSTEPS:
+                kread(s, ks + PF_K)
         s.need("V%db" % j)
-        s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %%[pf%d], %%[o%d]" % (j >> 1, VRING[j % PF][2], j & 1, j >> 1))
-        if j + PF < 32:
-            vread(s, j + PF)
+        s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %%[pf%d], %%[o%d]" % (j >> 1, VRING[j % PF_V][2], j & 1, j >> 1))
+        if j + PF_V < 32:
+            vread(s, j + PF_V)
     s.drain()
     s.lines += GUARD
     return s.text()
@@ -192,13 +195,14 @@ def main():
         "OWN_OPS_Q0_35": ", ".join('[q%d] "v"(qf[%d])' % (i, i) for i in range(KSTEPS)),
         "OWN_OPS_KA": ", ".join('[ka%d] "v"(ka[%d])' % (i, i) for i in range(4)),
         "OWN_OPS_VA": ", ".join('[va%d] "v"(va[%d])' % (i, i) for i in range(4)),
-        "OWN_OPS_KB_OUT": ", ".join('[kb%d] "=&v"(kb[%d])' % (i, i) for i in range(PF)),
-        "OWN_OPS_KB_INOUT": ", ".join('[kb%d] "+v"(kb[%d])' % (i, i) for i in range(PF)),
+        "OWN_OPS_KB_OUT": ", ".join('[kb%d] "=&v"(kb[%d])' % (i, i) for i in range(PF_K)),
+        "OWN_OPS_KB_INOUT": ", ".join('[kb%d] "+v"(kb[%d])' % (i, i) for i in range(PF_K)),
         "OWN_OPS_S": ", ".join('[s%d] "+v"(s[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_P": ", ".join('[p%d] "=&v"(p[%d])' % (i, i) for i in range(8)),
         "OWN_OPS_O": ", ".join('[o%d] "+a"(o[%d])' % (i, i) for i in range(16)),
         "OWN_CLOB_A": ", ".join('"%s"' % r for r in TA),
-        "OWN_CLOB_B": ", ".join('"v%d"' % r for r in range(240, 256)),
+        "OWN_CLOB_B": ", ".join('"v%d"' % r for r in range(VR0, 256)),
+        "OWN_PF_K": str(PF_K),
     }
     for name, text in ops.items():
         body.append("#define %s %s" % (name, text))

@@ -54,8 +54,10 @@ def test_workspace_size_is_host_arithmetic(nat):
     s1 = nat.mla_decode_workspace_size(d, 32, 1)
     s8 = nat.mla_decode_workspace_size(d, 16, 8)
     assert s1 > 0 and s8 > 0 and s1 % 4 == 0
-    # (range slots + sequences) x rows x (m, l, 512 accumulators) x 4 bytes
-    assert s1 % (128 * 514 * 4) == 0
+    # (range slots + sequences) x rows x ((m, l) in fp32 + 512 bf16 partials),
+    # the bf16 part starting on a 256-byte boundary
+    slots = s1 // (128 * (8 + 1024))
+    assert s1 == ((slots * 128 * 8 + 255) // 256) * 256 + slots * 128 * 1024
     bad = nat.mla_dims_default(128)
     bad.d_c = 256
     assert nat.mla_decode_workspace_size(bad, 32, 1) == 0
