@@ -855,6 +855,7 @@ __device__ __forceinline__ float max_xor32(float v) {
 }
 
 constexpr int OSTAGE = 4;                 // LDS stages: two read per iteration, two in flight
+constexpr int OUT_STRIDE = 1040;          // bytes per output row staged in LDS (1 KiB + 16: fewer bank conflicts)
 constexpr int KSTEPS16 = D_K / 16;        // k-steps of 16 features
 
 // Scale an accumulator held in AGPRs. The empty asm statements pin the value
@@ -876,14 +877,11 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
   const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c32 = lane & 31, h = lane >> 5;
 
+  // Workgroups are dealt to the 8 XCDs round-robin by id; give each XCD a
+  // contiguous run of work units, so the ranges of one sequence (and its query
+  // rows, which all of them load) share that XCD's L2.
   int unit = blockIdx.x;
-  if (a.n_rg > 1) {
-    const int full = (int)(gridDim.x / 64) * 64;
-    if (unit < full) {
-      const int loc = unit & 63;
-      unit = (unit & ~63) + (loc & 7) * 8 + (loc >> 3);
-    }
-  }
+  if ((gridDim.x & 7) == 0) unit = (unit & 7) * (int)(gridDim.x >> 3) + (unit >> 3);
   const int w = unit / a.n_rg;
   const int rg = unit - w * a.n_rg;
   const int64_t T = plan_total_tiles(a.seq_lens, a.B, a.max_blocks);
@@ -1042,40 +1040,44 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
                    : OWN_CLOB_B, "memory");
     }
 
-    // ---- finish the segment
+    // ---- finish the segment. Both outputs hold o / l in bf16 (the final
+    // o_lat, or a partial for the merge): each wave writes its 32 rows into
+    // LDS (the stages are free now), then every wave stores whole 1 KiB rows,
+    // one row per instruction.
     l_run += __shfl_xor(l_run, 32);
-    if (r < a.rows) {
-      const int64_t orow = (int64_t)b * a.rows + r;
-      if (whole) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      lds_barrier();                       // every wave is done with the stages
+      lds_char* orow_l = stages + (32 * wave + c32) * OUT_STRIDE + 8 * h;
 #pragma unroll
-        for (int cb = 0; cb < 16; ++cb)
+      for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float v0 = o[cb][4 * j] * inv, v1 = o[cb][4 * j + 1] * inv;
-            float v2 = o[cb][4 * j + 2] * inv, v3 = o[cb][4 * j + 3] * inv;
-            if (bad) v0 = v1 = v2 = v3 = NAN;
-            const u32x2 out = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            *(u32x2*)(a.o_lat + orow * D_C + 32 * cb + 8 * j + 4 * h) = out;
-          }
-        if (a.lse && h == 0) {
-          const float lv = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
-          a.lse[orow] = bad ? NAN : lv;
+        for (int j = 0; j < 4; ++j) {
+          float v0 = o[cb][4 * j] * inv, v1 = o[cb][4 * j + 1] * inv;
+          float v2 = o[cb][4 * j + 2] * inv, v3 = o[cb][4 * j + 3] * inv;
+          if (bad) v0 = v1 = v2 = v3 = NAN;
+          *(__attribute__((address_space(3))) u32x2*)(orow_l + (32 * cb + 8 * j) * 2) =
+              u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         }
-      } else {
-        const int64_t prow = (int64_t)(w + b) * a.rows + r;
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-#pragma unroll
-        for (int cb = 0; cb < 16; ++cb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float v0 = o[cb][4 * j] * inv, v1 = o[cb][4 * j + 1] * inv;
-            float v2 = o[cb][4 * j + 2] * inv, v3 = o[cb][4 * j + 3] * inv;
-            if (bad) v0 = v1 = v2 = v3 = NAN;
-            const u32x2 out = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            *(u32x2*)(a.ws_acc + prow * D_C + 32 * cb + 8 * j + 4 * h) = out;
+      lds_barrier();
+      uint16_t* dst = whole ? a.o_lat + (int64_t)b * a.rows * D_C
+                            : a.ws_acc + (int64_t)(w + b) * a.rows * D_C;
+#pragma unroll 4
+      for (int i = 0; i < 32; ++i) {
+        const int rl = 32 * wave + i;            // row within the group
+        const int rr = rg * 128 + rl;            // row within the sequence
+        if (rr >= a.rows) break;
+        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(stages + rl * OUT_STRIDE + 16 * lane);
+        *(u32x4*)(dst + (int64_t)rr * D_C + 8 * lane) = v;
+      }
+      if (r < a.rows && h == 0) {
+        if (whole) {
+          if (a.lse) {
+            const float lv = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
+            a.lse[(int64_t)b * a.rows + r] = bad ? NAN : lv;
           }
-        if (h == 0) {
+        } else {
+          const int64_t prow = (int64_t)(w + b) * a.rows + r;
           a.ws_ml[prow * 2 + 0] = bad ? NAN : m_run;
           a.ws_ml[prow * 2 + 1] = bad ? NAN : l_run;
         }
