@@ -38,7 +38,8 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration for traffic)")
+                    help="also run a plain 1 GiB device read (a sum) and a 1 GiB device write (a fill), "
+                         "the calibration of the traffic counters")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="parse two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench "
                          "with --copy-calib into profiles/traffic_decode_attn.json, then exit")
@@ -50,8 +51,9 @@ COPY_BYTES = 1 << 30
 
 def traffic_from(fetch_dir: str, write_dir: str, workload: str) -> dict:
     """HBM bytes per mla_decode_attn launch from FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), each scaled by what the counter reads for a plain copy of
-    COPY_BYTES (the copy reads and writes COPY_BYTES each)."""
+    dispatch), each scaled by what the counter reads for a plain kernel of known
+    traffic: a sum over COPY_BYTES (reads them) for FETCH_SIZE, a fill of
+    COPY_BYTES (writes them) for WRITE_SIZE."""
     import csv
     import glob
 
@@ -64,12 +66,14 @@ def traffic_from(fetch_dir: str, write_dir: str, workload: str) -> dict:
             name = row["Kernel_Name"]
             key = ("split" if any(k in name for k in ("attn_own", "attn_rows", "attn_cols")) else
                    "combine" if "attn_combine" in name else
-                   "copy" if "copyBuffer" in name else None)
+                   "read" if "reduce_kernel" in name else
+                   "write" if "FillFunctor" in name else None)
             if key:
                 acc.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)
-        return {k: sum(v) / len(v) for k, v in acc.items()}
+        # calibration kernels: the largest dispatch (a reduction may add a small second pass)
+        return {k: (max(v) if k in ("read", "write") else sum(v) / len(v)) for k, v in acc.items()}
     fe, wr = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    f_scale, w_scale = COPY_BYTES / fe["copy"], COPY_BYTES / wr["copy"]
+    f_scale, w_scale = COPY_BYTES / fe["read"], COPY_BYTES / wr["write"]
     fetch = (fe["split"] + fe.get("combine", 0.0)) * f_scale
     write = (wr["split"] + wr.get("combine", 0.0)) * w_scale
     return {"workload": workload, "kernel_source_hash": kernel_hash(),
@@ -262,7 +266,7 @@ def main():
                    "total_keys": int(w.lens.sum()), "block_table": w.table_kind, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved_gbps / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "mla_decode_attn (attn_split_kernel + attn_combine_kernel)",
+                     "kernel": "mla_decode_attn call (split kernel + combine kernel)",
                      "algorithmic_bytes_per_launch": alg["attn_bytes"],
                      "avg_launch_us": med["decode_attn"]},
         "latent_cache_GBps": alg["cache_bytes"] / attn_s / 1e9,
@@ -274,10 +278,10 @@ def main():
                  "wall_s_incl_host_generation": t_fill},
     }
     if args.copy_calib:
-        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
+        buf = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         for _ in range(3):
-            dst.copy_(src)
+            buf.sum()            # reads COPY_BYTES
+            buf.fill_(1.0)       # writes COPY_BYTES
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
