@@ -47,3 +47,17 @@ class DecodeStep:
         self.append(c_kv, k_pe, q_pos, slots)
         self.attend(q_nope, q_pe, q_pos)
         return self.o
+
+    def capture(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots):
+        """Record one whole step (five kernels, no allocation, no memset) as a
+        HIP graph over these input tensors; returns the graph, whose replay()
+        reruns the step on whatever the tensors then hold."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):       # one eager run initialises the stream state
+            self(c_kv, k_pe, q_nope, q_pe, q_pos, slots)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self(c_kv, k_pe, q_nope, q_pe, q_pos, slots)
+        return g
