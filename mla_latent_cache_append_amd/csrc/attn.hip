@@ -870,6 +870,11 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float f) {
   asm volatile("" : "+a"(acc));
 }
 
+// Slot swizzle of the query staging blocks: for a fixed chunk, the 16 rows
+// that 16 lanes of a fragment read (8 rows i of two row groups g) land on 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int qswz(int i, int g) { return ((i >> 1) & 3) | ((g & 1) << 2); }
+
 __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[OSTAGE * HT_BYTES];
   lds_char* stages = (lds_char*)smem;
@@ -982,26 +987,44 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     //   B: score MFMAs of e+1, k-steps 18..35, with the PV MFMAs of e,
     //      O^T[col][row] += V^T[col][token] P^T[token][row].
     // On the last half tile the scores rerun on stage e and are discarded.
-    // Stage e0 and the query go out together; the query's arrival is awaited
-    // (which also completes stage e0) before the next two stages are issued,
-    // so the first scores wait for one stage rather than three.
-    issue(e0);
-    // query fragments (B operand of S^T): row r, features 16 ks + 8 h .. +7
+    // Query fragments (B operand of S^T: row r, features 16 ks + 8 h .. +7)
+    // come through the LDS, which the stages do not use yet. On the global
+    // side every 8 lanes of a copy read one whole 128-byte line of a query
+    // row; a direct load per fragment would touch 32 rows per instruction,
+    // 32 bytes of each. Wave w copies and reads only its own 32 rows (36
+    // blocks of 1 KiB: block (m, g) holds line m of rows 32 w + 8 g + i,
+    // chunk p of row i at slot 8 i + (p ^ qswz(i, g))), so its own vmcnt wait
+    // is enough; rows past the last query row read as zeros.
     u32x4 qf[KSTEPS16];
     {
-      const bool valid = r < a.rows;
-      const uint16_t* qrow = a.q + ((int64_t)b * a.rows + (valid ? r : 0)) * D_K + 8 * h;
+      const int nv = max(0, min(128, a.rows - rg * 128));
+      sgpr_x4 qr = buffer_rsrc(a.q + ((int64_t)b * a.rows + rg * 128) * D_K, nv * ROW_BYTES);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS16; ++ks) {
-        u32x4 v = *(const u32x4*)(qrow + 16 * ks);
-        if (!valid) v = u32x4{0u, 0u, 0u, 0u};
-        qf[ks] = v;
-      }
+      for (int k = 0; k < 4; ++k) qr[k] = (uint32_t)uni((int)qr[k]);   // uniform: keep it in SGPRs
+      const uint32_t qdst = lds_addr(stages) + wave * 36 * 1024;
+      const int i = lane >> 3, sl = lane & 7;
+      const uint32_t qoff[2] = {(uint32_t)(i * ROW_BYTES + 16 * (sl ^ qswz(i, 0))),
+                                (uint32_t)(i * ROW_BYTES + 16 * (sl ^ qswz(i, 1)))};
+#pragma unroll
+      for (int m = 0; m < 9; ++m)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          buffer_load_lds_16(qr, qoff[g & 1], (32 * wave + 8 * g) * ROW_BYTES + m * 128, qdst + (m * 4 + g) * 1024);
+      wait_vmem_n<0>();
+      const int ii = c32 & 7, g = c32 >> 3;
+      lds_char* qsrc = stages + wave * 36 * 1024 + g * 1024 + ii * 128;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS16; ++ks)
+        qf[ks] = lds_read_b128(qsrc, (ks >> 2) * 4096 + 16 * ((2 * (ks & 3) + h) ^ qswz(ii, g)));
     }
-    // an empty statement reading every fragment: the compiler's wait for the
-    // query loads lands here, before the next copies are issued
-    asm volatile("" ::OWN_OPS_Q0_35);
+    lds_barrier();                         // every wave holds its fragments; the LDS is free
+    // Stage e0 is awaited alone, so the first scores start on it while the
+    // next two stages are still on their way.
+    issue(e0);
     for (int e = e0 + 1; e < min(e1, e0 + OSTAGE - 1); ++e) issue(e);
+    if (e1 - e0 >= 3) wait_vmem_n<18>();
+    else if (e1 - e0 == 2) wait_vmem_n<9>();
+    else wait_vmem_n<0>();
     lds_barrier();
     f32x16 sn;
     u32x4 kb[OWN_PF_K];
@@ -1092,14 +1115,24 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
 }
 
 // Merge the partials of each query row in range order. One wave per row,
-// 8 output columns per lane.
+// 8 output columns per lane. The lengths are read once; the (m, l) pairs of
+// the first 64 ranges and the first 8 partial rows are requested together,
+// so a row with up to 8 partials costs two memory round trips.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = blockIdx.x;
   const int r = blockIdx.y * 4 + wave;
   if (r >= a.rows) return;
-  const int64_t T = plan_total_tiles(a.seq_lens, a.B, a.max_blocks);
-  const int ntiles = tiles_of(a.seq_lens[b], a.max_blocks);
+  // total tiles T, first tile of sequence b, and its tile count
+  int64_t T = 0, start = 0;
+  int ntiles = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    const int bb = base + lane;
+    const int t = bb < a.B ? tiles_of(a.seq_lens[bb], a.max_blocks) : 0;
+    T += wave_sum_i(t);
+    start += wave_sum_i(bb < b ? t : 0);
+    if (b >= base && b < base + 64) ntiles = __shfl(t, b - base);
+  }
   const int64_t orow = (int64_t)b * a.rows + r;
   uint16_t* out = a.o_lat + orow * D_C + 8 * lane;
   if (ntiles == 0) {
@@ -1107,48 +1140,45 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     if (a.lse && lane == 0) a.lse[orow] = -INFINITY;
     return;
   }
-  // start of sequence b on the tile line: tiles of sequences before it
-  int64_t start = 0;
-  for (int base = 0; base < b; base += 64) {
-    const int bb = base + lane;
-    start += wave_sum_i(bb < b ? tiles_of(a.seq_lens[bb], a.max_blocks) : 0);
-  }
   const int w_lo = plan_owner(start, T, a.width);
   const int w_hi = plan_owner(start + ntiles - 1, T, a.width);
   if (w_lo == w_hi) return;  // one range held the whole sequence and wrote it
 
   // Ranges between w_lo and w_hi all lie inside sequence b, except empty ones
-  // (more workgroups than tiles), which wrote nothing and are skipped. They are
-  // taken 64 at a time: lane k reads (m, l) of range c + k, the wave reduces,
-  // and the partial rows are loaded eight at a time before their products.
+  // (more workgroups than tiles), which wrote nothing and get weight 0. They
+  // are taken 64 at a time: lane k holds (m, l) of range c + k; the partial
+  // rows are loaded eight at a time.
   auto empty = [&](int w) { return (int64_t)w * T / a.width == (int64_t)(w + 1) * T / a.width; };
-  float M = -INFINITY;
-  for (int c = w_lo; c <= w_hi; c += 64) {
+  auto load_ml = [&](int c) -> float2 {
     const int w = c + lane;
-    const float m = (w <= w_hi && !empty(w)) ? a.ws_ml[((int64_t)(w + b) * a.rows + r) * 2] : -INFINITY;
-    M = fmaxf(M, wave_max_f(m));
-  }
+    if (w > w_hi || empty(w)) return float2{-INFINITY, 0.f};
+    return *(const float2*)(a.ws_ml + ((int64_t)(w + b) * a.rows + r) * 2);
+  };
+  auto load_rows = [&](int c, int cnt, int k0, u32x4 (&v)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // ranges past the last one read row c (in bounds); their weight is 0
+      const int k = k0 + u < cnt ? k0 + u : 0;
+      v[u] = *(const u32x4*)(a.ws_acc + ((int64_t)(c + k + b) * a.rows + r) * D_C + 8 * lane);
+    }
+  };
+  const int cnt0 = min(64, w_hi - w_lo + 1);
+  const float2 ml0 = load_ml(w_lo);
+  u32x4 v[8];
+  load_rows(w_lo, cnt0, 0, v);
+  float M = wave_max_f(ml0.x);
+  for (int c = w_lo + 64; c <= w_hi; c += 64) M = fmaxf(M, wave_max_f(load_ml(c).x));
   const float Mref = M == -INFINITY ? 0.f : M;
   // partial k holds o_k / l_k: weight it by l_k 2^(m_k - M)
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
   for (int c = w_lo; c <= w_hi; c += 64) {
-    const int w = c + lane;
-    float wt = 0.f;
-    if (w <= w_hi && !empty(w)) {
-      const int64_t prow = (int64_t)(w + b) * a.rows + r;
-      wt = __builtin_amdgcn_exp2f(a.ws_ml[prow * 2] - Mref) * a.ws_ml[prow * 2 + 1];
-    }
+    const float2 ml = c == w_lo ? ml0 : load_ml(c);
+    const float wt = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - Mref) * ml.y;
     l += wave_sum_f(wt);
     const int cnt = min(64, w_hi - c + 1);
     for (int k0 = 0; k0 < cnt; k0 += 8) {
-      u32x4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        // ranges past the last one read row c (in bounds); their weight is 0
-        const int k = k0 + u < cnt ? k0 + u : 0;
-        v[u] = *(const u32x4*)(a.ws_acc + ((int64_t)(c + k + b) * a.rows + r) * D_C + 8 * lane);
-      }
+      if (c != w_lo || k0 != 0) load_rows(c, cnt, k0, v);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float wk = k0 + u < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), k0 + u)) : 0.f;
