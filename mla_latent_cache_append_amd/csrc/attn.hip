@@ -917,6 +917,9 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
       vbase[rr] = ht_off(8 * rr + tl, e) - (uint32_t)(rr * 9216) + 8 * (i16 & 1);
   }
   const uint32_t goff = (uint32_t)((lane >> 3) * ROW_BYTES + ((lane & 7) ^ swz2(8 * wave + (lane >> 3))) * 16);
+  uint32_t so[9];   // buffer offset of line cg of this wave's 8 tokens
+#pragma unroll
+  for (int cg = 0; cg < 9; ++cg) so[cg] = (uint32_t)(wave * 8 * ROW_BYTES + cg * 128);
 
   int64_t x = x_begin;
   while (x < x_end && b < a.B) {
@@ -931,6 +934,9 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     const int e0 = 2 * k_first, e1 = (key_end + HT_TOK - 1) / HT_TOK;
 
     const int lim = r < a.rows ? L - a.Lq + r / a.H : -1;   // last key row r sees
+    // last key that every row of this wave sees (rows grow with r; rows past
+    // the last one are never stored, so they need no mask)
+    const int lim_wave = uni(L - a.Lq + (rg * 128 + 32 * wave) / a.H);
     float m_run = -INFINITY, l_run = 0.f;
     f32x16 o[16];
 #pragma unroll
@@ -943,7 +949,15 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     int kq = k_first;
     int blk_q = bt[kq];
     int blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
-    auto issue = [&](int e) {
+    // Copy of half tile e into its stage: descriptor rs and this wave's LDS
+    // base mb (wave w copies tokens 8 w .. 8 w + 7, nine 1-KiB lines). Past
+    // the segment's last half tile the descriptor covers zero bytes, so the
+    // copy only writes zeros into a stage that is not read again; every
+    // iteration then has exactly nine copies per wave in flight.
+    auto prep = [&](int e, sgpr_x4& rs, uint32_t& mb) {
+      mb = lds_addr(stages + (e % OSTAGE) * HT_BYTES + wave * 9 * 1024);
+      rs = buffer_rsrc(a.pool, 0);
+      if (e >= e1) return;
       const int k = e >> 1;
       if (k != kq) {   // tiles advance one at a time
         kq = k;
@@ -956,12 +970,14 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
         return;
       }
       const int n_valid = min(HT_TOK, L - e * HT_TOK);
-      const sgpr_x4 rsrc =
-          buffer_rsrc((const char*)a.pool + (int64_t)blk * TILE_BYTES + (e & 1) * HT_BYTES, n_valid * ROW_BYTES);
-      const uint32_t dst = lds_addr(stages + (e % OSTAGE) * HT_BYTES + wave * 9 * 1024);
+      rs = buffer_rsrc((const char*)a.pool + (int64_t)blk * TILE_BYTES + (e & 1) * HT_BYTES, n_valid * ROW_BYTES);
+    };
+    auto issue = [&](int e) {
+      sgpr_x4 rs;
+      uint32_t mb;
+      prep(e, rs, mb);
 #pragma unroll
-      for (int cg = 0; cg < 9; ++cg)
-        buffer_load_lds_16(rsrc, goff, wave * 8 * ROW_BYTES + cg * 128, dst + cg * 1024);
+      for (int cg = 0; cg < 9; ++cg) buffer_load_lds_16(rs, goff, so[cg], mb + cg * 1024);
     };
 
     // LDS addresses of the K fragments (stage of half tile e) and of the V^T
@@ -1020,38 +1036,49 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     lds_barrier();                         // every wave holds its fragments; the LDS is free
     // Stage e0 is awaited alone, so the first scores start on it while the
     // next two stages are still on their way.
-    issue(e0);
-    for (int e = e0 + 1; e < min(e1, e0 + OSTAGE - 1); ++e) issue(e);
-    if (e1 - e0 >= 3) wait_vmem_n<18>();
-    else if (e1 - e0 == 2) wait_vmem_n<9>();
-    else wait_vmem_n<0>();
+    for (int e = e0; e < e0 + OSTAGE - 1; ++e) issue(e);
+    wait_vmem_n<18>();
     lds_barrier();
     f32x16 sn;
     u32x4 kb[OWN_PF_K];
     k_addr(e0);
     asm volatile(OWN_ASM_PRO : [sn] "=&v"(sn), OWN_OPS_KB_OUT : OWN_OPS_Q0_35, OWN_OPS_KA : "memory");
+    // Half tile e+3 goes into the stage of e-1; its nine copies are issued
+    // one per two score MFMAs inside the A sequence, which keeps the vector
+    // memory queue from stalling the wave. The descriptor of the next
+    // iteration's copies and its LDS addresses are prepared at the end of
+    // the current one, under the last MFMAs of B rather than after the barrier.
+    sgpr_x4 rs;
+    uint32_t mb;
+    prep(e0 + OSTAGE - 1, rs, mb);
+    k_addr(e0 + 1 < e1 ? e0 + 1 : e0);
+    v_addr(e0);
     for (int e = e0; e < e1; ++e) {
       const bool more = e + 1 < e1;
-      if (more) {
-        // stage e+1 complete; only the load of e+2 was issued after it
-        if (e + 2 < e1) wait_vmem_n<9>();
-        else wait_vmem_n<0>();
-      }
+      if (more) wait_vmem_n<9>();          // stage e+1 complete; the copies of e+2 may be in flight
       lds_barrier();                       // stage e+1 visible; stage e-1 free
-      if (e + OSTAGE - 1 < e1) issue(e + OSTAGE - 1);
-      k_addr(more ? e + 1 : e);
-      v_addr(e);
       const int lr = lim - (e * HT_TOK + 4 * h);
       float s[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = sn[i];
       float alpha;
       uint32_t p[8];
-      asm volatile(OWN_ASM_A
-                   : OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "=&v"(alpha), OWN_OPS_P,
-                     [sn] "=&v"(sn), OWN_OPS_KB_OUT
-                   : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "v"(a.scale_log2)
-                   : OWN_CLOB_A, "vcc", "memory");
+      // keys past a row's position exist only in the last half tiles of the
+      // sequence; elsewhere the sequence without the mask runs
+      if (e * HT_TOK + HT_TOK - 1 <= lim_wave)
+        asm volatile(OWN_ASM_A_FULL
+                     : OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "=&v"(alpha), OWN_OPS_P,
+                       [sn] "=&v"(sn), OWN_OPS_KB_OUT
+                     : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "v"(a.scale_log2),
+                       [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO
+                     : OWN_CLOB_A, "vcc", "m0", "memory");
+      else
+        asm volatile(OWN_ASM_A
+                     : OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "=&v"(alpha), OWN_OPS_P,
+                       [sn] "=&v"(sn), OWN_OPS_KB_OUT
+                     : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "v"(a.scale_log2),
+                       [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO
+                     : OWN_CLOB_A, "vcc", "m0", "memory");
       if (e > e0 && __any(alpha != 1.f)) {
 #pragma unroll
         for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
@@ -1061,6 +1088,11 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
                    : OWN_OPS_O, [sn] "+v"(sn), OWN_OPS_KB_INOUT
                    : OWN_OPS_Q18_35, OWN_OPS_KA, OWN_OPS_VA, [pf0] "v"(pf0), [pf1] "v"(pf1)
                    : OWN_CLOB_B, "memory");
+      if (more) {
+        prep(e + OSTAGE, rs, mb);
+        k_addr(e + 2 < e1 ? e + 2 : e + 1);
+        v_addr(e + 1);
+      }
     }
 
     // ---- finish the segment. Both outputs hold o / l in bf16 (the final

@@ -8,11 +8,13 @@ score MFMAs, and no register traffic between the accumulators and VGPRs.
 Register allocation stays with the compiler through named operands; only a
 few short-lived temporaries are fixed registers (declared as clobbers).
 
-Three templates:
+Templates:
   OWN_ASM_PRO  scores of the first half tile of a segment (36 k-steps)
   OWN_ASM_A    softmax of half tile e (from its scores) interleaved with the
-               score MFMAs of half tile e+1, k-steps 0..17; leaves the K
-               fragments of k-steps 18..21 loaded
+               score MFMAs of half tile e+1, k-steps 0..17, and the nine
+               buffer -> LDS copies of this wave's share of half tile e+3;
+               leaves the K fragments of k-steps 18..21 loaded
+  OWN_ASM_A_FULL  the same for a half tile whose keys every row sees (no mask)
   OWN_ASM_B    score MFMAs of half tile e+1, k-steps 18..35, interleaved with
                the 32 PV MFMAs of half tile e (V^T fragments read transposed)
 
@@ -103,17 +105,19 @@ def gen_pro():
     return s.text()
 
 
-def softmax_valu():
+def softmax_valu(mask=True):
     """Online softmax of one half tile for the lane's row, on operands s0..s15
     (score value i = token 8 (i / 4) + 4 h + i % 4 of the half tile; lr = last
     visible key minus the token of value 0). Returns the VALU instructions."""
     t0, t1, t2, t3, t4, ninf = TA
     # v_cndmask reads VCC over the constant bus, so -inf comes from a register
-    v = ["v_mov_b32 %s, %s" % (ninf, NEG_INF)]
-    for i in range(16):   # keys past the row's position -> -inf
-        off = 8 * (i >> 2) + (i & 3)
-        v.append("v_cmp_le_i32 vcc, %d, %%[lr]" % off)
-        v.append("v_cndmask_b32 %%[s%d], %s, %%[s%d], vcc" % (i, ninf, i))
+    v = []
+    if mask:
+        v.append("v_mov_b32 %s, %s" % (ninf, NEG_INF))
+        for i in range(16):   # keys past the row's position -> -inf
+            off = 8 * (i >> 2) + (i & 3)
+            v.append("v_cmp_le_i32 vcc, %d, %%[lr]" % off)
+            v.append("v_cndmask_b32 %%[s%d], %s, %%[s%d], vcc" % (i, ninf, i))
     v.append("v_max3_f32 %s, %%[s0], %%[s1], %%[s2]" % t0)
     for i in range(3, 15, 2):
         v.append("v_max3_f32 %s, %s, %%[s%d], %%[s%d]" % (t0, t0, i, i + 1))
@@ -145,16 +149,26 @@ def softmax_valu():
     return v
 
 
-def gen_a():
+def dma(seq, cg):
+    """Line cg of this wave's share of the next stage: buffer -> LDS copy of
+    1 KiB (M0 = LDS base of the line; the copy counts in vmcnt, not lgkmcnt)."""
+    seq.op("s_add_u32 m0, %%[mb], 0x%x" % (cg * 1024))
+    seq.op("s_nop 0")
+    seq.op("buffer_load_dwordx4 %%[go], %%[rs], %%[so%d] offen lds" % cg)
+
+
+def gen_a(mask=True):
     s = Seq()
     s.op("s_nop 1")
     for ks in range(PF_K):
         kread(s, ks)
-    valu = softmax_valu()
+    valu = softmax_valu(mask)
     per = (len(valu) + A_STEPS - 1) // A_STEPS
     for ks in range(A_STEPS):
         score_mfma(s, ks, ks == 0)
         kread(s, ks + PF_K)               # the last PF_K of these are template B's first k-steps
+        if ks % 2 == 0:
+            dma(s, ks // 2)
         for ins in valu[ks * per:(ks + 1) * per]:
             s.op(ins)
     s.drain()
@@ -185,7 +199,8 @@ def gen_b():
 def main():
     out = os.path.join(HERE, "own_asm.inc")
     body = ["// Generated by gen_own_asm.py; do not edit.", ""]
-    for name, text in (("OWN_ASM_PRO", gen_pro()), ("OWN_ASM_A", gen_a()), ("OWN_ASM_B", gen_b())):
+    for name, text in (("OWN_ASM_PRO", gen_pro()), ("OWN_ASM_A", gen_a()), ("OWN_ASM_A_FULL", gen_a(False)),
+                       ("OWN_ASM_B", gen_b())):
         body.append('#define %s "%s"' % (name, text))
         body.append("")
     # operand lists (names of attn_own_kernel's variables)
@@ -200,6 +215,7 @@ def main():
         "OWN_OPS_S": ", ".join('[s%d] "+v"(s[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_P": ", ".join('[p%d] "=&v"(p[%d])' % (i, i) for i in range(8)),
         "OWN_OPS_O": ", ".join('[o%d] "+a"(o[%d])' % (i, i) for i in range(16)),
+        "OWN_OPS_SO": ", ".join('[so%d] "s"(so[%d])' % (i, i) for i in range(9)),
         "OWN_CLOB_A": ", ".join('"%s"' % r for r in TA),
         "OWN_CLOB_B": ", ".join('"v%d"' % r for r in range(VR0, 256)),
         "OWN_PF_K": str(PF_K),
