@@ -905,16 +905,16 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
   // stage bases are multiples of 128 bytes.
   const uint32_t kbase = ht_off(c32, h);
   // V^T fragment of column block cb (columns 32 cb .. +31) and token block kk:
-  //   tr(((stage + vbase[0]) ^ ((cb & 1) << 6)) + kk * 18432 + (cb >> 1) * 1024)          tokens 16 kk + 4 h .. +3
-  //   tr(((stage + vbase[1]) ^ ((cb & 1) << 6)) + kk * 18432 + 9216 + (cb >> 1) * 1024)   tokens 16 kk + 8 + 4 h .. +3
-  uint32_t vbase[2];
+  //   tr(((stage + vbase) ^ ((cb & 1) << 6)) + kk * 18432 + (cb >> 1) * 1024)               tokens 16 kk + 4 h .. +3
+  //   tr(((stage + vbase) ^ 32 ^ ((cb & 1) << 6)) + kk * 18432 + 9216 + (cb >> 1) * 1024)   tokens 16 kk + 8 + 4 h .. +3
+  // (tokens 8 apart share the slot layout up to bit 1 of the swizzle, i.e.
+  // byte bit 5; vbase < 1024 and stage bases are multiples of 1024)
+  uint32_t vbase;
   {
     const int i16 = lane & 15, q = lane >> 4;
     const int tl = 4 * (q >> 1) + (i16 >> 2);
     const int e = 2 * (q & 1) + ((i16 & 3) >> 1);
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
-      vbase[rr] = ht_off(8 * rr + tl, e) - (uint32_t)(rr * 9216) + 8 * (i16 & 1);
+    vbase = ht_off(tl, e) + 8 * (i16 & 1);
   }
   const uint32_t goff = (uint32_t)((lane >> 3) * ROW_BYTES + ((lane & 7) ^ swz2(8 * wave + (lane >> 3))) * 16);
   uint32_t so[9];   // buffer offset of line cg of this wave's 8 tokens
@@ -943,28 +943,21 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
 
     // Block ids come through scalar loads (lgkmcnt, not vmcnt, so reading one
-    // never drains the tile loads in flight), one tile ahead of their use.
+    // never drains the tile copies in flight). In the loop the id of the
+    // half tile copied at the end of an iteration is requested right after
+    // its barrier, so the load is long complete when it is used.
     const __attribute__((address_space(4))) int32_t* bt =
         (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)b * a.max_blocks);
-    int kq = k_first;
-    int blk_q = bt[kq];
-    int blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
-    // Copy of half tile e into its stage: descriptor rs and this wave's LDS
-    // base mb (wave w copies tokens 8 w .. 8 w + 7, nine 1-KiB lines). Past
-    // the segment's last half tile the descriptor covers zero bytes, so the
-    // copy only writes zeros into a stage that is not read again; every
-    // iteration then has exactly nine copies per wave in flight.
-    auto prep = [&](int e, sgpr_x4& rs, uint32_t& mb) {
+    auto blk_of = [&](int e) { return (e >> 1) < ntiles ? bt[e >> 1] : -1; };
+    // Copy of half tile e (cache block blk) into its stage: descriptor rs and
+    // this wave's LDS base mb (wave w copies tokens 8 w .. 8 w + 7, nine
+    // 1-KiB lines). Past the segment's last half tile the descriptor covers
+    // zero bytes, so the copy only writes zeros into a stage that is not read
+    // again; every iteration then has exactly nine copies per wave in flight.
+    auto prep = [&](int e, int blk, sgpr_x4& rs, uint32_t& mb) {
       mb = lds_addr(stages + (e % OSTAGE) * HT_BYTES + wave * 9 * 1024);
       rs = buffer_rsrc(a.pool, 0);
       if (e >= e1) return;
-      const int k = e >> 1;
-      if (k != kq) {   // tiles advance one at a time
-        kq = k;
-        blk_q = blk_q1;
-        blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
-      }
-      const int blk = blk_q;
       if (blk < 0 || blk >= a.num_blocks) {
         bad = true;
         return;
@@ -975,7 +968,7 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     auto issue = [&](int e) {
       sgpr_x4 rs;
       uint32_t mb;
-      prep(e, rs, mb);
+      prep(e, blk_of(e), rs, mb);
 #pragma unroll
       for (int cg = 0; cg < 9; ++cg) buffer_load_lds_16(rs, goff, so[cg], mb + cg * 1024);
     };
@@ -989,11 +982,11 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
       for (int q = 0; q < 4; ++q) ka[q] = sb ^ (uint32_t)(q << 5);
     };
     auto v_addr = [&](int e) {
-      const uint32_t sb = lds_addr(stages + (e % OSTAGE) * HT_BYTES);
+      const uint32_t sb = lds_addr(stages + (e % OSTAGE) * HT_BYTES) + vbase;
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-        for (int c1 = 0; c1 < 2; ++c1) va[c1 + 2 * rr] = (sb + vbase[rr]) ^ (uint32_t)(c1 << 6);
+        for (int c1 = 0; c1 < 2; ++c1) va[c1 + 2 * rr] = sb ^ (uint32_t)((c1 << 6) | (rr << 5));
     };
 
     // ---- pipeline: iteration e reads stage e (V) and e+1 (K); e+2 and e+3 in flight.
@@ -1050,46 +1043,49 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     // the current one, under the last MFMAs of B rather than after the barrier.
     sgpr_x4 rs;
     uint32_t mb;
-    prep(e0 + OSTAGE - 1, rs, mb);
+    prep(e0 + OSTAGE - 1, blk_of(e0 + OSTAGE - 1), rs, mb);
     k_addr(e0 + 1 < e1 ? e0 + 1 : e0);
     v_addr(e0);
     for (int e = e0; e < e1; ++e) {
       const bool more = e + 1 < e1;
       if (more) wait_vmem_n<9>();          // stage e+1 complete; the copies of e+2 may be in flight
-      lds_barrier();                       // stage e+1 visible; stage e-1 free
+      // stage e+1 visible; stage e-1 free. B ends with every LDS read done,
+      // so the barrier needs no lgkmcnt wait, and the block-id scalar load
+      // issued at the end of the previous iteration stays in flight.
+      asm volatile("s_barrier" ::: "memory");
+      const int blk_next = blk_of(e + OSTAGE);   // for the copies prepared at the end
       const int lr = lim - (e * HT_TOK + 4 * h);
       float s[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = sn[i];
-      float alpha;
-      uint32_t p[8];
+      float alpha, mref;
       // keys past a row's position exist only in the last half tiles of the
       // sequence; elsewhere the sequence without the mask runs
       if (e * HT_TOK + HT_TOK - 1 <= lim_wave)
         asm volatile(OWN_ASM_A_FULL
-                     : OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "=&v"(alpha), OWN_OPS_P,
+                     : OWN_OPS_S, [mrun] "+v"(m_run), [alpha] "=&v"(alpha), [mref] "=&v"(mref),
                        [sn] "=&v"(sn), OWN_OPS_KB_OUT
-                     : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "v"(a.scale_log2),
-                       [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO
+                     : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "s"(a.scale_log2),
+                       [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_A
                      : OWN_CLOB_A, "vcc", "m0", "memory");
       else
         asm volatile(OWN_ASM_A
-                     : OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "=&v"(alpha), OWN_OPS_P,
+                     : OWN_OPS_S, [mrun] "+v"(m_run), [alpha] "=&v"(alpha), [mref] "=&v"(mref),
                        [sn] "=&v"(sn), OWN_OPS_KB_OUT
-                     : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "v"(a.scale_log2),
-                       [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO
+                     : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "s"(a.scale_log2),
+                       [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_A
                      : OWN_CLOB_A, "vcc", "m0", "memory");
       if (e > e0 && __any(alpha != 1.f)) {
 #pragma unroll
         for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
       }
-      const u32x4 pf0 = {p[0], p[1], p[2], p[3]}, pf1 = {p[4], p[5], p[6], p[7]};
       asm volatile(OWN_ASM_B
-                   : OWN_OPS_O, [sn] "+v"(sn), OWN_OPS_KB_INOUT
-                   : OWN_OPS_Q18_35, OWN_OPS_KA, OWN_OPS_VA, [pf0] "v"(pf0), [pf1] "v"(pf1)
-                   : OWN_CLOB_B, "memory");
+                   : OWN_OPS_O, [sn] "+v"(sn), OWN_OPS_KB_INOUT, OWN_OPS_S, [lrun] "+v"(l_run)
+                   : OWN_OPS_Q18_35, OWN_OPS_KA, OWN_OPS_VA, [alpha] "v"(alpha), [mref] "v"(mref),
+                     [scale] "s"(a.scale_log2), [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_B
+                   : OWN_CLOB_B, "m0", "memory");
       if (more) {
-        prep(e + OSTAGE, rs, mb);
+        prep(e + OSTAGE, blk_next, rs, mb);
         k_addr(e + 2 < e1 ? e + 2 : e + 1);
         v_addr(e + 1);
       }

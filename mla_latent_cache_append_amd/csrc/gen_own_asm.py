@@ -10,13 +10,16 @@ few short-lived temporaries are fixed registers (declared as clobbers).
 
 Templates:
   OWN_ASM_PRO  scores of the first half tile of a segment (36 k-steps)
-  OWN_ASM_A    softmax of half tile e (from its scores) interleaved with the
-               score MFMAs of half tile e+1, k-steps 0..17, and the nine
+  OWN_ASM_A    first half of the softmax of half tile e (mask, row max,
+               rescale factor) interleaved with the score MFMAs of half
+               tile e+1, k-steps 0..17, and the nine
                buffer -> LDS copies of this wave's share of half tile e+3;
                leaves the K fragments of k-steps 18..21 loaded
   OWN_ASM_A_FULL  the same for a half tile whose keys every row sees (no mask)
-  OWN_ASM_B    score MFMAs of half tile e+1, k-steps 18..35, interleaved with
-               the 32 PV MFMAs of half tile e (V^T fragments read transposed)
+  OWN_ASM_B    score MFMAs of half tile e+1, k-steps 18..35, carrying the
+               second half of the softmax (probabilities, row sum, bf16
+               packing), then the 32 PV MFMAs of half tile e (V^T fragments
+               read transposed, prefetched under the last score MFMAs)
 
 Operand names and layouts are those of attn_own_kernel; the MFMA is
 v_mfma_f32_32x32x16_bf16 throughout. Run: python gen_own_asm.py (the build
@@ -27,17 +30,22 @@ import os
 
 KSTEPS = 36          # 576 features / 16
 A_STEPS = 18         # score k-steps in template A
-PF_K = int(os.environ.get("OWN_PF_K", "5"))   # K fragments in flight
-PF_V = int(os.environ.get("OWN_PF_V", "5"))   # V^T fragments in flight (two reads each)
+PF_K = int(os.environ.get("OWN_PF_K", "4"))   # K fragments in flight
+PF_V = int(os.environ.get("OWN_PF_V", "4"))   # V^T fragments in flight (two reads each)
 assert PF_K + 2 * PF_V <= 15, "LDS reads in flight must fit lgkmcnt"
 NEG_INF = "0xff800000"
 HERE = os.path.dirname(os.path.abspath(__file__))
 
-# fixed temporaries (clobbered): A uses TA, B uses the V ring
-TA = ["v%d" % r for r in range(250, 256)]
+# fixed temporaries (clobbered): A uses TA; B uses the V ring, the packed
+# probabilities P (two MFMA operands of 4 registers) and one accumulator
+TA = ["v%d" % r for r in range(252, 256)]
 VR0 = 256 - 4 * PF_V
 VRING = [("v[%d:%d]" % (VR0 + 4 * i, VR0 + 4 * i + 1), "v[%d:%d]" % (VR0 + 4 * i + 2, VR0 + 4 * i + 3),
           "v[%d:%d]" % (VR0 + 4 * i, VR0 + 4 * i + 3)) for i in range(PF_V)]
+PR0 = VR0 - 8
+P_OP = ["v[%d:%d]" % (PR0, PR0 + 3), "v[%d:%d]" % (PR0 + 4, PR0 + 7)]
+TB = "v%d" % (PR0 - 1)
+B_CLOB0 = PR0 - 1
 GUARD = ["s_nop 7", "s_nop 7", "s_nop 7"]   # MFMA results settle before the compiler's code reads them
 
 
@@ -105,14 +113,16 @@ def gen_pro():
     return s.text()
 
 
-def softmax_valu(mask=True):
-    """Online softmax of one half tile for the lane's row, on operands s0..s15
-    (score value i = token 8 (i / 4) + 4 h + i % 4 of the half tile; lr = last
-    visible key minus the token of value 0). Returns the VALU instructions."""
-    t0, t1, t2, t3, t4, ninf = TA
-    # v_cndmask reads VCC over the constant bus, so -inf comes from a register
+def softmax_max(mask=True):
+    """First half of the online softmax of one half tile for the lane's row,
+    on operands s0..s15 (score value i = token 8 (i / 4) + 4 h + i % 4 of the
+    half tile; lr = last visible key minus the token of value 0): key mask,
+    row max, the rescale factor alpha of the running state, the new running
+    max and the reference mref the probabilities are taken against."""
+    t0, t1, t2, ninf = TA
     v = []
     if mask:
+        # v_cndmask reads VCC over the constant bus, so -inf comes from a register
         v.append("v_mov_b32 %s, %s" % (ninf, NEG_INF))
         for i in range(16):   # keys past the row's position -> -inf
             off = 8 * (i >> 2) + (i & 3)
@@ -136,17 +146,32 @@ def softmax_valu(mask=True):
     v.append("v_cndmask_b32 %%[alpha], 1.0, %s, vcc" % t1)     # 1 unless the max moved
     v.append("v_mov_b32 %%[mrun], %s" % t2)
     v.append("v_cmp_neq_f32 vcc, %s, %s" % (NEG_INF, t2))
-    v.append("v_cndmask_b32 %s, 0, %s, vcc" % (t3, t2))        # reference: 0 while nothing is visible
-    for i in range(16):
-        v.append("v_fma_f32 %%[s%d], %%[s%d], %%[scale], -%s" % (i, i, t3))
-        v.append("v_exp_f32 %%[s%d], %%[s%d]" % (i, i))
-    v.append("v_add_f32 %s, %%[s0], %%[s1]" % t4)
-    for i in range(2, 16):
-        v.append("v_add_f32 %s, %s, %%[s%d]" % (t4, t4, i))
-    for j in range(8):
-        v.append("v_cvt_pk_bf16_f32 %%[p%d], %%[s%d], %%[s%d]" % (j, 2 * j, 2 * j + 1))
-    v.append("v_fma_f32 %%[lrun], %%[lrun], %%[alpha], %s" % t4)
+    v.append("v_cndmask_b32 %%[mref], 0, %s, vcc" % t2)        # reference: 0 while nothing is visible
     return v
+
+
+def softmax_exp():
+    """Second half: probabilities 2^(s scale - mref), their sum into the
+    running l (after alpha), and the bf16 packing into P for the PV MFMAs."""
+    v = []
+    for i in range(16):
+        v.append("v_fma_f32 %%[s%d], %%[s%d], %%[scale], -%%[mref]" % (i, i))
+        v.append("v_exp_f32 %%[s%d], %%[s%d]" % (i, i))
+    v.append("v_add_f32 %s, %%[s0], %%[s1]" % TB)
+    for i in range(2, 16):
+        v.append("v_add_f32 %s, %s, %%[s%d]" % (TB, TB, i))
+    for j in range(8):
+        v.append("v_cvt_pk_bf16_f32 v%d, %%[s%d], %%[s%d]" % (PR0 + j, 2 * j, 2 * j + 1))
+    v.append("v_fma_f32 %%[lrun], %%[lrun], %%[alpha], %s" % TB)
+    return v
+
+
+# The nine copies of the wave's share of the next stage, spread over the
+# whole iteration (the vector memory unit takes the four waves' copies one
+# at a time; bunched together they stall the issuing waves): lines 0..3
+# after these score MFMAs of A, lines 4..8 after these PV MFMAs of B.
+DMA_A = [1, 5, 9, 13]
+DMA_B = [2, 8, 14, 20, 26]
 
 
 def dma(seq, cg):
@@ -162,13 +187,13 @@ def gen_a(mask=True):
     s.op("s_nop 1")
     for ks in range(PF_K):
         kread(s, ks)
-    valu = softmax_valu(mask)
+    valu = softmax_max(mask)
     per = (len(valu) + A_STEPS - 1) // A_STEPS
     for ks in range(A_STEPS):
         score_mfma(s, ks, ks == 0)
         kread(s, ks + PF_K)               # the last PF_K of these are template B's first k-steps
-        if ks % 2 == 0:
-            dma(s, ks // 2)
+        if ks in DMA_A:
+            dma(s, DMA_A.index(ks))
         for ins in valu[ks * per:(ks + 1) * per]:
             s.op(ins)
     s.drain()
@@ -176,21 +201,35 @@ def gen_a(mask=True):
     return s.text()
 
 
+B_VALU_STEPS = 13      # score MFMAs of B that carry the exp half of the softmax
+
+
 def gen_b():
     s = Seq()
     s.op("s_nop 1")
-    for j in range(PF_V):
-        vread(s, j)
+    valu = softmax_exp()
+    per = (len(valu) + B_VALU_STEPS - 1) // B_VALU_STEPS
+    vnext = 0
+    for j in range(KSTEPS - A_STEPS):
+        ks = A_STEPS + j
+        score_mfma(s, ks, False)
+        if ks + PF_K < KSTEPS:
+            kread(s, ks + PF_K)
+        elif vnext < PF_V:                 # K reads done: start the V^T ring
+            vread(s, vnext)
+            vnext += 1
+        for ins in valu[j * per:(j + 1) * per]:
+            s.op(ins)
+    while vnext < PF_V:
+        vread(s, vnext)
+        vnext += 1
     for j in range(32):
-        if j < KSTEPS - A_STEPS:
-            ks = A_STEPS + j
-            score_mfma(s, ks, False)
-            if ks + PF_K < KSTEPS:
-                kread(s, ks + PF_K)
         s.need("V%db" % j)
-        s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %%[pf%d], %%[o%d]" % (j >> 1, VRING[j % PF_V][2], j & 1, j >> 1))
+        s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %s, %%[o%d]" % (j >> 1, VRING[j % PF_V][2], P_OP[j & 1], j >> 1))
         if j + PF_V < 32:
             vread(s, j + PF_V)
+        if j in DMA_B:
+            dma(s, len(DMA_A) + DMA_B.index(j))
     s.drain()
     s.lines += GUARD
     return s.text()
@@ -213,11 +252,11 @@ def main():
         "OWN_OPS_KB_OUT": ", ".join('[kb%d] "=&v"(kb[%d])' % (i, i) for i in range(PF_K)),
         "OWN_OPS_KB_INOUT": ", ".join('[kb%d] "+v"(kb[%d])' % (i, i) for i in range(PF_K)),
         "OWN_OPS_S": ", ".join('[s%d] "+v"(s[%d])' % (i, i) for i in range(16)),
-        "OWN_OPS_P": ", ".join('[p%d] "=&v"(p[%d])' % (i, i) for i in range(8)),
         "OWN_OPS_O": ", ".join('[o%d] "+a"(o[%d])' % (i, i) for i in range(16)),
-        "OWN_OPS_SO": ", ".join('[so%d] "s"(so[%d])' % (i, i) for i in range(9)),
+        "OWN_OPS_SO_A": ", ".join('[so%d] "s"(so[%d])' % (i, i) for i in range(len(DMA_A))),
+        "OWN_OPS_SO_B": ", ".join('[so%d] "s"(so[%d])' % (i, i) for i in range(len(DMA_A), 9)),
         "OWN_CLOB_A": ", ".join('"%s"' % r for r in TA),
-        "OWN_CLOB_B": ", ".join('"v%d"' % r for r in range(VR0, 256)),
+        "OWN_CLOB_B": ", ".join('"v%d"' % r for r in range(B_CLOB0, 256)),
         "OWN_PF_K": str(PF_K),
     }
     for name, text in ops.items():
