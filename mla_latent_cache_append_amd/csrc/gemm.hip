@@ -26,8 +26,9 @@ constexpr int AQ_CHUNKS = D_C / AQ_COLS;     // 4 workgroups per head
 // each) then hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int aq_swz(int j) { return 2 * (j & 3) + 8 * ((j >> 3) & 1); }
 
-// Blocks 0..N-1 rotate q_pe (one token each, dispatched first); the others
-// each compute a [N x 128] column slice of q_lat for one head.
+// Each workgroup computes a [N x 128] column slice of q_lat for one head and
+// rotates a quarter of that head's rope pairs (q_pe[n][h], one pair per
+// thread and pass), so the rotation spreads over the whole grid.
 // W_UK[h] is stored [128 j][512 c] (rows of nn.Linear(d_c, H*d_nope).weight)
 // and the contraction runs over j, its row index: the MFMA A operand
 // (8 consecutive j of one column c) comes from two transposing LDS reads
@@ -35,45 +36,38 @@ __device__ __forceinline__ int aq_swz(int j) { return 2 * (j & 3) + 8 * ((j >> 3
 __global__ __launch_bounds__(256) void absorb_q_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const int32_t* __restrict__ pos, const uint16_t* __restrict__ w_uk,
-    uint16_t* __restrict__ q_out, int N, int H, double base) {
+    uint16_t* __restrict__ q_out, int N, int H, RopeFreqs fr) {
   __shared__ __attribute__((aligned(16))) char wl[D_NOPE * AQ_COLS * 2];
-  __shared__ double rot[D_ROPE / 2][2];
-  if ((int)blockIdx.x < N) {
-    // rope of one query token, all heads: q_out[n][h][512 + 2i .. +1]. The 32
-    // (cos, sin) pairs depend only on the position: computed once, shared by
-    // every head.
-    const int n = blockIdx.x;
-    if (threadIdx.x < D_ROPE / 2) rope_cos_sin(pos[n], threadIdx.x, base, rot[threadIdx.x][0], rot[threadIdx.x][1]);
-    __syncthreads();
-    // pair k = (head k / 32, pair k % 32); eight pairs per thread per pass, all
-    // loads issued before the first rotation
-    constexpr int U = 8;
-    const int npairs = H * (D_ROPE / 2);
-    for (int k0 = 0; k0 < npairs; k0 += U * 256) {
-      uint32_t x[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = k0 + u * 256 + threadIdx.x;
-        x[u] = k < npairs ? *(const uint32_t*)(q_pe + (int64_t)n * H * D_ROPE + 2 * k) : 0u;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = k0 + u * 256 + threadIdx.x;
-        if (k < npairs) {
-          const int h = k / (D_ROPE / 2), i = k % (D_ROPE / 2);
-          *(uint32_t*)(q_out + ((int64_t)n * H + h) * D_K + D_C + 2 * i) =
-              rope_rotate_bf16(x[u], rot[i][0], rot[i][1]);
-        }
-      }
-    }
-    return;
-  }
-  const int gb = blockIdx.x - N;
-  const int h = gb / AQ_CHUNKS;
-  const int c0 = (gb % AQ_CHUNKS) * AQ_COLS;
+  const int h = blockIdx.x / AQ_CHUNKS;
+  const int chunk = blockIdx.x % AQ_CHUNKS;
+  const int c0 = chunk * AQ_COLS;
   const uint16_t* w = w_uk + (int64_t)h * D_NOPE * D_C + c0;
   __attribute__((address_space(3))) char* wls = (__attribute__((address_space(3))) char*)wl;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c = lane & 15;
+  // B = q_nope^T[K = j][N = token] of two 16-token blocks: lane (g, c) holds
+  // token n0 + 16 tb + c, rows 32 ks + 8 g .. +7. Lanes past the last token
+  // load a valid row; their columns are not stored.
+  bf16x8 bq[2][D_NOPE / 32];
+  auto load_q = [&](int n0) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int n = min(n0 + 16 * tb + c, N - 1);
+      const uint16_t* src = q_nope + ((int64_t)n * H + h) * D_NOPE + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < D_NOPE / 32; ++ks) bq[tb][ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
+    }
+  };
+  load_q(0);   // in flight together with the weight slice
+  {
+    // rope pairs p = (token p / 32, pair p % 32) of head h: q_out[n][h][512 + 2i .. +1]
+    const int npairs = N * (D_ROPE / 2);
+    for (int p = chunk * 256 + (int)threadIdx.x; p < npairs; p += AQ_CHUNKS * 256) {
+      const int n = p / (D_ROPE / 2), i = p % (D_ROPE / 2);
+      const uint32_t x = *(const uint32_t*)(q_pe + ((int64_t)n * H + h) * D_ROPE + 2 * i);
+      *(uint32_t*)(q_out + ((int64_t)n * H + h) * D_K + D_C + 2 * i) = rope_pair_bf16(x, pos[n], fr.f[i]);
+    }
+  }
   {
     // 2048 chunks of 16 bytes, eight per thread: all loads in flight before the LDS writes
     constexpr int PER = D_NOPE * (AQ_COLS / 8) / 256;
@@ -91,8 +85,6 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
   }
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4, c = lane & 15;
   // A = W^T[M = column][K = j]: this wave's two 16-column blocks
   // (c0 + 32 wave + 16 cb + c), k-step ks covers j = 32 ks .. +31 and lane
   // group g its rows 32 ks + 8 g .. +7.
@@ -111,15 +103,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
   }
   // two 16-token blocks per pass, all their loads in flight before the products
   for (int n0 = 0; n0 < N; n0 += 32) {
-    bf16x8 bq[2][D_NOPE / 32];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      // lanes past the last token load a valid row; their columns are not stored
-      const int n = min(n0 + 16 * tb + c, N - 1);
-      const uint16_t* src = q_nope + ((int64_t)n * H + h) * D_NOPE + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < D_NOPE / 32; ++ks) bq[tb][ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
-    }
+    if (n0 > 0) load_q(n0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -141,14 +125,20 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
 
 constexpr int OU_ROWS = 64;                 // W_UV rows (output features) per workgroup
 constexpr int OU_CHUNKS = D_V / OU_ROWS;    // 2 workgroups per head
+constexpr int OU_TOK = 32;                  // tokens per pass (two 16-token MFMA blocks)
 
-// W_UV[h] is stored [128 j][512 c] and the contraction runs over c, which is
-// the contiguous axis of both W_UV and o_lat: every fragment is a 16-byte
-// global load and no LDS is needed. Each wave keeps its 16 rows of W_UV (64
-// VGPRs) and sweeps the tokens.
+// W_UV[h] is stored [128 j][512 c] and the contraction runs over c, the
+// contiguous axis of both W_UV and o_lat. Each wave keeps its 16 rows of
+// W_UV (64 VGPRs, 16-byte global loads) and sweeps the tokens; the o_lat rows
+// of a pass are staged once per workgroup in LDS (32 rows x 1 KiB, 16-byte
+// chunk q of row t at slot q ^ (t & 15), so the 16 rows one fragment read
+// covers hit 16 distinct bank groups) instead of being loaded by every wave.
 __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict__ o_lat,
                                                      const uint16_t* __restrict__ w_uv,
                                                      uint16_t* __restrict__ o, int N, int H) {
+  __shared__ __attribute__((aligned(16))) char ol[OU_TOK * D_C * 2];
+  typedef __attribute__((address_space(3))) char lchar;
+  lchar* ols = (lchar*)ol;
   const int h = blockIdx.x / OU_CHUNKS;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
@@ -157,26 +147,39 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
   bf16x8 af[D_C / 32];
 #pragma unroll
   for (int ks = 0; ks < D_C / 32; ++ks) af[ks] = as_bf16x8(*(const u32x4*)(w + 32 * ks + 8 * g));
-  // two 16-token blocks per pass, all their loads in flight before the products
-  for (int n0 = 0; n0 < N; n0 += 32) {
-    bf16x8 bv[2][D_C / 32];
+  for (int n0 = 0; n0 < N; n0 += OU_TOK) {
+    if (n0 > 0) __syncthreads();          // the previous pass has read its rows
+    {
+      // 2048 chunks of 16 bytes, eight per thread, all loads before the LDS writes;
+      // rows past the last token repeat a valid row (their outputs are not stored)
+      constexpr int PER = OU_TOK * (D_C / 8) / 256;
+      u32x4 v[PER];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      // lanes past the last token load a valid row; their outputs are not stored
-      const int n = min(n0 + 16 * tb + c, N - 1);
-      const uint16_t* src = o_lat + ((int64_t)n * H + h) * D_C + 8 * g;
+      for (int u = 0; u < PER; ++u) {
+        const int k = u * 256 + threadIdx.x, t = k >> 6, q = k & 63;
+        const int n = min(n0 + t, N - 1);
+        v[u] = *(const u32x4*)(o_lat + ((int64_t)n * H + h) * D_C + 8 * q);
+      }
 #pragma unroll
-      for (int ks = 0; ks < D_C / 32; ++ks) bv[tb][ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
+      for (int u = 0; u < PER; ++u) {
+        const int k = u * 256 + threadIdx.x, t = k >> 6, q = k & 63;
+        *(__attribute__((address_space(3))) u32x4*)(ols + t * 1024 + ((q ^ (t & 15)) << 4)) = v[u];
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int n = n0 + 16 * tb + c;
+      const int t = 16 * tb + c;
+      bf16x8 bv[D_C / 32];   // B = o_lat^T[K = c][N = token]: chunk 4 ks + g of row t
+#pragma unroll
+      for (int ks = 0; ks < D_C / 32; ++ks)
+        bv[ks] = as_bf16x8(lds_read_b128(ols, t * 1024 + (((4 * ks + g) ^ (t & 15)) << 4)));
       // four independent accumulator chains keep the MFMA pipe busy
       f32x4 acc4[4] = {};
 #pragma unroll
-      for (int ks = 0; ks < D_C / 32; ++ks) acc4[ks & 3] = mfma16x16x32(af[ks], bv[tb][ks], acc4[ks & 3]);
+      for (int ks = 0; ks < D_C / 32; ++ks) acc4[ks & 3] = mfma16x16x32(af[ks], bv[ks], acc4[ks & 3]);
       const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+      const int n = n0 + t;
       if (n < N) {
         u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
         *(u32x2*)(o + ((int64_t)n * H + h) * D_V + j0 + 4 * g) = out;
@@ -188,8 +191,8 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
 hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
                            const uint16_t* w_uk, uint16_t* q_out, int32_t N, int32_t H,
                            double rope_base, hipStream_t stream) {
-  hipLaunchKernelGGL(absorb_q_kernel, dim3(H * AQ_CHUNKS + N), dim3(256), 0, stream, q_nope, q_pe,
-                     pos, w_uk, q_out, N, H, rope_base);
+  hipLaunchKernelGGL(absorb_q_kernel, dim3(H * AQ_CHUNKS), dim3(256), 0, stream, q_nope, q_pe,
+                     pos, w_uk, q_out, N, H, rope_freqs(rope_base));
   return hipGetLastError();
 }
 
