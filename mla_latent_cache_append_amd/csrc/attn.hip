@@ -33,6 +33,8 @@
 //    balanced exactly. A range that covers a whole sequence writes the final
 //    o_lat; otherwise it writes (m, l, acc) partials that the combine kernel
 //    merges in a fixed order (deterministic, no atomics).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "own_asm.inc"
@@ -938,9 +940,7 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     // the last one are never stored, so they need no mask)
     const int lim_wave = uni(L - a.Lq + (rg * 128 + 32 * wave) / a.H);
     float m_run = -INFINITY, l_run = 0.f;
-    f32x16 o[16];
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
+    f32x16 o[16];   // set by the first half tile's PV MFMAs (zero accumulator input)
 
     // Block ids come through scalar loads (lgkmcnt, not vmcnt, so reading one
     // never drains the tile copies in flight). In the loop the id of the
@@ -1046,7 +1046,10 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     prep(e0 + OSTAGE - 1, blk_of(e0 + OSTAGE - 1), rs, mb);
     k_addr(e0 + 1 < e1 ? e0 + 1 : e0);
     v_addr(e0);
-    for (int e = e0; e < e1; ++e) {
+    // one iteration; the first half tile of the segment (FIRST) starts the
+    // PV accumulators from zero and is peeled off the loop
+    auto step = [&](const int e, auto first) {
+      constexpr bool FIRST = decltype(first)::value;
       const bool more = e + 1 < e1;
       if (more) wait_vmem_n<9>();          // stage e+1 complete; the copies of e+2 may be in flight
       // stage e+1 visible; stage e-1 free. B ends with every LDS read done,
@@ -1075,21 +1078,30 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
                      : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "s"(a.scale_log2),
                        [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_A
                      : OWN_CLOB_A, "vcc", "m0", "memory");
-      if (e > e0 && __any(alpha != 1.f)) {
+      if (!FIRST && __any(alpha != 1.f)) {
 #pragma unroll
         for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
       }
-      asm volatile(OWN_ASM_B
-                   : OWN_OPS_O, [sn] "+v"(sn), OWN_OPS_KB_INOUT, OWN_OPS_S, [lrun] "+v"(l_run)
-                   : OWN_OPS_Q18_35, OWN_OPS_KA, OWN_OPS_VA, [alpha] "v"(alpha), [mref] "v"(mref),
-                     [scale] "s"(a.scale_log2), [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_B
-                   : OWN_CLOB_B, "m0", "memory");
+      if constexpr (FIRST)
+        asm volatile(OWN_ASM_B_FIRST
+                     : OWN_OPS_O_OUT, [sn] "+v"(sn), OWN_OPS_KB_INOUT, OWN_OPS_S, [lrun] "+v"(l_run)
+                     : OWN_OPS_Q18_35, OWN_OPS_KA, OWN_OPS_VA, [alpha] "v"(alpha), [mref] "v"(mref),
+                       [scale] "s"(a.scale_log2), [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_B
+                     : OWN_CLOB_B, "m0", "memory");
+      else
+        asm volatile(OWN_ASM_B
+                     : OWN_OPS_O, [sn] "+v"(sn), OWN_OPS_KB_INOUT, OWN_OPS_S, [lrun] "+v"(l_run)
+                     : OWN_OPS_Q18_35, OWN_OPS_KA, OWN_OPS_VA, [alpha] "v"(alpha), [mref] "v"(mref),
+                       [scale] "s"(a.scale_log2), [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_B
+                     : OWN_CLOB_B, "m0", "memory");
       if (more) {
         prep(e + OSTAGE, blk_next, rs, mb);
         k_addr(e + 2 < e1 ? e + 2 : e + 1);
         v_addr(e + 1);
       }
-    }
+    };
+    step(e0, std::true_type{});
+    for (int e = e0 + 1; e < e1; ++e) step(e, std::false_type{});
 
     // ---- finish the segment. Both outputs hold o / l in bf16 (the final
     // o_lat, or a partial for the merge): each wave writes its 32 rows into

@@ -20,6 +20,8 @@ Templates:
                second half of the softmax (probabilities, row sum, bf16
                packing), then the 32 PV MFMAs of half tile e (V^T fragments
                read transposed, prefetched under the last score MFMAs)
+  OWN_ASM_B_FIRST  the same for the first half tile of a segment: the PV
+               accumulators start from zero inside the MFMAs
 
 Operand names and layouts are those of attn_own_kernel; the MFMA is
 v_mfma_f32_32x32x16_bf16 throughout. Run: python gen_own_asm.py (the build
@@ -204,7 +206,7 @@ def gen_a(mask=True):
 B_VALU_STEPS = 13      # score MFMAs of B that carry the exp half of the softmax
 
 
-def gen_b():
+def gen_b(first=False):
     s = Seq()
     s.op("s_nop 1")
     valu = softmax_exp()
@@ -225,7 +227,8 @@ def gen_b():
         vnext += 1
     for j in range(32):
         s.need("V%db" % j)
-        s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %s, %%[o%d]" % (j >> 1, VRING[j % PF_V][2], P_OP[j & 1], j >> 1))
+        acc = "0" if first and j % 2 == 0 else "%%[o%d]" % (j >> 1)   # first half tile: start from 0
+        s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %s, %s" % (j >> 1, VRING[j % PF_V][2], P_OP[j & 1], acc))
         if j + PF_V < 32:
             vread(s, j + PF_V)
         if j in DMA_B:
@@ -239,7 +242,7 @@ def main():
     out = os.path.join(HERE, "own_asm.inc")
     body = ["// Generated by gen_own_asm.py; do not edit.", ""]
     for name, text in (("OWN_ASM_PRO", gen_pro()), ("OWN_ASM_A", gen_a()), ("OWN_ASM_A_FULL", gen_a(False)),
-                       ("OWN_ASM_B", gen_b())):
+                       ("OWN_ASM_B", gen_b()), ("OWN_ASM_B_FIRST", gen_b(True))):
         body.append('#define %s "%s"' % (name, text))
         body.append("")
     # operand lists (names of attn_own_kernel's variables)
@@ -253,6 +256,7 @@ def main():
         "OWN_OPS_KB_INOUT": ", ".join('[kb%d] "+v"(kb[%d])' % (i, i) for i in range(PF_K)),
         "OWN_OPS_S": ", ".join('[s%d] "+v"(s[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_O": ", ".join('[o%d] "+a"(o[%d])' % (i, i) for i in range(16)),
+        "OWN_OPS_O_OUT": ", ".join('[o%d] "=&a"(o[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_SO_A": ", ".join('[so%d] "s"(so[%d])' % (i, i) for i in range(len(DMA_A))),
         "OWN_OPS_SO_B": ", ".join('[so%d] "s"(so[%d])' % (i, i) for i in range(len(DMA_A), 9)),
         "OWN_CLOB_A": ", ".join('"%s"' % r for r in TA),
