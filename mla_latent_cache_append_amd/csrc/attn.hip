@@ -936,9 +936,6 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     const int e0 = 2 * k_first, e1 = (key_end + HT_TOK - 1) / HT_TOK;
 
     const int lim = r < a.rows ? L - a.Lq + r / a.H : -1;   // last key row r sees
-    // last key that every row of this wave sees (rows grow with r; rows past
-    // the last one are never stored, so they need no mask)
-    const int lim_wave = uni(L - a.Lq + (rg * 128 + 32 * wave) / a.H);
     float m_run = -INFINITY, l_run = 0.f;
     f32x16 o[16];   // set by the first half tile's PV MFMAs (zero accumulator input)
 
@@ -990,12 +987,16 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     };
 
     // ---- pipeline: iteration e reads stage e (V) and e+1 (K); e+2 and e+3 in flight.
-    // The instruction sequences (own_asm.inc) per iteration:
-    //   A: online softmax of half tile e from its scores (mask, row max,
-    //      probabilities, alpha, l) under the score MFMAs of e+1, k-steps 0..17;
-    //   B: score MFMAs of e+1, k-steps 18..35, with the PV MFMAs of e,
-    //      O^T[col][row] += V^T[col][token] P^T[token][row].
-    // On the last half tile the scores rerun on stage e and are discarded.
+    // One instruction sequence per iteration (own_asm.inc):
+    //   phase S: the score MFMAs of half tile e+1 under the probability half
+    //            of the softmax of half tile e (2^(s scale - mref), l, P);
+    //   phase P: the PV MFMAs of e, O^T[col][row] += V^T[col][token] P^T[token][row],
+    //            under the max half of the softmax of e+1 (mask, row max,
+    //            alpha, running max, mref, masked scores into s).
+    // Between iterations the accumulators are rescaled by alpha (rarely: the
+    // running max moves only in steps above 8 in log2 units). On the last
+    // half tile the scores rerun on stage e: their max never exceeds the
+    // running max, so the state is left as it is.
     // Query fragments (B operand of S^T: row r, features 16 ks + 8 h .. +7)
     // come through the LDS, which the stages do not use yet. On the global
     // side every 8 lanes of a copy read one whole 128-byte line of a query
@@ -1032,15 +1033,21 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     for (int e = e0; e < e0 + OSTAGE - 1; ++e) issue(e);
     wait_vmem_n<18>();
     lds_barrier();
-    f32x16 sn;
-    u32x4 kb[OWN_PF_K];
     k_addr(e0);
-    asm volatile(OWN_ASM_PRO : [sn] "=&v"(sn), OWN_OPS_KB_OUT : OWN_OPS_Q0_35, OWN_OPS_KA : "memory");
-    // Half tile e+3 goes into the stage of e-1; its nine copies are issued
-    // one per two score MFMAs inside the A sequence, which keeps the vector
+    float s[16];          // masked scores of the half tile whose PV comes next
+    float alpha, mref;    // its rescale factor and probability reference
+    {
+      const int lr = lim - (e0 * HT_TOK + 4 * h);
+      asm volatile(OWN_ASM_PRO
+                   : OWN_OPS_S_OUT, [mrun] "+v"(m_run), [alpha] "=&v"(alpha), [mref] "=&v"(mref)
+                   : OWN_OPS_Q, OWN_OPS_KA, [lr] "v"(lr), [scale] "s"(a.scale_log2)
+                   : OWN_CLOB, "vcc", "memory");
+    }
+    // Half tile e+3 goes into the stage of e-1; its nine copies are spread
+    // over the iteration's instruction sequence, which keeps the vector
     // memory queue from stalling the wave. The descriptor of the next
     // iteration's copies and its LDS addresses are prepared at the end of
-    // the current one, under the last MFMAs of B rather than after the barrier.
+    // the current one.
     sgpr_x4 rs;
     uint32_t mb;
     prep(e0 + OSTAGE - 1, blk_of(e0 + OSTAGE - 1), rs, mb);
@@ -1052,49 +1059,30 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
       constexpr bool FIRST = decltype(first)::value;
       const bool more = e + 1 < e1;
       if (more) wait_vmem_n<9>();          // stage e+1 complete; the copies of e+2 may be in flight
-      // stage e+1 visible; stage e-1 free. B ends with every LDS read done,
-      // so the barrier needs no lgkmcnt wait, and the block-id scalar load
-      // issued at the end of the previous iteration stays in flight.
+      // stage e+1 visible; stage e-1 free. The sequence ends with every LDS
+      // read done, so the barrier needs no lgkmcnt wait, and the block-id
+      // scalar load issued right after it completes under the MFMAs.
       asm volatile("s_barrier" ::: "memory");
       const int blk_next = blk_of(e + OSTAGE);   // for the copies prepared at the end
-      const int lr = lim - (e * HT_TOK + 4 * h);
-      float s[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = sn[i];
-      float alpha, mref;
-      // keys past a row's position exist only in the last half tiles of the
-      // sequence; elsewhere the sequence without the mask runs
-      if (e * HT_TOK + HT_TOK - 1 <= lim_wave)
-        asm volatile(OWN_ASM_A_FULL
-                     : OWN_OPS_S, [mrun] "+v"(m_run), [alpha] "=&v"(alpha), [mref] "=&v"(mref),
-                       [sn] "=&v"(sn), OWN_OPS_KB_OUT
-                     : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "s"(a.scale_log2),
-                       [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_A
-                     : OWN_CLOB_A, "vcc", "m0", "memory");
-      else
-        asm volatile(OWN_ASM_A
-                     : OWN_OPS_S, [mrun] "+v"(m_run), [alpha] "=&v"(alpha), [mref] "=&v"(mref),
-                       [sn] "=&v"(sn), OWN_OPS_KB_OUT
-                     : OWN_OPS_Q0_17, OWN_OPS_KA, [lr] "v"(lr), [scale] "s"(a.scale_log2),
-                       [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_A
-                     : OWN_CLOB_A, "vcc", "m0", "memory");
-      if (!FIRST && __any(alpha != 1.f)) {
-#pragma unroll
-        for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
-      }
+      const int lr = lim - ((e + 1) * HT_TOK + 4 * h);   // mask of the scores of e+1
+#define OWN_ITER(NAME, OPS_O)                                                                         \
+  asm volatile(NAME                                                                                   \
+               : OPS_O, OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "+v"(alpha),       \
+                 [mref] "+v"(mref)                                                                    \
+               : OWN_OPS_Q, OWN_OPS_KA, OWN_OPS_VA, [lr] "v"(lr), [scale] "s"(a.scale_log2),          \
+                 [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO                               \
+               : OWN_CLOB, "vcc", "m0", "memory")
       if constexpr (FIRST)
-        asm volatile(OWN_ASM_B_FIRST
-                     : OWN_OPS_O_OUT, [sn] "+v"(sn), OWN_OPS_KB_INOUT, OWN_OPS_S, [lrun] "+v"(l_run)
-                     : OWN_OPS_Q18_35, OWN_OPS_KA, OWN_OPS_VA, [alpha] "v"(alpha), [mref] "v"(mref),
-                       [scale] "s"(a.scale_log2), [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_B
-                     : OWN_CLOB_B, "m0", "memory");
+        OWN_ITER(OWN_ASM_IT_FIRST, OWN_OPS_O_OUT);
       else
-        asm volatile(OWN_ASM_B
-                     : OWN_OPS_O, [sn] "+v"(sn), OWN_OPS_KB_INOUT, OWN_OPS_S, [lrun] "+v"(l_run)
-                     : OWN_OPS_Q18_35, OWN_OPS_KA, OWN_OPS_VA, [alpha] "v"(alpha), [mref] "v"(mref),
-                       [scale] "s"(a.scale_log2), [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO_B
-                     : OWN_CLOB_B, "m0", "memory");
+        OWN_ITER(OWN_ASM_IT, OWN_OPS_O);
+#undef OWN_ITER
       if (more) {
+        // alpha belongs to half tile e+1, whose PV runs in the next iteration
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
+        }
         prep(e + OSTAGE, blk_next, rs, mb);
         k_addr(e + 2 < e1 ? e + 2 : e + 1);
         v_addr(e + 1);

@@ -3,52 +3,66 @@ kernel's inner loop (attn_own_kernel in attn.hip), as inline-asm templates.
 
 The loop body is emitted instruction by instruction so that the schedule is
 exactly the one intended: LDS operand reads issued several MFMAs ahead of
-their use with exact lgkmcnt waits, the softmax VALU work interleaved with the
-score MFMAs, and no register traffic between the accumulators and VGPRs.
-Register allocation stays with the compiler through named operands; only a
-few short-lived temporaries are fixed registers (declared as clobbers).
+their use with exact lgkmcnt waits, the softmax VALU work interleaved with
+the MFMAs, and no register traffic between the accumulators and VGPRs.
+Values that live across iterations (query fragments, the masked scores of
+the next half tile, the running max and sum, the PV accumulators, LDS
+addresses) are named operands allocated by the compiler; values that live
+only inside one iteration (the score accumulator, the K and V^T fragment
+rings, the packed probabilities, temporaries) sit in fixed registers listed
+as clobbers.
 
-Templates:
-  OWN_ASM_PRO  scores of the first half tile of a segment (36 k-steps)
-  OWN_ASM_A    first half of the softmax of half tile e (mask, row max,
-               rescale factor) interleaved with the score MFMAs of half
-               tile e+1, k-steps 0..17, and the nine
-               buffer -> LDS copies of this wave's share of half tile e+3;
-               leaves the K fragments of k-steps 18..21 loaded
-  OWN_ASM_A_FULL  the same for a half tile whose keys every row sees (no mask)
-  OWN_ASM_B    score MFMAs of half tile e+1, k-steps 18..35, carrying the
-               second half of the softmax (probabilities, row sum, bf16
-               packing), then the 32 PV MFMAs of half tile e (V^T fragments
-               read transposed, prefetched under the last score MFMAs)
-  OWN_ASM_B_FIRST  the same for the first half tile of a segment: the PV
-               accumulators start from zero inside the MFMAs
+Templates (iteration e scores half tile e+1 and accumulates half tile e):
+  OWN_ASM_PRO
+        scores of the first half tile of a segment (36 k-steps), then the
+        first half of its softmax (key mask, row max, rescale factor, new
+        running max, reference mref); the masked scores go to s0..s15
+  OWN_ASM_IT, OWN_ASM_IT_FIRST
+        phase S: the 36 score MFMAs of half tile e+1 carrying the second half
+                 of the softmax of half tile e (probabilities 2^(s scale -
+                 mref), row sum into l after alpha, bf16 packing into P);
+        phase P: the 32 PV MFMAs of half tile e,
+                 O^T[col][row] += V^T[col][token] P^T[token][row], V^T
+                 fragments read transposed, carrying the first half of the
+                 softmax of half tile e+1 (with the key mask);
+        nine buffer -> LDS copies of this wave's share of half tile e+3 are
+        spread over both phases; FIRST starts the PV accumulators from zero.
 
-Operand names and layouts are those of attn_own_kernel; the MFMA is
-v_mfma_f32_32x32x16_bf16 throughout. Run: python gen_own_asm.py (the build
-runs it before compiling).
+The MFMA is v_mfma_f32_32x32x16_bf16 throughout. Run: python gen_own_asm.py
+(the build runs it before compiling).
 """
 
 import os
 
 KSTEPS = 36          # 576 features / 16
-A_STEPS = 18         # score k-steps in template A
-PF_K = int(os.environ.get("OWN_PF_K", "4"))   # K fragments in flight
-PF_V = int(os.environ.get("OWN_PF_V", "4"))   # V^T fragments in flight (two reads each)
-assert PF_K + 2 * PF_V <= 15, "LDS reads in flight must fit lgkmcnt"
+PF_K = int(os.environ.get("OWN_PF_K", "5"))   # K fragments in flight
+PF_V = int(os.environ.get("OWN_PF_V", "5"))   # V^T fragments in flight (two reads each)
 NEG_INF = "0xff800000"
 HERE = os.path.dirname(os.path.abspath(__file__))
 
-# fixed temporaries (clobbered): A uses TA; B uses the V ring, the packed
-# probabilities P (two MFMA operands of 4 registers) and one accumulator
-TA = ["v%d" % r for r in range(252, 256)]
-VR0 = 256 - 4 * PF_V
+# ---- fixed registers (clobbered by every template), from v255 down
+_top = 256
+VR0 = _top - 4 * PF_V                      # V^T ring: slot i = v[VR0 + 4i : +3]
 VRING = [("v[%d:%d]" % (VR0 + 4 * i, VR0 + 4 * i + 1), "v[%d:%d]" % (VR0 + 4 * i + 2, VR0 + 4 * i + 3),
           "v[%d:%d]" % (VR0 + 4 * i, VR0 + 4 * i + 3)) for i in range(PF_V)]
-PR0 = VR0 - 8
-P_OP = ["v[%d:%d]" % (PR0, PR0 + 3), "v[%d:%d]" % (PR0 + 4, PR0 + 7)]
-TB = "v%d" % (PR0 - 1)
-B_CLOB0 = PR0 - 1
+KR0 = VR0 - 4 * PF_K                       # K ring: slot i = v[KR0 + 4i : +3]
+KRING = ["v[%d:%d]" % (KR0 + 4 * i, KR0 + 4 * i + 3) for i in range(PF_K)]
+P0 = KR0 - 8                               # packed probabilities, two MFMA operands
+P_OP = ["v[%d:%d]" % (P0, P0 + 3), "v[%d:%d]" % (P0 + 4, P0 + 7)]
+SN0 = P0 - 16                              # score accumulator of the next half tile
+SN = "v[%d:%d]" % (SN0, SN0 + 15)
+T0 = SN0 - 4                               # temporaries
+TMP = ["v%d" % (T0 + i) for i in range(4)]
+CLOB_LO = T0
 GUARD = ["s_nop 7", "s_nop 7", "s_nop 7"]   # MFMA results settle before the compiler's code reads them
+
+# the nine copies of the next stage: lines 0..4 after these score MFMAs,
+# lines 5..8 after these PV MFMAs (the vector memory unit takes the four
+# waves' copies one at a time; bunched together they stall the issuing waves)
+DMA_S = [2, 9, 16, 23, 30]
+DMA_P = [3, 11, 19, 27]
+S_VALU_STEPS = 16    # score MFMAs that carry the probability half of the softmax
+P_VALU_FROM = 3      # PV MFMA after which the max half of the softmax starts
 
 
 class Seq:
@@ -83,13 +97,13 @@ class Seq:
 
 
 def kread(seq, ks):
-    """K fragment of k-step ks into ring slot ks % PF_K (16 bytes per lane)."""
-    seq.lds("ds_read_b128 %%[kb%d], %%[ka%d] offset:%d" % (ks % PF_K, ks & 3, (ks >> 2) * 1024), "K%d" % ks)
+    """K fragment of k-step ks (token c32, chunk 2 ks + h) into ring slot ks % PF_K."""
+    seq.lds("ds_read_b128 %s, %%[ka%d] offset:%d" % (KRING[ks % PF_K], ks & 3, (ks >> 2) * 1024), "K%d" % ks)
 
 
-def score_mfma(seq, ks, first):
+def score_mfma(seq, ks):
     seq.need("K%d" % ks)
-    seq.op("v_mfma_f32_32x32x16_bf16 %%[sn], %%[kb%d], %%[q%d], %s" % (ks % PF_K, ks, "0" if first else "%[sn]"))
+    seq.op("v_mfma_f32_32x32x16_bf16 %s, %s, %%[q%d], %s" % (SN, KRING[ks % PF_K], ks, "0" if ks == 0 else SN))
 
 
 def vread(seq, j):
@@ -102,26 +116,26 @@ def vread(seq, j):
             "V%db" % j)
 
 
-def gen_pro():
-    s = Seq()
-    s.op("s_nop 1")
-    for ks in range(PF_K):
-        kread(s, ks)
-    for ks in range(KSTEPS):
-        score_mfma(s, ks, ks == 0)
-        if ks + PF_K < KSTEPS:
-            kread(s, ks + PF_K)
-    s.lines += GUARD
-    return s.text()
+def dma(seq, cg):
+    """Line cg of this wave's share of the next stage: buffer -> LDS copy of
+    1 KiB (M0 = LDS base of the line; the copy counts in vmcnt, not lgkmcnt)."""
+    seq.op("s_add_u32 m0, %%[mb], 0x%x" % (cg * 1024))
+    seq.op("s_nop 0")
+    seq.op("buffer_load_dwordx4 %%[go], %%[rs], %%[so%d] offen lds" % cg)
 
 
-def softmax_max(mask=True):
+def sn_reg(i):
+    return "v%d" % (SN0 + i)
+
+
+def softmax_max(mask):
     """First half of the online softmax of one half tile for the lane's row,
-    on operands s0..s15 (score value i = token 8 (i / 4) + 4 h + i % 4 of the
+    on the score accumulator (value i = token 8 (i / 4) + 4 h + i % 4 of the
     half tile; lr = last visible key minus the token of value 0): key mask,
     row max, the rescale factor alpha of the running state, the new running
-    max and the reference mref the probabilities are taken against."""
-    t0, t1, t2, ninf = TA
+    max and the reference mref the probabilities are taken against. The
+    masked scores end in s0..s15."""
+    t0, t1, t2, ninf = TMP
     v = []
     if mask:
         # v_cndmask reads VCC over the constant bus, so -inf comes from a register
@@ -129,7 +143,10 @@ def softmax_max(mask=True):
         for i in range(16):   # keys past the row's position -> -inf
             off = 8 * (i >> 2) + (i & 3)
             v.append("v_cmp_le_i32 vcc, %d, %%[lr]" % off)
-            v.append("v_cndmask_b32 %%[s%d], %s, %%[s%d], vcc" % (i, ninf, i))
+            v.append("v_cndmask_b32 %%[s%d], %s, %s, vcc" % (i, ninf, sn_reg(i)))
+    else:
+        for i in range(16):
+            v.append("v_mov_b32 %%[s%d], %s" % (i, sn_reg(i)))
     v.append("v_max3_f32 %s, %%[s0], %%[s1], %%[s2]" % t0)
     for i in range(3, 15, 2):
         v.append("v_max3_f32 %s, %s, %%[s%d], %%[s%d]" % (t0, t0, i, i + 1))
@@ -155,84 +172,79 @@ def softmax_max(mask=True):
 def softmax_exp():
     """Second half: probabilities 2^(s scale - mref), their sum into the
     running l (after alpha), and the bf16 packing into P for the PV MFMAs."""
+    tb = TMP[0]
     v = []
     for i in range(16):
         v.append("v_fma_f32 %%[s%d], %%[s%d], %%[scale], -%%[mref]" % (i, i))
         v.append("v_exp_f32 %%[s%d], %%[s%d]" % (i, i))
-    v.append("v_add_f32 %s, %%[s0], %%[s1]" % TB)
+    v.append("v_add_f32 %s, %%[s0], %%[s1]" % tb)
     for i in range(2, 16):
-        v.append("v_add_f32 %s, %s, %%[s%d]" % (TB, TB, i))
+        v.append("v_add_f32 %s, %s, %%[s%d]" % (tb, tb, i))
     for j in range(8):
-        v.append("v_cvt_pk_bf16_f32 v%d, %%[s%d], %%[s%d]" % (PR0 + j, 2 * j, 2 * j + 1))
-    v.append("v_fma_f32 %%[lrun], %%[lrun], %%[alpha], %s" % TB)
+        v.append("v_cvt_pk_bf16_f32 v%d, %%[s%d], %%[s%d]" % (P0 + j, 2 * j, 2 * j + 1))
+    v.append("v_fma_f32 %%[lrun], %%[lrun], %%[alpha], %s" % tb)
     return v
 
 
-# The nine copies of the wave's share of the next stage, spread over the
-# whole iteration (the vector memory unit takes the four waves' copies one
-# at a time; bunched together they stall the issuing waves): lines 0..3
-# after these score MFMAs of A, lines 4..8 after these PV MFMAs of B.
-DMA_A = [1, 5, 9, 13]
-DMA_B = [2, 8, 14, 20, 26]
-
-
-def dma(seq, cg):
-    """Line cg of this wave's share of the next stage: buffer -> LDS copy of
-    1 KiB (M0 = LDS base of the line; the copy counts in vmcnt, not lgkmcnt)."""
-    seq.op("s_add_u32 m0, %%[mb], 0x%x" % (cg * 1024))
-    seq.op("s_nop 0")
-    seq.op("buffer_load_dwordx4 %%[go], %%[rs], %%[so%d] offen lds" % cg)
-
-
-def gen_a(mask=True):
+def gen_pro(mask):
     s = Seq()
     s.op("s_nop 1")
     for ks in range(PF_K):
         kread(s, ks)
-    valu = softmax_max(mask)
-    per = (len(valu) + A_STEPS - 1) // A_STEPS
-    for ks in range(A_STEPS):
-        score_mfma(s, ks, ks == 0)
-        kread(s, ks + PF_K)               # the last PF_K of these are template B's first k-steps
-        if ks in DMA_A:
-            dma(s, DMA_A.index(ks))
-        for ins in valu[ks * per:(ks + 1) * per]:
-            s.op(ins)
-    s.drain()
-    s.lines += GUARD
+    for ks in range(KSTEPS):
+        score_mfma(s, ks)
+        if ks + PF_K < KSTEPS:
+            kread(s, ks + PF_K)
+    s.lines += GUARD                 # scores settle before the VALU reads them
+    s.lines += softmax_max(mask)
     return s.text()
 
 
-B_VALU_STEPS = 13      # score MFMAs of B that carry the exp half of the softmax
-
-
-def gen_b(first=False):
+def gen_iter(mask, first):
     s = Seq()
     s.op("s_nop 1")
-    valu = softmax_exp()
-    per = (len(valu) + B_VALU_STEPS - 1) // B_VALU_STEPS
+    for ks in range(PF_K):
+        kread(s, ks)
+    # a few probability instructions cover the latency of the first K read
+    exp_valu = softmax_exp()
+    lead, rest = exp_valu[:8], exp_valu[8:]
+    per = (len(rest) + S_VALU_STEPS - 1) // S_VALU_STEPS
+    for ins in lead:
+        s.op(ins)
     vnext = 0
-    for j in range(KSTEPS - A_STEPS):
-        ks = A_STEPS + j
-        score_mfma(s, ks, False)
+    for ks in range(KSTEPS):
+        score_mfma(s, ks)
         if ks + PF_K < KSTEPS:
             kread(s, ks + PF_K)
-        elif vnext < PF_V:                 # K reads done: start the V^T ring
+        elif vnext < PF_V:                 # K reads done: fill the V^T ring
             vread(s, vnext)
             vnext += 1
-        for ins in valu[j * per:(j + 1) * per]:
+        if ks in DMA_S:
+            dma(s, DMA_S.index(ks))
+        for ins in rest[ks * per:(ks + 1) * per]:
             s.op(ins)
     while vnext < PF_V:
         vread(s, vnext)
         vnext += 1
+    max_valu = softmax_max(mask)
+    nsteps = 32 - P_VALU_FROM - 2
+    mper = (len(max_valu) + nsteps - 1) // nsteps
     for j in range(32):
         s.need("V%db" % j)
         acc = "0" if first and j % 2 == 0 else "%%[o%d]" % (j >> 1)   # first half tile: start from 0
         s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %s, %s" % (j >> 1, VRING[j % PF_V][2], P_OP[j & 1], acc))
         if j + PF_V < 32:
             vread(s, j + PF_V)
-        if j in DMA_B:
-            dma(s, len(DMA_A) + DMA_B.index(j))
+        if j in DMA_P:
+            dma(s, len(DMA_S) + DMA_P.index(j))
+        if j == P_VALU_FROM:
+            s.op("s_nop 7")                # the last score MFMA's result settles
+            s.op("s_nop 7")
+            s.op("s_nop 3")
+        if j >= P_VALU_FROM:
+            k = j - P_VALU_FROM
+            for ins in max_valu[k * mper:(k + 1) * mper]:
+                s.op(ins)
     s.drain()
     s.lines += GUARD
     return s.text()
@@ -241,27 +253,24 @@ def gen_b(first=False):
 def main():
     out = os.path.join(HERE, "own_asm.inc")
     body = ["// Generated by gen_own_asm.py; do not edit.", ""]
-    for name, text in (("OWN_ASM_PRO", gen_pro()), ("OWN_ASM_A", gen_a()), ("OWN_ASM_A_FULL", gen_a(False)),
-                       ("OWN_ASM_B", gen_b()), ("OWN_ASM_B_FIRST", gen_b(True))):
+    # the key mask always runs: in phase P its VALU work hides under the PV
+    # MFMAs, and one sequence per call site keeps register allocation simple
+    temps = [("OWN_ASM_PRO", gen_pro(True)), ("OWN_ASM_IT", gen_iter(True, False)),
+             ("OWN_ASM_IT_FIRST", gen_iter(True, True))]
+    for name, text in temps:
         body.append('#define %s "%s"' % (name, text))
         body.append("")
     # operand lists (names of attn_own_kernel's variables)
     ops = {
-        "OWN_OPS_Q0_17": ", ".join('[q%d] "v"(qf[%d])' % (i, i) for i in range(A_STEPS)),
-        "OWN_OPS_Q18_35": ", ".join('[q%d] "v"(qf[%d])' % (i, i) for i in range(A_STEPS, KSTEPS)),
-        "OWN_OPS_Q0_35": ", ".join('[q%d] "v"(qf[%d])' % (i, i) for i in range(KSTEPS)),
+        "OWN_OPS_Q": ", ".join('[q%d] "v"(qf[%d])' % (i, i) for i in range(KSTEPS)),
         "OWN_OPS_KA": ", ".join('[ka%d] "v"(ka[%d])' % (i, i) for i in range(4)),
         "OWN_OPS_VA": ", ".join('[va%d] "v"(va[%d])' % (i, i) for i in range(4)),
-        "OWN_OPS_KB_OUT": ", ".join('[kb%d] "=&v"(kb[%d])' % (i, i) for i in range(PF_K)),
-        "OWN_OPS_KB_INOUT": ", ".join('[kb%d] "+v"(kb[%d])' % (i, i) for i in range(PF_K)),
+        "OWN_OPS_S_OUT": ", ".join('[s%d] "=&v"(s[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_S": ", ".join('[s%d] "+v"(s[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_O": ", ".join('[o%d] "+a"(o[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_O_OUT": ", ".join('[o%d] "=&a"(o[%d])' % (i, i) for i in range(16)),
-        "OWN_OPS_SO_A": ", ".join('[so%d] "s"(so[%d])' % (i, i) for i in range(len(DMA_A))),
-        "OWN_OPS_SO_B": ", ".join('[so%d] "s"(so[%d])' % (i, i) for i in range(len(DMA_A), 9)),
-        "OWN_CLOB_A": ", ".join('"%s"' % r for r in TA),
-        "OWN_CLOB_B": ", ".join('"v%d"' % r for r in range(B_CLOB0, 256)),
-        "OWN_PF_K": str(PF_K),
+        "OWN_OPS_SO": ", ".join('[so%d] "s"(so[%d])' % (i, i) for i in range(9)),
+        "OWN_CLOB": ", ".join('"v%d"' % r for r in range(CLOB_LO, 256)),
     }
     for name, text in ops.items():
         body.append("#define %s %s" % (name, text))
