@@ -26,7 +26,7 @@ Templates (iteration e scores half tile e+1 and accumulates half tile e):
                  fragments read transposed, carrying the first half of the
                  softmax of half tile e+1 (with the key mask);
         nine buffer -> LDS copies of this wave's share of half tile e+3 are
-        spread over both phases; FIRST starts the PV accumulators from zero.
+        spread over phase S; FIRST starts the PV accumulators from zero.
 
 The MFMA is v_mfma_f32_32x32x16_bf16 throughout. Run: python gen_own_asm.py
 (the build runs it before compiling).
@@ -56,11 +56,11 @@ TMP = ["v%d" % (T0 + i) for i in range(4)]
 CLOB_LO = T0
 GUARD = ["s_nop 7", "s_nop 7", "s_nop 7"]   # MFMA results settle before the compiler's code reads them
 
-# the nine copies of the next stage: lines 0..4 after these score MFMAs,
-# lines 5..8 after these PV MFMAs (the vector memory unit takes the four
-# waves' copies one at a time; bunched together they stall the issuing waves)
-DMA_S = [2, 9, 16, 23, 30]
-DMA_P = [3, 11, 19, 27]
+# the nine copies of the next stage, one after every fourth score MFMA (the
+# vector memory unit takes the four waves' copies one at a time; bunched
+# together they stall the issuing waves; issued in phase P they arrive later)
+DMA_S = [1, 5, 9, 13, 17, 21, 25, 29, 33]
+DMA_P = []
 S_VALU_STEPS = 16    # score MFMAs that carry the probability half of the softmax
 P_VALU_FROM = 3      # PV MFMA after which the max half of the softmax starts
 
