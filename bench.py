@@ -4,13 +4,16 @@ A step is the whole hot path for one batch: mla_cache_append (the B*Lq new
 tokens) -> mla_absorb_q -> mla_decode_attn (split + combine) -> mla_out_up,
 with every input already resident in HBM. The default workload is the
 128-head, 16k-context decode (B=32, H=128, L=16384, Lq=1, block tables
-randomly permuted over the pool), the configuration the >=70 %-of-roofline
-target is stated on.
+randomly permuted over the pool).
 
 Prints one JSON line: throughput (tokens/s) over HIP-graph replays of the
-whole step, per-call times from eager steps with HIP events around each call,
-the attention call's roofline (algorithmic bytes / HIP-event duration vs
-8 TB/s HBM), and the fp64 oracle timed on the host cores on a bounded sample.
+whole step, per-call times from eager steps with HIP events around each call
+(median, p10, p90), the attention call's roofline (algorithmic bytes /
+HIP-event duration vs 8 TB/s HBM and 2.5 PFLOP/s bf16), the same call against
+what this box achieves on a plain stream read and on a loop of bf16 MFMAs,
+the call with caches flushed before every step (a 1 GiB read evicts L2 and
+the 256 MiB MALL), and the fp64 oracle timed on the host cores on a bounded
+sample.
 """
 
 from __future__ import annotations
@@ -31,6 +34,7 @@ ROW_BYTES = 576 * 2
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--cold-steps", type=int, default=20, help="steps timed after a cache flush each")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="v3_b32_h128_l16384")
@@ -81,6 +85,47 @@ def traffic_from(fetch_dir: str, write_dir: str, workload: str) -> dict:
             "bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
             "fetch_scale": f_scale, "write_scale": w_scale,
             "raw_kib": {"fetch": fe, "write": wr}}
+
+
+def achievable_peaks(torch, dev) -> dict:
+    """What this machine reaches with the probes of libmla_probe.so: a plain
+    stream read of 2 GiB (16-byte loads, eight in flight per thread, 2048
+    workgroups) and a loop of back-to-back bf16 32x32x16 MFMAs on every SIMD;
+    median of 10 and of 5 launches, HIP events. The practical ceilings next to
+    the datasheet peaks."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "mla_latent_cache_append_amd",
+                                   "libmla_probe.so"))
+    lib.mla_probe_stream_read.restype = ctypes.c_int
+    lib.mla_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_probe_mfma.restype = ctypes.c_int
+    lib.mla_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 2 * COPY_BYTES
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    out = torch.empty(2048 * 256 * 4, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps, skip):
+        ts = []
+        for i in range(reps + skip):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            assert fn() == 0
+            e1.record()
+            e1.synchronize()
+            if i >= skip:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    t_read = timed(lambda: lib.mla_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                                     ctypes.c_void_p(out.data_ptr()), stream), 10, 3)
+    waves4, iters = 1024, 2000
+    t_mfma = timed(lambda: lib.mla_probe_mfma(waves4, iters, ctypes.c_void_p(out.data_ptr()), stream), 5, 2)
+    del buf, out
+    return {"hbm_read_GBps": nbytes / t_read / 1e9,
+            "hbm_read_probe": "stream read of 2 GiB, 16-byte loads, median of 10",
+            "mfma_bf16_TFLOPs": waves4 * 4 * 4 * iters * 32768 / t_mfma / 1e12,
+            "mfma_probe": "back-to-back v_mfma_f32_32x32x16_bf16, 4 chains per wave, 16 waves per CU, median of 5"}
 
 
 def algorithmic(w):
@@ -234,6 +279,21 @@ def main():
             per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # us
     step_us = [evs[i][0].elapsed_time(evs[i][4]) * 1e3 for i in range(args.steps)]
     med = {n: float(np.median(v)) for n, v in per.items()}
+    pct = {n: {"p10": float(np.percentile(v, 10)), "p90": float(np.percentile(v, 90))} for n, v in per.items()}
+
+    # cold steps: a 1 GiB read between steps evicts L2 and MALL (a read
+    # leaves no dirty lines to write back during the step), so every step
+    # reads the cache and the weights from HBM; events around each call
+    flush = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    cold = {n: [] for n in names}
+    for i in range(args.cold_steps):
+        flush.sum()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        one_step(ev)
+        torch.cuda.synchronize()
+        for j, n in enumerate(names):
+            cold[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+    del flush
 
     # graph steps: the whole step recorded once as a HIP graph and replayed, the
     # way a decode loop issues it; this is the timed throughput
@@ -252,6 +312,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = max(wall * 1e3, g0.elapsed_time(g1)) / args.steps
 
+    ach = achievable_peaks(torch, dev)
     alg = algorithmic(w)
     attn_s = med["decode_attn"] * 1e-6
     achieved_gbps = alg["attn_bytes"] / attn_s / 1e9
@@ -291,6 +352,12 @@ def main():
         "mfma_TFLOPs": tflops,
         "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
         "call_us_median": med,
+        "call_us_p10_p90": pct,
+        "achievable": dict(ach, frac_hbm=achieved_gbps / ach["hbm_read_GBps"],
+                           frac_mfma=tflops / ach["mfma_bf16_TFLOPs"]),
+        "cold_cache": {"steps": args.cold_steps,
+                       "call_us_median": {n: float(np.median(v)) for n, v in cold.items()},
+                       "decode_attn_GBps": alg["attn_bytes"] / (float(np.median(cold["decode_attn"])) * 1e-6) / 1e9},
         "step_mode": "hip_graph replay of the whole step (eager per-call events give call_us_median)",
         "eager_ms_per_step": eager_wall * 1e3 / args.steps,
         "eager_step_us_median_events": float(np.median(step_us)),

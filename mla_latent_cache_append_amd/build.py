@@ -1,4 +1,5 @@
-"""Compile libmla_absorb.so (HIP kernels + C ABI) for gfx950, in-tree."""
+"""Compile libmla_absorb.so (HIP kernels + C ABI) and the measurement probes
+libmla_probe.so for gfx950, in-tree."""
 
 import os
 import subprocess
@@ -8,6 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_absorb.so")
+PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
 SOURCES = ["append.hip", "gemm.hip", "attn.hip", "capi.cpp"]
 
 HIPCC_FLAGS = [
@@ -36,6 +38,13 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libmla_absorb.so")
     os.replace(tmp, LIB)
+    # the measurement probes bench.py reports next to the datasheet peaks
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([hipcc, *HIPCC_FLAGS, "-o", tmp, os.path.join(CSRC, "probe.hip")], capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libmla_probe.so")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

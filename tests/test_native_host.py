@@ -88,3 +88,13 @@ def test_invalid_arguments_return_status(nat):
     d.softmax_scale = 0.0
     assert lib.mla_out_up(ctypes.byref(d), fake, fake, fake, 1, null) == nat.MLA_ERR_INVALID_ARG
     assert lib.mla_cache_append(None, fake, fake, fake, fake, fake, 4, 1, null) == nat.MLA_ERR_INVALID_ARG
+
+
+def test_probe_library_exports_its_two_probes(nat):
+    # the stream-read and MFMA-loop probes bench.py reports as achievable peaks
+    from mla_latent_cache_append_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        build.build()
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    for n in ("mla_probe_stream_read", "mla_probe_mfma"):
+        assert hasattr(lib, n), n
