@@ -872,11 +872,6 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float f) {
   asm volatile("" : "+a"(acc));
 }
 
-// Slot swizzle of the query staging blocks: for a fixed chunk, the 16 rows
-// that 16 lanes of a fragment read (8 rows i of two row groups g) land on 16
-// distinct 16-byte bank groups.
-__device__ __forceinline__ int qswz(int i, int g) { return ((i >> 1) & 3) | ((g & 1) << 2); }
-
 __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[OSTAGE * HT_BYTES];
   lds_char* stages = (lds_char*)smem;
@@ -962,14 +957,6 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
       const int n_valid = min(HT_TOK, L - e * HT_TOK);
       rs = buffer_rsrc((const char*)a.pool + (int64_t)blk * TILE_BYTES + (e & 1) * HT_BYTES, n_valid * ROW_BYTES);
     };
-    auto issue = [&](int e) {
-      sgpr_x4 rs;
-      uint32_t mb;
-      prep(e, blk_of(e), rs, mb);
-#pragma unroll
-      for (int cg = 0; cg < 9; ++cg) buffer_load_lds_16(rs, goff, so[cg], mb + cg * 1024);
-    };
-
     // LDS addresses of the K fragments (stage of half tile e) and of the V^T
     // fragments (stage of half tile e), as the instruction sequences take them
     uint32_t ka[4], va[4];
@@ -997,42 +984,33 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     // running max moves only in steps above 8 in log2 units). On the last
     // half tile the scores rerun on stage e: their max never exceeds the
     // running max, so the state is left as it is.
-    // Query fragments (B operand of S^T: row r, features 16 ks + 8 h .. +7)
-    // come through the LDS, which the stages do not use yet. On the global
-    // side every 8 lanes of a copy read one whole 128-byte line of a query
-    // row; a direct load per fragment would touch 32 rows per instruction,
-    // 32 bytes of each. Wave w copies and reads only its own 32 rows (36
-    // blocks of 1 KiB: block (m, g) holds line m of rows 32 w + 8 g + i,
-    // chunk p of row i at slot 8 i + (p ^ qswz(i, g))), so its own vmcnt wait
-    // is enough; rows past the last query row read as zeros.
+    // Start of the segment, in one instruction sequence: the copies of half
+    // tile e0, the query fragments (B operand of S^T: row r, features
+    // 16 ks + 8 h .. +7) loaded straight into registers, then the copies of
+    // e0+1 and e0+2; it returns once e0 and the fragments have arrived, so
+    // the query loads overlap the first copies' trip to memory. A fragment
+    // load reads 32 bytes of each of 32 query rows; the rows are shared by
+    // the workgroups of the sequence and come from L2. Rows past the last
+    // query row read as zeros (the descriptor ends there).
     u32x4 qf[KSTEPS16];
     {
       const int nv = max(0, min(128, a.rows - rg * 128));
       sgpr_x4 qr = buffer_rsrc(a.q + ((int64_t)b * a.rows + rg * 128) * D_K, nv * ROW_BYTES);
 #pragma unroll
       for (int k = 0; k < 4; ++k) qr[k] = (uint32_t)uni((int)qr[k]);   // uniform: keep it in SGPRs
-      const uint32_t qdst = lds_addr(stages) + wave * 36 * 1024;
-      const int i = lane >> 3, sl = lane & 7;
-      const uint32_t qoff[2] = {(uint32_t)(i * ROW_BYTES + 16 * (sl ^ qswz(i, 0))),
-                                (uint32_t)(i * ROW_BYTES + 16 * (sl ^ qswz(i, 1)))};
-#pragma unroll
-      for (int m = 0; m < 9; ++m)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          buffer_load_lds_16(qr, qoff[g & 1], (32 * wave + 8 * g) * ROW_BYTES + m * 128, qdst + (m * 4 + g) * 1024);
-      wait_vmem_n<0>();
-      const int ii = c32 & 7, g = c32 >> 3;
-      lds_char* qsrc = stages + wave * 36 * 1024 + g * 1024 + ii * 128;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS16; ++ks)
-        qf[ks] = lds_read_b128(qsrc, (ks >> 2) * 4096 + 16 * ((2 * (ks & 3) + h) ^ qswz(ii, g)));
+      const uint32_t qv = (uint32_t)((32 * wave + c32) * ROW_BYTES + 16 * h);
+      sgpr_x4 rs0, rs1, rs2;
+      uint32_t mb0, mb1, mb2;
+      prep(e0, blk_of(e0), rs0, mb0);
+      prep(e0 + 1, blk_of(e0 + 1), rs1, mb1);
+      prep(e0 + 2, blk_of(e0 + 2), rs2, mb2);
+      asm volatile(OWN_ASM_QLOAD
+                   : OWN_OPS_Q_OUT
+                   : [qv] "v"(qv), [qr] "s"(qr), [mb0] "s"(mb0), [rs0] "s"(rs0), [mb1] "s"(mb1), [rs1] "s"(rs1),
+                     [mb2] "s"(mb2), [rs2] "s"(rs2), [go] "v"(goff), OWN_OPS_SO
+                   : "m0", "memory");
     }
-    lds_barrier();                         // every wave holds its fragments; the LDS is free
-    // Stage e0 is awaited alone, so the first scores start on it while the
-    // next two stages are still on their way.
-    for (int e = e0; e < e0 + OSTAGE - 1; ++e) issue(e);
-    wait_vmem_n<18>();
-    lds_barrier();
+    lds_barrier();                         // every wave's copies of e0 are in the LDS
     k_addr(e0);
     float s[16];          // masked scores of the half tile whose PV comes next
     float alpha, mref;    // its rescale factor and probability reference
@@ -1098,6 +1076,9 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     l_run += __shfl_xor(l_run, 32);
     {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      // the copies issued past the segment's end (zero-byte descriptors) still
+      // write zeros into their stages: let them land before the staging
+      wait_vmem_n<0>();
       lds_barrier();                       // every wave is done with the stages
       lds_char* orow_l = stages + (32 * wave + c32) * OUT_STRIDE + 8 * h;
 #pragma unroll

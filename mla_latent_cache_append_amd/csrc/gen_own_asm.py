@@ -13,6 +13,10 @@ rings, the packed probabilities, temporaries) sit in fixed registers listed
 as clobbers.
 
 Templates (iteration e scores half tile e+1 and accumulates half tile e):
+  OWN_ASM_QLOAD
+        start of a segment: copies of its first three half tiles with the
+        query fragments loaded in between, waiting for the first half tile
+        and the fragments
   OWN_ASM_PRO
         scores of the first half tile of a segment (36 k-steps), then the
         first half of its softmax (key mask, row max, rescale factor, new
@@ -106,22 +110,29 @@ def score_mfma(seq, ks):
     seq.op("v_mfma_f32_32x32x16_bf16 %s, %s, %%[q%d], %s" % (SN, KRING[ks % PF_K], ks, "0" if ks == 0 else SN))
 
 
+def pv_step(j):
+    """Column block and token block of PV step j. The 16 column blocks of
+    token block 0 come first, then those of token block 1, so an MFMA never
+    accumulates onto the result of the one just before it."""
+    return j % 16, j // 16
+
+
 def vread(seq, j):
-    """V^T fragment of PV step j (column block j / 2, token block j % 2): two
-    transposing reads into the two halves of ring slot j % PF_V."""
-    cb, kk = j >> 1, j & 1
+    """V^T fragment of PV step j: two transposing reads into the two halves
+    of ring slot j % PF_V."""
+    cb, kk = pv_step(j)
     lo, hi, _ = VRING[j % PF_V]
     seq.lds("ds_read_b64_tr_b16 %s, %%[va%d] offset:%d" % (lo, cb & 1, kk * 18432 + (cb >> 1) * 1024), "V%da" % j)
     seq.lds("ds_read_b64_tr_b16 %s, %%[va%d] offset:%d" % (hi, 2 + (cb & 1), kk * 18432 + 9216 + (cb >> 1) * 1024),
             "V%db" % j)
 
 
-def dma(seq, cg):
-    """Line cg of this wave's share of the next stage: buffer -> LDS copy of
-    1 KiB (M0 = LDS base of the line; the copy counts in vmcnt, not lgkmcnt)."""
-    seq.op("s_add_u32 m0, %%[mb], 0x%x" % (cg * 1024))
+def dma(seq, cg, mb="mb", rs="rs"):
+    """Line cg of this wave's share of a stage: buffer -> LDS copy of 1 KiB
+    (M0 = LDS base of the line; the copy counts in vmcnt, not lgkmcnt)."""
+    seq.op("s_add_u32 m0, %%[%s], 0x%x" % (mb, cg * 1024))
     seq.op("s_nop 0")
-    seq.op("buffer_load_dwordx4 %%[go], %%[rs], %%[so%d] offen lds" % cg)
+    seq.op("buffer_load_dwordx4 %%[go], %%[%s], %%[so%d] offen lds" % (rs, cg))
 
 
 def sn_reg(i):
@@ -186,6 +197,24 @@ def softmax_exp():
     return v
 
 
+def gen_qload():
+    """Start of a segment: the copies of the first half tile, the 36 query
+    fragments straight into registers (row 32 wave + l % 32 at byte offset
+    qv, k-step ks at + 32 ks), then the copies of the next two half tiles;
+    returns once the first half tile and the fragments have arrived (vector
+    memory results count down in issue order)."""
+    s = Seq()
+    for cg in range(9):
+        dma(s, cg, "mb0", "rs0")
+    for ks in range(KSTEPS):
+        s.op("buffer_load_dwordx4 %%[q%d], %%[qv], %%[qr], 0 offen offset:%d" % (ks, 32 * ks))
+    for st in (1, 2):
+        for cg in range(9):
+            dma(s, cg, "mb%d" % st, "rs%d" % st)
+    s.op("s_waitcnt vmcnt(18)")
+    return s.text()
+
+
 def gen_pro(mask):
     s = Seq()
     s.op("s_nop 1")
@@ -231,8 +260,9 @@ def gen_iter(mask, first):
     mper = (len(max_valu) + nsteps - 1) // nsteps
     for j in range(32):
         s.need("V%db" % j)
-        acc = "0" if first and j % 2 == 0 else "%%[o%d]" % (j >> 1)   # first half tile: start from 0
-        s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %s, %s" % (j >> 1, VRING[j % PF_V][2], P_OP[j & 1], acc))
+        cb, kk = pv_step(j)
+        acc = "0" if first and kk == 0 else "%%[o%d]" % cb   # first half tile: start from 0
+        s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %s, %s" % (cb, VRING[j % PF_V][2], P_OP[kk], acc))
         if j + PF_V < 32:
             vread(s, j + PF_V)
         if j in DMA_P:
@@ -255,7 +285,7 @@ def main():
     body = ["// Generated by gen_own_asm.py; do not edit.", ""]
     # the key mask always runs: in phase P its VALU work hides under the PV
     # MFMAs, and one sequence per call site keeps register allocation simple
-    temps = [("OWN_ASM_PRO", gen_pro(True)), ("OWN_ASM_IT", gen_iter(True, False)),
+    temps = [("OWN_ASM_QLOAD", gen_qload()), ("OWN_ASM_PRO", gen_pro(True)), ("OWN_ASM_IT", gen_iter(True, False)),
              ("OWN_ASM_IT_FIRST", gen_iter(True, True))]
     for name, text in temps:
         body.append('#define %s "%s"' % (name, text))
@@ -263,6 +293,7 @@ def main():
     # operand lists (names of attn_own_kernel's variables)
     ops = {
         "OWN_OPS_Q": ", ".join('[q%d] "v"(qf[%d])' % (i, i) for i in range(KSTEPS)),
+        "OWN_OPS_Q_OUT": ", ".join('[q%d] "=&v"(qf[%d])' % (i, i) for i in range(KSTEPS)),
         "OWN_OPS_KA": ", ".join('[ka%d] "v"(ka[%d])' % (i, i) for i in range(4)),
         "OWN_OPS_VA": ", ".join('[va%d] "v"(va[%d])' % (i, i) for i in range(4)),
         "OWN_OPS_S_OUT": ", ".join('[s%d] "=&v"(s[%d])' % (i, i) for i in range(16)),
