@@ -133,6 +133,9 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t Lq);
  *   o_lat        device [B*Lq][H][512] bf16
  *   lse          device [B*Lq][H] float32, or NULL
  *   workspace    device, at least mla_decode_workspace_size(dims, B, Lq) bytes
+ * Lq may be a whole prefill chunk (many new tokens per sequence). Returns
+ * MLA_ERR_UNSUPPORTED when H is not a multiple of 16, Lq*H exceeds 2^20, the
+ * table spans more than 2^30 keys, or B*ceil(Lq*H/4) exceeds 2^31-1.
  * Device-value handling: a length above max_blocks_per_seq*64 or a block id
  * outside [0, num_blocks) makes that sequence's outputs NaN (never an
  * out-of-bounds access); a length <= 0 gives zero outputs and lse = -inf, as
@@ -155,6 +158,23 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
  */
 int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o,
                int32_t N, void* stream);
+
+/*
+ * mla_linear — a bias-free linear map, for the projections around the
+ * attention ([MLA80] §2: Wdq, Wuq, Wqr, Wdkv, Wkr and the output projection
+ * Wo are nn.Linear(bias=False) maps of the layer).
+ * y[n] = W x[n] (+ residual[n])
+ *   x         device [N][K] bf16
+ *   w         device [M][K] bf16 (nn.Linear weight layout: [out][in])
+ *   residual  device [N][M] bf16, or NULL; may be the same buffer as y
+ *   y         device [N][M] bf16
+ * fp32 accumulation (bf16 MFMA), the residual added in fp32, one rounding to
+ * bf16. K must be a multiple of 32 and M of 4, N at most 2,097,120
+ * (MLA_ERR_UNSUPPORTED otherwise); null pointers or sizes <= 0 give
+ * MLA_ERR_INVALID_ARG. Deterministic (fixed summation order).
+ */
+int mla_linear(const uint16_t* x, const uint16_t* w, const uint16_t* residual, uint16_t* y,
+               int32_t N, int32_t K, int32_t M, void* stream);
 
 #ifdef __cplusplus
 }

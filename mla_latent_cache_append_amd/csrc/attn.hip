@@ -1129,8 +1129,9 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
 // so a row with up to 8 partials costs two memory round trips.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int b = blockIdx.x;
-  const int r = blockIdx.y * 4 + wave;
+  const int rb = (a.rows + 3) >> 2;           // workgroups per sequence, four rows each
+  const int b = (int)(blockIdx.x / (unsigned)rb);
+  const int r = (int)(blockIdx.x - (unsigned)b * (unsigned)rb) * 4 + wave;
   if (r >= a.rows) return;
   // total tiles T, first tile of sequence b, and its tile count
   int64_t T = 0, start = 0;
@@ -1282,7 +1283,7 @@ hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t n
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(B, (a.rows + 3) / 4), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)B * (unsigned)((a.rows + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -87,6 +87,8 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
   // rows of one sequence index 32-bit offsets inside the kernels
   if ((int64_t)Lq * dims->num_heads > (1 << 20) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
     return MLA_ERR_UNSUPPORTED;
+  // the merge launches one workgroup per four query rows of every sequence
+  if ((int64_t)B * (((int64_t)Lq * dims->num_heads + 3) / 4) > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
   const size_t need = mla::attention_workspace_bytes(B, Lq, dims->num_heads);
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   return launch_status(mla::launch_decode_attn(q, pool, num_blocks, block_table, max_blocks_per_seq,
@@ -102,6 +104,13 @@ int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv
   if (!o_lat || !w_uv || !o || N <= 0) return MLA_ERR_INVALID_ARG;
   return launch_status(
       mla::launch_out_up(o_lat, w_uv, o, N, dims->num_heads, (hipStream_t)stream));
+}
+
+int mla_linear(const uint16_t* x, const uint16_t* w, const uint16_t* residual, uint16_t* y,
+               int32_t N, int32_t K, int32_t M, void* stream) {
+  if (!x || !w || !y || N <= 0 || K <= 0 || M <= 0) return MLA_ERR_INVALID_ARG;
+  if (K % 32 != 0 || M % 4 != 0 || N > 65535 * 32) return MLA_ERR_UNSUPPORTED;
+  return launch_status(mla::launch_linear(x, w, residual, y, N, K, M, (hipStream_t)stream));
 }
 
 }  // extern "C"

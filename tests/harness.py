@@ -153,6 +153,37 @@ def oracle_seq(w: workloads.Workload, b: int, step: int = 0, q_nope=None, q_pe=N
     return orc.absorbed_decode(f(q_nope[sl]), f(q_pe[sl]), f(ckv), f(kpe), f(wuk), f(wuv))
 
 
+def oracle_queries(w: workloads.Workload, b: int, idx, step: int = 0) -> dict:
+    """fp64 oracle outputs of query tokens idx (indices into the Lq new
+    tokens) of sequence b only, at their absolute positions: the oracle's
+    steps on a subset of rows, for sequences too long to take whole."""
+    Lq = w.Lq
+    q_nope, q_pe = w.queries(step)
+    f = orc.bf16_bits_to_f64
+    L = int(w.lens[b])
+    ckv, kpe = w.seq_cache(b)
+    wuk, wuv = w.weights()
+    rows = b * Lq + np.asarray(idx)
+    q_pos = L - Lq + np.asarray(idx, dtype=np.int64)
+    c_kv = f(ckv)
+    k_r = orc.rope(f(kpe), np.arange(L))
+    q_lat, q_r = orc.absorb_q(f(q_nope[rows]), f(q_pe[rows]), q_pos, f(wuk))
+    o_lat, lse = orc.latent_attention(q_lat, q_r, c_kv, k_r, q_pos, orc.default_scale())
+    return dict(q_lat=q_lat, q_r=q_r, o_lat=o_lat, lse=lse, o=orc.out_up(o_lat, f(wuv)))
+
+
+def check_queries(name: str, w, out: dict, b: int, idx) -> None:
+    """Compare the GPU outputs of query tokens idx of sequence b with the oracle."""
+    ref = oracle_queries(w, b, idx)
+    rows = b * w.Lq + np.asarray(idx)
+    q = orc.bf16_bits_to_f64(out["q"][rows])
+    assert_parity(f"{name} b={b} q_lat", q[..., :512], ref["q_lat"])
+    assert_parity(f"{name} b={b} q_r", q[..., 512:], ref["q_r"])
+    assert_parity(f"{name} b={b} o_lat", orc.bf16_bits_to_f64(out["o_lat"][rows]), ref["o_lat"])
+    assert_parity(f"{name} b={b} lse", out["lse"][rows], ref["lse"], max_rel=2e-2, mean_rel=5e-3)
+    assert_parity(f"{name} b={b} o", orc.bf16_bits_to_f64(out["o"][rows]), ref["o"])
+
+
 def check_seq(name: str, w, out: dict, b: int, ref: dict | None = None) -> None:
     """Compare the GPU outputs of sequence b with the oracle, stage by stage."""
     ref = oracle_seq(w, b) if ref is None else ref

@@ -76,6 +76,9 @@ def test_append_skips_out_of_range_slots():
     (128, 1, [1, 64, 65, 700]),
     (128, 8, [8, 9, 71, 200]),
     (16, 3, [3, 4, 64, 66, 190]),
+    # prefill chunks: many query tokens per sequence, causal among themselves
+    (128, 64, [64, 100, 1000]),
+    (16, 203, [203, 777]),
 ], ids=lambda v: str(v))
 def test_decode_step_small(H, Lq, lens):
     name = {16: "v2lite_b64_h16_l4096", 32: "v2lite_b64_h16_l4096"}.get(H, "v3_b32_h128_l16384")
@@ -187,3 +190,16 @@ def test_full_size_sampled(name):
     picks = sorted({0, w.B - 1, int(np.argmax(w.lens)), int(np.argmin(w.lens)), w.B // 2})
     for b in picks:
         hz.check_seq(name, w, out, b)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", workloads.PREFILL_WORKLOADS)
+def test_prefill_chunk_full_size_sampled(name):
+    """A 512-token prefill chunk on a 16k context at 128 heads: 65,536 query
+    rows per sequence. The oracle takes a few query tokens of each sequence
+    (the first, the last and two between), the GPU computes all of them."""
+    w = workloads.make(name, seed=0)
+    _say(f"prefill chunk {name}: B={w.B} H={w.H} Lq={w.Lq} total keys={int(w.lens.sum())}")
+    out = hz.GpuRun(w).run()
+    for b in (0, w.B - 1):
+        hz.check_queries(name, w, out, b, [0, 1, w.Lq // 2 + 3, w.Lq - 1])

@@ -52,3 +52,25 @@ def test_query_positions_and_slots():
     s = w.slots(1, np.arange(100))
     assert len(np.unique(s)) == 100
     assert np.all(s // 64 == np.repeat(w.block_table[1, :2], 64)[:100])
+
+
+def test_prefill_chunk_workload_shape():
+    w = workloads.make("chunk512_b4_h128_l16896", seed=0)
+    assert (w.B, w.H, w.Lq, w.N) == (4, 128, 512, 2048)
+    assert np.all(w.lens == 16896) and w.num_blocks == 4 * 264
+    q = w.query_positions()
+    assert q[0] == 16384 and q[511] == 16895 and q[512] == 16384
+
+
+def test_query_subset_oracle_matches_whole_sequence():
+    # the sampled check used at full size takes the oracle's steps on a
+    # subset of query tokens; on a small case it must give the same rows
+    from tests import harness as hz
+    w = workloads.Workload("subset", 2, 16, 6, [6, 40], "permuted", seed=21)
+    for b in (0, 1):
+        full = hz.oracle_seq(w, b)
+        idx = [0, 3, 5]
+        part = hz.oracle_queries(w, b, idx)
+        for k in ("q_lat", "q_r", "o_lat", "o"):
+            np.testing.assert_allclose(part[k], full[k][idx], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(part["lse"], full["lse"][idx], rtol=1e-12, atol=1e-12)

@@ -142,6 +142,11 @@ def make(name: str, seed: int = 0, B: int | None = None, L: int | None = None,
         B = 16 if B is None else B
         L = 65536 + 8 if L is None else L
         return Workload(name, B, 128, 8, [L] * B if lens is None else lens, "permuted", seed)
+    if name == "chunk512_b4_h128_l16896":
+        # chunked prefill: a 512-token chunk appended to 16,384 cached tokens
+        B = 4 if B is None else B
+        L = 16384 + 512 if L is None else L
+        return Workload(name, B, 128, 512, [L] * B if lens is None else lens, "permuted", seed)
     raise KeyError(name)
 
 
@@ -152,3 +157,6 @@ FULL_WORKLOADS = (
     "ragged_b128_h128_l1to32768",
     "causal8_b16_h128_l65544",
 )
+
+# chunked prefill over the latent: many query tokens per sequence
+PREFILL_WORKLOADS = ("chunk512_b4_h128_l16896",)
