@@ -239,6 +239,65 @@ def naive_decode(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, scale=None, base=ROPE_BAS
 
 
 # --------------------------------------------------------------------------
+# one whole attention layer around the decode, and a stack of layers
+# ([MLA80] §2 MLA.__init__ / forward: the projections Wdq, Wuq, Wqr, Wdkv,
+# Wkr, Wo around the attention; [AUDIT] §9 item 4: error over several layers)
+
+
+def linear(x, w, dtype=np.float64) -> np.ndarray:
+    """nn.Linear without bias: y = x @ w.T, w stored [out, in] ([MLA80] §2)."""
+    return np.matmul(np.asarray(x, dtype=dtype), np.asarray(w, dtype=dtype).T)
+
+
+def layer_projections(h, lw, dtype=np.float64) -> dict:
+    """The new tokens' inputs of one layer from hidden states h [Lq, d_model]
+    ([MLA80] §2 forward): c_kv = Wdkv h, k_pe = Wkr h (un-rotated: RoPE is
+    applied where the key is used), qz = Wdq h, q_nope = Wuq qz and
+    q_pe = Wqr qz, split per head. ``lw`` maps the weight names to arrays in
+    nn.Linear layout ([out, in])."""
+    H = np.asarray(lw["w_uk"]).shape[0]
+    Lq = np.asarray(h).shape[0]
+    qz = linear(h, lw["w_dq"], dtype)
+    return dict(c_kv=linear(h, lw["w_dkv"], dtype), k_pe=linear(h, lw["w_kr"], dtype), qz=qz,
+                q_nope=linear(qz, lw["w_uq"], dtype).reshape(Lq, H, -1),
+                q_pe=linear(qz, lw["w_qr"], dtype).reshape(Lq, H, -1))
+
+
+def layer_decode(h, hist_c_kv, hist_k_pe, lw, path: str = "absorbed", dtype=np.float64) -> dict:
+    """One layer for one sequence: the Lq new tokens h [Lq, d_model] follow
+    hist_c_kv / hist_k_pe (the cached latents of the earlier tokens, keys
+    0 .. L-Lq-1); their own latents are appended before attending, and the
+    layer returns y = Wo [o_0 | ... | o_{H-1}] ([MLA80] §2: the heads'
+    outputs concatenated, then Wo). ``path`` picks the absorbed or the
+    expanded attention (the two definitions of the same result)."""
+    pr = layer_projections(h, lw, dtype)
+    c_kv = np.concatenate([np.asarray(hist_c_kv, dtype=dtype), pr["c_kv"]])
+    k_pe = np.concatenate([np.asarray(hist_k_pe, dtype=dtype), pr["k_pe"]])
+    if path == "absorbed":
+        att = absorbed_decode(pr["q_nope"], pr["q_pe"], c_kv, k_pe, lw["w_uk"], lw["w_uv"], dtype=dtype)
+    elif path == "naive":
+        att = naive_decode(pr["q_nope"], pr["q_pe"], c_kv, k_pe, lw["w_uk"], lw["w_uv"], dtype=dtype)
+    else:
+        raise ValueError(path)
+    Lq = np.asarray(h).shape[0]
+    y = linear(att["o"].reshape(Lq, -1), lw["w_o"], dtype)
+    return dict(pr, o=att["o"], y=y)
+
+
+def stack_decode(h0, hists, layers, dtype=np.float64) -> list:
+    """Layers applied in turn with a residual connection around each:
+    h_{l+1} = h_l + layer_l(h_l). The residual is a reading: the pages'
+    module is one layer returning Wo(o) alone, and a stack of layers adds its
+    output to the stream it read. Returns [h_1, ..., h_n]."""
+    h = np.asarray(h0, dtype=dtype)
+    out = []
+    for (hc, hk), lw in zip(hists, layers):
+        h = h + layer_decode(h, hc, hk, lw, dtype=dtype)["y"]
+        out.append(h)
+    return out
+
+
+# --------------------------------------------------------------------------
 # split-KV partials and their merge (flash-decode split of the key range)
 
 
