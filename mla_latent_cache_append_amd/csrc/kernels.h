@@ -31,6 +31,9 @@ hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_pe, const i
 hipError_t launch_out_up(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int32_t N,
                          int32_t H, hipStream_t stream);
 
+hipError_t launch_linear(const uint16_t* x, const uint16_t* w, const uint16_t* r, uint16_t* y,
+                         int32_t N, int32_t K, int32_t M, hipStream_t stream);
+
 // Split-KV plan shared by the host (workspace sizing, grid) and the kernels.
 struct AttnPlan {
   int variant;    // kernel shape, see attn.hip

@@ -58,6 +58,7 @@ _SIG = {
     "mla_decode_attn": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _I64, _P, _I32, _P, _I32, _I32,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
     "mla_out_up": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I32, _P]),
+    "mla_linear": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _P]),
 }
 
 
@@ -176,6 +177,18 @@ def mla_out_up(dims: MlaDims, o_lat, w_uv, o, stream=None):
     _check("o", o, torch.bfloat16, (N, H, D_V))
     _ok("mla_out_up", lib().mla_out_up(
         ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), _ptr(o), N, _stream(stream)))
+
+
+def mla_linear(x, w, y, residual=None, stream=None):
+    """y[n] = W x[n] (+ residual[n]); x [N, K], w [M, K], y [N, M] bf16."""
+    N, K = x.shape
+    M = w.shape[0]
+    _check("x", x, torch.bfloat16, (N, K))
+    _check("w", w, torch.bfloat16, (M, K))
+    _check("y", y, torch.bfloat16, (N, M))
+    if residual is not None:
+        _check("residual", residual, torch.bfloat16, (N, M))
+    _ok("mla_linear", lib().mla_linear(_ptr(x), _ptr(w), _ptr(residual), _ptr(y), N, K, M, _stream(stream)))
 
 
 def default_scale() -> float:

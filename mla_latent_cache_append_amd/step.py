@@ -1,7 +1,10 @@
 """One absorbed-MLA decode step over a paged latent cache, as four library calls.
 
 append (new tokens' [c_kv | RoPE(k_pe)] rows) -> absorb_q -> decode_attn -> out_up,
-all on the current stream, into buffers allocated once here.
+all on the current stream, into buffers allocated once here. ``LayerStep``
+wraps a step in the layer's projections (bias-free linear maps, [MLA80] §2 of
+the CSDN page "80 行 PyTorch 从零写 DeepSeek 的 MLA") and a residual output
+projection, for stacks of layers.
 """
 
 from __future__ import annotations
@@ -61,3 +64,45 @@ class DecodeStep:
         with torch.cuda.graph(g):
             self(c_kv, k_pe, q_nope, q_pe, q_pos, slots)
         return g
+
+
+class LayerStep:
+    """One attention layer for the new tokens of B sequences, around a
+    ``DecodeStep`` (which owns the layer's cache, W_UK and W_UV):
+
+        c_kv = Wdkv h, k_pe = Wkr h, qz = Wdq h, q_nope = Wuq qz, q_pe = Wqr qz
+        o = decode(c_kv, k_pe, q_nope, q_pe)
+        h_out = h + Wo [o_0 | ... | o_{H-1}]
+
+    Weights are [out, in] bf16 device tensors; every product runs in
+    ``mla_linear`` (the residual add is fused into the last one)."""
+
+    def __init__(self, decode: DecodeStep, w_dq, w_uq, w_qr, w_dkv, w_kr, w_o, device="cuda"):
+        self.decode = decode
+        self.w_dq, self.w_uq, self.w_qr, self.w_dkv, self.w_kr, self.w_o = w_dq, w_uq, w_qr, w_dkv, w_kr, w_o
+        N, H = decode.N, decode.H
+        d_model, d_cq = w_dq.shape[1], w_dq.shape[0]
+        if tuple(w_uq.shape) != (H * nat.D_NOPE, d_cq) or tuple(w_qr.shape) != (H * nat.D_ROPE, d_cq):
+            raise ValueError("query up-projections do not match the heads or the query latent width")
+        if tuple(w_dkv.shape) != (nat.D_C, d_model) or tuple(w_kr.shape) != (nat.D_ROPE, d_model):
+            raise ValueError("KV down-projections do not match the latent widths or d_model")
+        if tuple(w_o.shape) != (d_model, H * nat.D_V):
+            raise ValueError("output projection does not match the heads or d_model")
+        bf = dict(dtype=torch.bfloat16, device=device)
+        self.qz = torch.empty(N, d_cq, **bf)
+        self.q_nope = torch.empty(N, H, nat.D_NOPE, **bf)
+        self.q_pe = torch.empty(N, H, nat.D_ROPE, **bf)
+        self.c_kv = torch.empty(N, nat.D_C, **bf)
+        self.k_pe = torch.empty(N, nat.D_ROPE, **bf)
+        self.out = torch.empty(N, d_model, **bf)
+
+    def __call__(self, h, q_pos, slots):
+        N = self.decode.N
+        nat.mla_linear(h, self.w_dkv, self.c_kv)
+        nat.mla_linear(h, self.w_kr, self.k_pe)
+        nat.mla_linear(h, self.w_dq, self.qz)
+        nat.mla_linear(self.qz, self.w_uq, self.q_nope.view(N, -1))
+        nat.mla_linear(self.qz, self.w_qr, self.q_pe.view(N, -1))
+        self.decode(self.c_kv, self.k_pe, self.q_nope, self.q_pe, q_pos, slots)
+        nat.mla_linear(self.decode.o.view(N, -1), self.w_o, self.out, residual=h)
+        return self.out

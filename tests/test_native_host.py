@@ -30,7 +30,7 @@ def nat():
 
 def test_header_declares_the_four_calls():
     names = declared_functions()
-    for n in ("mla_cache_append", "mla_absorb_q", "mla_decode_attn", "mla_out_up",
+    for n in ("mla_cache_append", "mla_absorb_q", "mla_decode_attn", "mla_out_up", "mla_linear",
               "mla_decode_workspace_size", "mla_status_str", "mla_dims_default"):
         assert n in names
 

@@ -19,6 +19,7 @@ import dataclasses
 import numpy as np
 
 TAG_CKV, TAG_KPE, TAG_QNOPE, TAG_QPE, TAG_WUK, TAG_WUV, TAG_LENS, TAG_TABLE = range(1, 9)
+TAG_LAYER, TAG_HIDDEN = 9, 10
 
 BLOCK = 64
 D_C, D_ROPE, D_NOPE, D_V = 512, 64, 128, 128
@@ -157,6 +158,22 @@ FULL_WORKLOADS = (
     "ragged_b128_h128_l1to32768",
     "causal8_b16_h128_l65544",
 )
+
+def layer_weights(seed: int, layer: int, H: int, d_model: int, d_cq: int) -> dict:
+    """bf16 bits of one layer's projection weights in nn.Linear layout
+    ([out, in]), each N(0, 1/in): Wdq [d_cq, d_model], Wuq [H*128, d_cq],
+    Wqr [H*64, d_cq], Wdkv [512, d_model], Wkr [64, d_model],
+    Wo [d_model, H*128]. (W_UK and W_UV come from the layer's Workload.)"""
+    shapes = dict(w_dq=(d_cq, d_model), w_uq=(H * D_NOPE, d_cq), w_qr=(H * D_ROPE, d_cq),
+                  w_dkv=(D_C, d_model), w_kr=(D_ROPE, d_model), w_o=(d_model, H * D_V))
+    return {k: normal_bf16((seed, TAG_LAYER, layer, i), shp, 1.0 / np.sqrt(shp[1]))
+            for i, (k, shp) in enumerate(shapes.items())}
+
+
+def hidden_states(seed: int, N: int, d_model: int) -> np.ndarray:
+    """bf16 bits of the new tokens' hidden states entering the first layer, N(0, 1)."""
+    return normal_bf16((seed, TAG_HIDDEN), (N, d_model))
+
 
 # chunked prefill over the latent: many query tokens per sequence
 PREFILL_WORKLOADS = ("chunk512_b4_h128_l16896",)
