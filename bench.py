@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layer", action="store_true",
+                    help="also time the whole layer: the projections around the step (synthetic weights) "
+                         "and the residual output projection, eager per call and as one HIP graph")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device read (a sum) and a 1 GiB device write (a fill), "
                          "the calibration of the traffic counters")
@@ -126,6 +129,82 @@ def achievable_peaks(torch, dev) -> dict:
             "hbm_read_probe": "stream read of 2 GiB, 16-byte loads, median of 10",
             "mfma_bf16_TFLOPs": waves4 * 4 * 4 * iters * 32768 / t_mfma / 1e12,
             "mfma_probe": "back-to-back v_mfma_f32_32x32x16_bf16, 4 chains per wave, 16 waves per CU, median of 5"}
+
+
+def _capture_graph(torch, fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def layer_timing(torch, nat, workloads, w, step, args, to_dev, qpos, slots) -> dict:
+    """The step wrapped in its layer: c_kv = Wdkv h, k_pe = Wkr h, qz = Wdq h,
+    q_nope = Wuq qz, q_pe = Wqr qz, the decode step, h_out = h + Wo o. Model
+    widths: d_model 2048 at 16 heads (V2-Lite), 7168 at 128 heads (V3); query
+    latent 1536. Weights N(0, 1/in), hidden states N(0, 1). Per call: HIP
+    events around replays of a graph of 20 calls; the whole layer as HIP-graph
+    replays."""
+    from mla_latent_cache_append_amd.step import LayerStep
+    d_model = 2048 if w.H <= 16 else 7168
+    d_cq = 1536
+    lw = {k: to_dev(v) for k, v in workloads.layer_weights(args.seed, 0, w.H, d_model, d_cq).items()}
+    ls = LayerStep(step, **lw)
+    h = to_dev(workloads.hidden_states(args.seed, w.N, d_model))
+    N = w.N
+    calls = {
+        "w_dkv": lambda: nat.mla_linear(h, ls.w_dkv, ls.c_kv),
+        "w_kr": lambda: nat.mla_linear(h, ls.w_kr, ls.k_pe),
+        "w_dq": lambda: nat.mla_linear(h, ls.w_dq, ls.qz),
+        "w_uq": lambda: nat.mla_linear(ls.qz, ls.w_uq, ls.q_nope.view(N, -1)),
+        "w_qr": lambda: nat.mla_linear(ls.qz, ls.w_qr, ls.q_pe.view(N, -1)),
+        "w_o": lambda: nat.mla_linear(step.o.view(N, -1), ls.w_o, ls.out, residual=h),
+    }
+    ls(h, qpos, slots)
+    torch.cuda.synchronize()
+    # per call: a HIP graph of 20 back-to-back calls, replayed, so that the
+    # host's per-call overhead does not enter the GPU time
+    per = {}
+    for name, fn in calls.items():
+        def twenty(fn=fn):
+            for _ in range(20):
+                fn()
+        gc = _capture_graph(torch, twenty)
+        for _ in range(2):
+            gc.replay()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gc.replay()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / 20)
+        per[name] = float(np.median(ts))
+    g = ls.capture(h, qpos, slots)
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(args.steps // 4, 10)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    layer_us = e0.elapsed_time(e1) * 1e3 / reps
+    wbytes = {k: int(v.numel()) * 2 for k, v in lw.items()}
+    io = lambda k: N * (lw[k].shape[0] + lw[k].shape[1]) * 2      # activations in and out
+    gbps = {k: (wbytes[k] + io(k)) / (per[k] * 1e-6) / 1e9 for k in calls}
+    return {"d_model": d_model, "d_cq": d_cq, "call_us_median": per,
+            "weight_bytes": wbytes, "GBps": gbps,
+            "w_o_frac_of_8TBps": gbps["w_o"] / HBM_PEAK_GBPS,
+            "layer_us_graph": layer_us, "layer_tokens_per_s": N / (layer_us * 1e-6)}
 
 
 def algorithmic(w):
@@ -312,6 +391,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = max(wall * 1e3, g0.elapsed_time(g1)) / args.steps
 
+    layer = layer_timing(torch, nat, workloads, w, step, args, to_dev, qpos, slot_n) if args.layer else None
     ach = achievable_peaks(torch, dev)
     alg = algorithmic(w)
     attn_s = med["decode_attn"] * 1e-6
@@ -373,6 +453,8 @@ def main():
         "fill": {"tokens": int(w.lens.sum()) - w.N, "append_kernel_s": fill_events * 1e-3,
                  "wall_s_incl_host_generation": t_fill},
     }
+    if layer is not None:
+        out["layer"] = layer
     if args.copy_calib:
         buf = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         for _ in range(3):

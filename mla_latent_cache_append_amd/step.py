@@ -55,15 +55,20 @@ class DecodeStep:
         """Record one whole step (five kernels, no allocation, no memset) as a
         HIP graph over these input tensors; returns the graph, whose replay()
         reruns the step on whatever the tensors then hold."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):       # one eager run initialises the stream state
-            self(c_kv, k_pe, q_nope, q_pe, q_pos, slots)
-        torch.cuda.current_stream().wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            self(c_kv, k_pe, q_nope, q_pe, q_pos, slots)
-        return g
+        return _capture(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots)
+
+
+def _capture(fn, *args):
+    """HIP graph of one call fn(*args), after one eager call on a side stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # one eager run initialises the stream state
+        fn(*args)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(*args)
+    return g
 
 
 class LayerStep:
@@ -106,3 +111,8 @@ class LayerStep:
         self.decode(self.c_kv, self.k_pe, self.q_nope, self.q_pe, q_pos, slots)
         nat.mla_linear(self.decode.o.view(N, -1), self.w_o, self.out, residual=h)
         return self.out
+
+    def capture(self, h, q_pos, slots):
+        """Record the whole layer (twelve kernels) as a HIP graph over these
+        input tensors; replay() reruns it on whatever they then hold."""
+        return _capture(self, h, q_pos, slots)

@@ -108,3 +108,30 @@ def test_layer_stack_error_growth():
         print(f"  layer {l}: h max_rel {mh['max_rel']:.2e} mean_rel {mh['mean_rel']:.2e} | "
               f"y max_rel {my['max_rel']:.2e} mean_rel {my['mean_rel']:.2e}", flush=True)
         prev_r = ref_h[l]
+
+
+def test_layer_graph_replays_match_eager():
+    """The whole layer (projections, decode step, residual output projection)
+    recorded as one HIP graph replays bit for bit to the eager layer, with
+    eager work that overwrites the outputs between replays."""
+    from mla_latent_cache_append_amd.step import LayerStep
+    H, d_model, d_cq = 16, 2048, 1536
+    w = workloads.Workload("layer_graph", 3, H, 1, [70, 600, 1500], "permuted", seed=300)
+    run = hz.GpuRun(w)
+    lw = workloads.layer_weights(300, 0, H, d_model, d_cq)
+    st = LayerStep(run.step, **{k: hz.to_dev(v) for k, v in lw.items()})
+    h = hz.to_dev(workloads.hidden_states(300, w.B, d_model))
+    _, _, qpos, slot = run.new
+    print("\n[case] layer graph: H=16, lens [70, 600, 1500]", flush=True)
+    eager = st(h, qpos, slot).clone()
+    torch.cuda.synchronize()
+    g = st.capture(h, qpos, slot)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.out.fill_(float("nan"))
+        st.decode.o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out.view(torch.int16), eager.view(torch.int16)), rep
+        print(f"  replay {rep}: bitwise equal to the eager layer", flush=True)
