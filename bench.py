@@ -68,6 +68,7 @@ def traffic_from(fetch_dir: str, write_dir: str, workload: str) -> dict:
     def per_kernel(d, counter):
         f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
         acc = {}
+        last_attn = -1
         for row in csv.DictReader(open(f)):
             if row["Counter_Name"] != counter:
                 continue
@@ -75,13 +76,22 @@ def traffic_from(fetch_dir: str, write_dir: str, workload: str) -> dict:
             key = ("split" if any(k in name for k in ("attn_own", "attn_rows", "attn_cols")) else
                    "combine" if "attn_combine" in name else
                    "read" if "reduce_kernel" in name else
-                   "write" if "FillFunctor" in name else None)
+                   "write" if "FillFunctor" in name else
+                   "copy" if "copyBuffer" in name else None)
             if key:
-                acc.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)
-        # calibration kernels: the largest dispatch (a reduction may add a small second pass)
-        return {k: (max(v) if k in ("read", "write") else sum(v) / len(v)) for k, v in acc.items()}
+                did = int(row["Dispatch_Id"])
+                if key in ("split", "combine"):
+                    last_attn = max(last_attn, did)
+                acc.setdefault(key, []).append((did, float(row["Counter_Value"]) * 1024.0))
+        # calibration kernels run after the last attention call (earlier fills, such as
+        # the probe buffer's, have other sizes); the largest of those dispatches, since
+        # a reduction may add a small second pass
+        return {k: (max(x for d, x in v if d > last_attn) if k in ("read", "write", "copy")
+                    else sum(x for _, x in v) / len(v)) for k, v in acc.items()}
     fe, wr = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    f_scale, w_scale = COPY_BYTES / fe["read"], COPY_BYTES / wr["write"]
+    # scale from a plain device-to-device copy of COPY_BYTES (reads and writes them);
+    # the sum and the fill are kept in raw_kib as a cross-check
+    f_scale, w_scale = COPY_BYTES / fe["copy"], COPY_BYTES / wr["copy"]
     fetch = (fe["split"] + fe.get("combine", 0.0)) * f_scale
     write = (wr["split"] + wr.get("combine", 0.0)) * w_scale
     return {"workload": workload, "kernel_source_hash": kernel_hash(),
@@ -457,9 +467,11 @@ def main():
         out["layer"] = layer
     if args.copy_calib:
         buf = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(buf)
         for _ in range(3):
             buf.sum()            # reads COPY_BYTES
             buf.fill_(1.0)       # writes COPY_BYTES
+            dst.copy_(buf)       # reads and writes COPY_BYTES (device-to-device copy kernel)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
