@@ -200,6 +200,98 @@ def absorbed_decode(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, scale=None, base=ROPE_
 
 
 # --------------------------------------------------------------------------
+# FP8 latent cache ([AUDIT] §6.1: FlashMLA's support matrix lists an FP8 KV
+# cache for its MQA-mode kernels; the pages name the format but not its
+# scaling). Reading taken here: the 576-element row of each token is stored
+# as OCP FP8 E4M3 codes ("e4m3fn": 4 exponent bits with bias 7, 3 mantissa
+# bits, no infinities, 0x7f / 0xff are NaN, largest finite 448) with one fp32
+# scale per token, scale = max|row| / 448. The codes are integers, so the
+# quantizer takes its decisions in float32, the precision of the kernel that
+# writes them; everything after decoding is fp64 again.
+
+FP8_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Exact value of E4M3 (e4m3fn) codes as float64: sign bit 7, exponent
+    bits 6..3 (bias 7), mantissa bits 2..0. Exponent field 0 is subnormal,
+    m/8 * 2^-6; otherwise (1 + m/8) * 2^(e-7); 0x7f and 0xff are NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(u) -> np.ndarray:
+    """float32 values -> E4M3 codes, rounding to the nearest representable
+    value (ties to the even mantissa) and saturating at +-448.
+
+    The grid spacing is 2^(E-3) in the binade [2^E, 2^(E+1)) for E >= -6
+    and 2^-9 below 2^-6 (subnormals); dividing by that power of two is exact,
+    np.rint rounds half to even, and a result that reaches the next binade is
+    that binade's first value."""
+    u = np.asarray(u, dtype=np.float32).astype(np.float64)
+    a = np.abs(u)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))      # a = f * 2^ex, f in [0.5, 1)
+    E = np.maximum(ex - 1, -6)                      # binade exponent, subnormals share -6
+    quantum = np.ldexp(1.0, E - 3)
+    v = np.minimum(np.rint(a / quantum) * quantum, FP8_MAX)
+    # code of the (now representable) magnitude v
+    _, vex = np.frexp(np.where(v > 0, v, 1.0))
+    ve = vex - 1
+    normal = v >= 2.0 ** -6
+    e_field = np.where(normal, ve + 7, 0)
+    m_field = np.where(normal, np.rint((v / np.ldexp(1.0, ve) - 1.0) * 8.0), np.rint(v / 2.0 ** -9))
+    code = (e_field.astype(np.int64) << 3) | m_field.astype(np.int64)
+    code = np.where(np.signbit(u), code | 0x80, code)
+    code = np.where(np.isnan(u), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_rows_fp8(rows) -> tuple[np.ndarray, np.ndarray]:
+    """Per-token scaled FP8 of float32 rows [..., 576]: scale = max|row| / 448
+    (float32 division; 1 for an all-zero row), codes = E4M3(row / scale) with
+    the division in float32. Returns (codes uint8 [..., 576], scale float32 [...])."""
+    r = np.asarray(rows, dtype=np.float32)
+    amax = np.max(np.abs(r), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    codes = e4m3_encode((r / scale[..., None]).astype(np.float32))
+    return codes, scale
+
+
+def dequantize_rows_fp8(codes, scale) -> np.ndarray:
+    """Row value the FP8 cache stands for: code value times its token's scale (fp64, exact)."""
+    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def cache_rows_fp8(c_kv, k_pe, pos, base: float = ROPE_BASE) -> tuple[np.ndarray, np.ndarray]:
+    """FP8 cache row of each appended token: the same [c_kv | RoPE(k_pe, pos)]
+    as ``cache_rows`` (rotation in fp64), rounded once to float32 (the
+    quantizer's input precision; the bf16 latent is exact in float32), then
+    quantized per token. Returns (codes [T, 576] uint8, scale [T] float32)."""
+    rows = cache_rows(c_kv, k_pe, pos, base).astype(np.float32)
+    return quantize_rows_fp8(rows)
+
+
+def absorbed_decode_fp8(q_nope, q_pe, codes, scale, w_uk, w_uv, softmax_scale=None,
+                        base=ROPE_BASE) -> dict:
+    """Absorbed MLA decode of one sequence over its FP8 cache rows (keys
+    0..L-1, rows already rotated): the rows are decoded exactly and attended
+    to in fp64 as in ``absorbed_decode``. Returns dict(q_lat, q_r, o_lat, lse, o)."""
+    if softmax_scale is None:
+        softmax_scale = default_scale()
+    rows = dequantize_rows_fp8(codes, scale)
+    L, Lq = rows.shape[0], np.asarray(q_nope).shape[0]
+    q_pos = query_positions(L, Lq)
+    q_lat, q_r = absorb_q(q_nope, q_pe, q_pos, w_uk, base)
+    o_lat, lse = latent_attention(q_lat, q_r, rows[:, :D_C], rows[:, D_C:], q_pos, softmax_scale)
+    return dict(q_lat=q_lat, q_r=q_r, o_lat=o_lat, lse=lse, o=out_up(o_lat, w_uv))
+
+
+# --------------------------------------------------------------------------
 # naive (expanding) path ([AUDIT] §2.1; [MLA80] §2 MLA.forward)
 
 
