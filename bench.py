@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="v3_b32_h128_l16384")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cache", choices=("bf16", "fp8"), default="bf16",
+                    help="latent cache format: bf16 rows, or E4M3 codes with one fp32 scale per token")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -217,11 +219,12 @@ def layer_timing(torch, nat, workloads, w, step, args, to_dev, qpos, slots) -> d
             "layer_us_graph": layer_us, "layer_tokens_per_s": N / (layer_us * 1e-6)}
 
 
-def algorithmic(w):
-    """Algorithmic bytes and flops of one attention call (and of one step)."""
+def algorithmic(w, fp8: bool = False):
+    """Algorithmic bytes and flops of one attention call (and of one step).
+    A cache row is 1,152 bytes in bf16, 576 code bytes + a 4-byte scale in FP8."""
     L = w.lens.astype(np.int64)
     rows = w.Lq * w.H
-    cache = int(L.sum()) * ROW_BYTES
+    cache = int(L.sum()) * (576 + 4 if fp8 else ROW_BYTES)
     q_bytes = w.N * w.H * 576 * 2
     olat_bytes = w.N * w.H * 512 * 2 + w.N * w.H * 4
     attn_bytes = cache + q_bytes + olat_bytes
@@ -293,10 +296,12 @@ def main():
 
     # ---- setup (untimed): weights, paged pool filled through mla_cache_append
     wuk, wuv = w.weights()
-    pool = torch.empty((w.num_blocks, 64, 576), dtype=torch.bfloat16, device=dev)
+    fp8 = args.cache == "fp8"
+    pool = torch.empty((w.num_blocks, 64, 576), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    pool_scale = torch.empty((w.num_blocks, 64), dtype=torch.float32, device=dev) if fp8 else None
     block_table = torch.from_numpy(w.block_table).to(dev)
     seq_lens = torch.from_numpy(w.lens.astype(np.int32)).to(dev)
-    step = DecodeStep(w.H, w.B, w.Lq, pool, block_table, seq_lens, to_dev(wuk), to_dev(wuv))
+    step = DecodeStep(w.H, w.B, w.Lq, pool, block_table, seq_lens, to_dev(wuk), to_dev(wuv), pool_scale=pool_scale)
     new_ckv = np.zeros((w.N, 512), np.uint16)
     new_kpe = np.zeros((w.N, 64), np.uint16)
     new_slot = np.zeros(w.N, np.int64)
@@ -343,8 +348,7 @@ def main():
         nat.mla_absorb_q(step.dims, qn, qp, qpos, step.w_uk, step.q)
         if ev is not None:
             ev[2].record()
-        nat.mla_decode_attn(step.dims, step.q, step.pool, step.block_table, step.seq_lens, step.Lq,
-                            step.o_lat, step.lse, step.workspace)
+        step.decode_attn()
         if ev is not None:
             ev[3].record()
         nat.mla_out_up(step.dims, step.o_lat, step.w_uv, step.o)
@@ -403,7 +407,7 @@ def main():
 
     layer = layer_timing(torch, nat, workloads, w, step, args, to_dev, qpos, slot_n) if args.layer else None
     ach = achievable_peaks(torch, dev)
-    alg = algorithmic(w)
+    alg = algorithmic(w, fp8)
     attn_s = med["decode_attn"] * 1e-6
     achieved_gbps = alg["attn_bytes"] / attn_s / 1e9
     tflops = alg["attn_flops"] / attn_s / 1e12
@@ -412,7 +416,8 @@ def main():
     if os.path.exists(tf):
         try:
             t = json.load(open(tf))
-            if t.get("workload") == w.name and t.get("kernel_source_hash") == kernel_hash():
+            if (t.get("workload") == w.name and t.get("kernel_source_hash") == kernel_hash()
+                    and t.get("cache", "bf16") == args.cache):
                 traffic = t.get("bytes_per_launch")
         except Exception:
             traffic = None
@@ -441,9 +446,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq,
                    "keys_per_seq": int(w.lens.max()) if w.lens.min() == w.lens.max() else "ragged",
-                   "total_keys": int(w.lens.sum()), "block_table": w.table_kind, "seed": args.seed},
+                   "total_keys": int(w.lens.sum()), "block_table": w.table_kind, "seed": args.seed,
+                   "cache": "fp8-e4m3 (per-token fp32 scale)" if fp8 else "bf16"},
         "roofline": dict(roof, traffic=traffic,
-                         kernel="mla_decode_attn call (split kernel + combine kernel)",
+                         kernel=("mla_decode_attn_fp8" if fp8 else "mla_decode_attn")
+                         + " call (split kernel + combine kernel)",
                          algorithmic_bytes_per_launch=alg["attn_bytes"],
                          algorithmic_flops_per_launch=alg["attn_flops"],
                          avg_launch_us=med["decode_attn"]),

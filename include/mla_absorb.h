@@ -149,6 +149,47 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * FP8 latent cache ([AUDIT] §6.1: FlashMLA's support matrix pairs its
+ * MQA-mode kernels with an FP8 KV cache; the pages name the format only).
+ * Reading used here: the same 576-element row per token, stored as OCP FP8
+ * E4M3 codes ("e4m3fn": exponent bias 7, 3 mantissa bits, largest finite 448,
+ * 0x7f / 0xff NaN) of row / scale, with one fp32 scale per token,
+ * scale = max|row| / 448 (1 for an all-zero row). Half the bytes of the bf16
+ * pool per token (576 + 4 against 1,152).
+ *   pool8       device [num_blocks][64][576] uint8  E4M3 codes
+ *   pool_scale  device [num_blocks][64]      fp32   scale of each slot's row
+ */
+
+/*
+ * mla_cache_append_fp8 — mla_cache_append into the FP8 pool. The row
+ * [c_kv | RoPE(k_pe, pos)] is formed in fp32 (the latent exactly, the rope
+ * part with an fp64 angle and rotation, rounded once), its absmax taken, and
+ * every element encoded as E4M3 of (element / scale) with IEEE fp32 division,
+ * nearest value with ties to even. Arguments as mla_cache_append; a slot
+ * outside [0, num_blocks*64) is skipped (neither codes nor scale written).
+ * Non-finite inputs give unspecified codes.
+ */
+int mla_cache_append_fp8(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                         const int32_t* pos, const int64_t* slot_mapping, uint8_t* pool8,
+                         float* pool_scale, int64_t num_blocks, int32_t T, void* stream);
+
+/*
+ * mla_decode_attn_fp8 — mla_decode_attn over the FP8 pool: C_t is the row the
+ * codes stand for, code value x pool_scale of its slot. Scores are formed
+ * from the exact code values in bf16 MFMAs and multiplied by the token scale
+ * in fp32; probabilities are multiplied by the token scale before their bf16
+ * rounding for the weighted sum (the row sum takes them unscaled). Every
+ * other argument, the workspace (the same mla_decode_workspace_size), the
+ * error codes, the device-value handling and determinism are as for
+ * mla_decode_attn.
+ */
+int mla_decode_attn_fp8(const mla_dims* dims, const uint16_t* q, const uint8_t* pool8,
+                        const float* pool_scale, int64_t num_blocks, const int32_t* block_table,
+                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B, int32_t Lq,
+                        uint16_t* o_lat, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * mla_out_up — expand the latent context through W_UV per head.
  * o[n][h] = W_UV[h] o_lat[n][h]   ([AUDIT] §2.3: sum_t p_t (W_V c_t) = W_V (sum_t p_t c_t))
  *   o_lat  device [N][H][512] bf16

@@ -126,7 +126,8 @@ __device__ __forceinline__ int plan_owner(int64_t x, int64_t T, int width) {
 
 struct AttnArgs {
   const uint16_t* q;            // [B*rows][576]   (row (b, r) = b*rows + r)
-  const uint16_t* pool;         // [num_blocks][64][576]
+  const uint16_t* pool;         // [num_blocks][64][576] bf16 (FP8 pool: [num_blocks][64][576] E4M3 codes)
+  const float* pool_scale;      // FP8 pool only: [num_blocks][64] fp32 scale of each token's row
   const int32_t* block_table;   // [B][max_blocks]
   const int32_t* seq_lens;      // [B]
   uint16_t* o_lat;              // [B*rows][512]
@@ -188,10 +189,15 @@ constexpr float RESCALE_LOG2 = 8.f;
 // 16 (NK = 2 k-blocks x 8) values per lane in PV k-slot order. Returns the
 // packed bf16 probabilities. NCB accumulators per row block are rescaled only
 // when some lane's max moved by more than RESCALE_LOG2.
-template <int RB, int NCB>
+//
+// PMUL (FP8 cache): the probability of key j is multiplied by pmul[kb][j],
+// its token's dequantization scale, before the bf16 rounding that feeds PV;
+// the row sum takes the unscaled probability.
+template <int RB, int NCB, bool PMUL = false>
 __device__ __forceinline__ void softmax_update(float (&pv)[RB][2][8], float (&m_run)[RB],
                                                float (&l_run)[RB], f32x4 (&o)[RB][NCB],
-                                               bf16x8 (&pf)[RB][2]) {
+                                               bf16x8 (&pf)[RB][2],
+                                               const float (*pmul)[8] = nullptr) {
   float mx[RB];
   bool need = false;
 #pragma unroll
@@ -229,7 +235,8 @@ __device__ __forceinline__ void softmax_update(float (&pv)[RB][2][8], float (&m_
       for (int j = 0; j < 8; ++j) {
         const float p = __builtin_amdgcn_exp2f(pv[rb][kb][j] - m_ref);
         psum += p;
-        pk[j] = (__bf16)p;
+        if constexpr (PMUL) pk[j] = (__bf16)(p * pmul[kb][j]);
+        else pk[j] = (__bf16)p;
       }
       pf[rb][kb] = pk;
     }
@@ -284,8 +291,13 @@ __device__ __forceinline__ void scale_mask(f32x4 (&s)[RB][NTB], float scale_log2
 
 // Column split, one tile: wave w scores tokens 16w..16w+15 for all RB*16 rows,
 // shares the scores through LDS, and accumulates columns 128w..128w+127.
-template <int RB, bool MASK>
+//
+// FP8: the tile holds the E4M3 codes converted exactly to bf16 and tsc (LDS)
+// the 64 token scales; score t is multiplied by tsc[t] before the softmax
+// scale and probability t by tsc[t] before PV.
+template <int RB, bool MASK, bool FP8 = false>
 __device__ __forceinline__ void cols_tile(lds_char* cur, __attribute__((address_space(3))) float* sbuf,
+                                          const __attribute__((address_space(3))) float* tsc,
                                           const bf16x8 (&qf)[RB][KSTEPS], f32x4 (&o)[RB][8],
                                           float (&m_run)[RB], float (&l_run)[RB],
                                           const int (&lim)[RB], int key0, float scale_log2,
@@ -304,11 +316,17 @@ __device__ __forceinline__ void cols_tile(lds_char* cur, __attribute__((address_
     for (int rb = 0; rb < RB; ++rb) s[rb][0] = mfma16x16x32(as_bf16x8(kc), qf[rb][ks], s[rb][0]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (FP8) {
+    const f32x4 ts = *(const __attribute__((address_space(3))) f32x4*)(tsc + 16 * wave + 4 * g);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s[rb][0] *= ts;
+  }
   scale_mask<RB, 1, MASK>(s, scale_log2, key0, wave, g, lim);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
     *(__attribute__((address_space(3))) f32x4*)(sbuf + (rb * 16 + c16) * SB + 16 * wave + 4 * g) = s[rb][0];
-  __syncthreads();
+  if constexpr (FP8) lds_barrier();  // tile copies in flight in registers stay in flight
+  else __syncthreads();
   float pv[RB][2][8];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -322,24 +340,108 @@ __device__ __forceinline__ void cols_tile(lds_char* cur, __attribute__((address_
         for (int i = 0; i < 4; ++i) pv[rb][kb][4 * h2 + i] = v[i];
       }
   bf16x8 pf[RB][2];
-  softmax_update<RB, 8>(pv, m_run, l_run, o, pf);
+  if constexpr (FP8) {
+    // scales of the keys in PV k-slot order: token 32 kb + 16 h2 + 4 g + i
+    float pm[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(tsc + 32 * kb + 16 * h2 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pm[kb][4 * h2 + i] = v[i];
+      }
+    softmax_update<RB, 8, true>(pv, m_run, l_run, o, pf, pm);
+  } else {
+    softmax_update<RB, 8>(pv, m_run, l_run, o, pf);
+  }
   pv_product<RB, 8>(cur, vbase, 8 * wave, pf, o);
+}
+
+// ------------------------------------------------------------- FP8 tiles
+//
+// FP8 pool: [num_blocks][64][576] E4M3 codes (one byte per element, a block
+// is 36,864 contiguous bytes) and [num_blocks][64] fp32 token scales. A tile
+// is copied into registers (nine 16-byte loads per thread, consecutive threads
+// on consecutive 16 bytes), converted to bf16 exactly (every E4M3 value is a
+// bf16 value) by v_cvt_scalef32_pk_bf16_fp8 with scale 1, and written to an
+// LDS tile in the same swizzled bf16 layout the bf16 kernels read. The token
+// scales are applied in fp32 to the scores and probabilities instead.
+constexpr int TILE_BYTES8 = BLOCK * D_K;               // 36,864
+constexpr int FP8_LOADS = TILE_BYTES8 / 16 / 256;      // 9 per thread
+constexpr int ROW_CHUNKS8 = D_K / 16;                  // 36 sixteen-byte chunks per row
+
+struct Fp8Stage {
+  u32x4 v[FP8_LOADS];
+  f32x4 sc;
+  int n_valid;
+};
+
+// Codes and scales of tile `blk`. The whole block lies inside the pool, so
+// every load is in bounds; tokens at or past n_valid (never written, any
+// bits) become zero codes and zero scales only when the tile is stored, so
+// that nothing waits for the loads before then.
+__device__ __forceinline__ void fp8_tile_load(const uint8_t* pool8, const float* scales, int blk,
+                                              int n_valid, int tid, Fp8Stage& st) {
+  const uint8_t* base = pool8 + (int64_t)blk * TILE_BYTES8;
+#pragma unroll
+  for (int i = 0; i < FP8_LOADS; ++i) st.v[i] = *(const u32x4*)(base + 16 * (tid + 256 * i));
+  st.sc = *(const f32x4*)(scales + (int64_t)blk * BLOCK + 4 * (tid & (BLOCK / 4 - 1)));
+  st.n_valid = n_valid;
+}
+
+// Four E4M3 codes (bytes 0..3 of w) -> four bf16, exact.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);  // bytes 0, 1
+  const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);   // bytes 2, 3
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+// Converted tile into the LDS tile at dst (bf16 chunks 2c and 2c+1 of token t
+// for the 16 codes of fp8 chunk c) and its scales into sdst[64].
+__device__ __forceinline__ void fp8_tile_store(const Fp8Stage& st, lds_char* dst,
+                                               __attribute__((address_space(3))) float* sdst, int tid) {
+#pragma unroll
+  for (int i = 0; i < FP8_LOADS; ++i) {
+    const int j = tid + 256 * i;
+    const int t = j / ROW_CHUNKS8, c = j - ROW_CHUNKS8 * t;
+    const u32x4 v = t < st.n_valid ? st.v[i] : u32x4{0u, 0u, 0u, 0u};
+    const u32x2 a = fp8x4_to_bf16x4(v[0]), b = fp8x4_to_bf16x4(v[1]);
+    const u32x2 e = fp8x4_to_bf16x4(v[2]), f = fp8x4_to_bf16x4(v[3]);
+    *(__attribute__((address_space(3))) u32x4*)(dst + lds_chunk_off(t, 2 * c)) = u32x4{a[0], a[1], b[0], b[1]};
+    *(__attribute__((address_space(3))) u32x4*)(dst + lds_chunk_off(t, 2 * c + 1)) = u32x4{e[0], e[1], f[0], f[1]};
+  }
+  if (tid < BLOCK / 4) {
+    f32x4 sc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sc[e] = 4 * tid + e < st.n_valid ? st.sc[e] : 0.f;
+    *(__attribute__((address_space(3))) f32x4*)(sdst + 4 * tid) = sc;
+  }
 }
 
 // Few rows per sequence (16 or 32, e.g. 16 heads): the 4 waves of a
 // workgroup share the same RB*16 rows (RB = 16-row MFMA blocks); see cols_tile.
-template <int RB>
+//
+// FP8 = true reads the FP8 pool (codes + token scales): tiles are staged
+// through registers (see fp8_tile_load), one tile in flight while the
+// previous one is computed; with more rows than one workgroup takes, several
+// row groups share each key range (n_rg > 1).
+template <int RB, bool FP8 = false>
 __global__ __launch_bounds__(256, 1) void attn_cols_kernel(AttnArgs a) {
   constexpr bool CS = true;
   constexpr int NW = 4;
   constexpr int RG = RB * 16;   // rows per workgroup
   constexpr int NCB = 8;        // 16-column blocks per wave
   constexpr int SB_BYTES = RB * 16 * 68 * 4;
+  constexpr int SC_BYTES = FP8 ? 2 * BLOCK * 4 : 0;   // token scales of the two tiles
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_BYTES + SB_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_BYTES + SB_BYTES + SC_BYTES];
   lds_char* tiles = (lds_char*)smem;
   __attribute__((address_space(3))) float* sbuf =
       (__attribute__((address_space(3))) float*)(tiles + 2 * TILE_BYTES);
+  __attribute__((address_space(3))) float* tscale =
+      (__attribute__((address_space(3))) float*)(tiles + 2 * TILE_BYTES + SB_BYTES);
+  const uint8_t* pool8 = (const uint8_t*)a.pool;
 
   const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
@@ -399,9 +501,11 @@ __global__ __launch_bounds__(256, 1) void attn_cols_kernel(AttnArgs a) {
     // scalar loads (lgkmcnt): reading a block id never waits on the tile loads
     const __attribute__((address_space(4))) int32_t* bt =
         (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)b * a.max_blocks);
+    Fp8Stage stage;
     {
       const int blk = bt[k_first];
       if (blk < 0 || blk >= a.num_blocks) bad = true;
+      else if constexpr (FP8) fp8_tile_load(pool8, a.pool_scale, blk, min(BLOCK, L - k_first * BLOCK), threadIdx.x, stage);
       else load_tile<NW>(a.pool, blk, min(BLOCK, L - k_first * BLOCK), tiles, wave, goff_lane);
     }
 
@@ -446,13 +550,36 @@ __global__ __launch_bounds__(256, 1) void attn_cols_kernel(AttnArgs a) {
       }
       return tiles + ((k - k_first) & 1) * TILE_BYTES;
     };
-    for (int k = k_first; k < k_mask; ++k) {
-      lds_char* cur = step(k);
-      cols_tile<RB, false>(cur, sbuf, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, wave, g, c16);
-    }
-    for (int k = k_mask; k < k_last; ++k) {
-      lds_char* cur = step(k);
-      cols_tile<RB, true>(cur, sbuf, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, wave, g, c16);
+    if constexpr (FP8) {
+      // tile k is in LDS at the barrier; tile k + 1 travels in registers
+      // while k is computed and is converted into the other buffer after it
+      if (!bad) fp8_tile_store(stage, tiles, tscale, threadIdx.x);
+      auto fp8_tile = [&](int k, auto mask) {
+        lds_barrier();
+        const int nb = (k + 1 - k_first) & 1;
+        bool more = k + 1 < k_last;
+        if (more) {
+          const int blk = bt[k + 1];
+          if (blk < 0 || blk >= a.num_blocks) { bad = true; more = false; }
+          else fp8_tile_load(pool8, a.pool_scale, blk, min(BLOCK, L - (k + 1) * BLOCK), threadIdx.x, stage);
+        }
+        const int cb = (k - k_first) & 1;
+        cols_tile<RB, decltype(mask)::value, true>(tiles + cb * TILE_BYTES, sbuf, tscale + cb * BLOCK, qf, o,
+                                                   m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase,
+                                                   wave, g, c16);
+        if (more) fp8_tile_store(stage, tiles + nb * TILE_BYTES, tscale + nb * BLOCK, threadIdx.x);
+      };
+      for (int k = k_first; k < k_mask; ++k) fp8_tile(k, std::false_type{});
+      for (int k = k_mask; k < k_last; ++k) fp8_tile(k, std::true_type{});
+    } else {
+      for (int k = k_first; k < k_mask; ++k) {
+        lds_char* cur = step(k);
+        cols_tile<RB, false>(cur, sbuf, nullptr, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, wave, g, c16);
+      }
+      for (int k = k_mask; k < k_last; ++k) {
+        lds_char* cur = step(k);
+        cols_tile<RB, true>(cur, sbuf, nullptr, qf, o, m_run, l_run, lim, k * BLOCK, a.scale_log2, kbase, vbase, wave, g, c16);
+      }
     }
 
     // ---- finish the segment: row sums across the 4 lanes of each row
@@ -1227,10 +1354,24 @@ AttnPlan plan_attention(int32_t B, int32_t Lq, int32_t H) {
   return p;
 }
 
+// FP8 pool: the column kernel for every shape, 16 or 32 rows per row group.
+AttnPlan plan_attention_fp8(int32_t B, int32_t Lq, int32_t H) {
+  (void)B;
+  AttnPlan p;
+  const int rows = Lq * H;
+  if (rows <= 16) { p.variant = V_COLS16; p.rg_rows = 16; }
+  else { p.variant = V_COLS32; p.rg_rows = 32; }
+  p.n_rg = (rows + p.rg_rows - 1) / p.rg_rows;
+  p.width = (TARGET_WGS + p.n_rg - 1) / p.n_rg;
+  return p;
+}
+
 // Workspace: (m, l) of every partial in fp32, then the partials themselves
-// in bf16, normalized by their l, starting on a 256-byte boundary.
+// in bf16, normalized by their l, starting on a 256-byte boundary. Sized for
+// the wider of the two plans, so one workspace serves both cache formats.
 static size_t ws_slots(int32_t B, int32_t Lq, int32_t H) {
-  return (size_t)plan_attention(B, Lq, H).width + (size_t)B;
+  const int w = max(plan_attention(B, Lq, H).width, plan_attention_fp8(B, Lq, H).width);
+  return (size_t)w + (size_t)B;
 }
 static size_t ws_ml_bytes(int32_t B, int32_t Lq, int32_t H) {
   const size_t bytes = ws_slots(B, Lq, H) * (size_t)Lq * (size_t)H * 2 * sizeof(float);
@@ -1238,19 +1379,20 @@ static size_t ws_ml_bytes(int32_t B, int32_t Lq, int32_t H) {
 }
 
 size_t attention_workspace_bytes(int32_t B, int32_t Lq, int32_t H) {
-  const AttnPlan p = plan_attention(B, Lq, H);
   return ws_ml_bytes(B, Lq, H) + ws_slots(B, Lq, H) * (size_t)Lq * (size_t)H * D_C * sizeof(uint16_t);
 }
 
-hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t num_blocks,
-                              const int32_t* block_table, int32_t max_blocks,
-                              const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
-                              float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
-                              hipStream_t stream) {
-  const AttnPlan p = plan_attention(B, Lq, H);
+static hipError_t launch_attention(const uint16_t* q, const void* pool, const float* pool_scale,
+                                   int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
+                                   float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
+                                   hipStream_t stream) {
+  const bool fp8 = pool_scale != nullptr;
+  const AttnPlan p = fp8 ? plan_attention_fp8(B, Lq, H) : plan_attention(B, Lq, H);
   AttnArgs a;
   a.q = q;
-  a.pool = pool;
+  a.pool = (const uint16_t*)pool;
+  a.pool_scale = pool_scale;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.o_lat = o_lat;
@@ -1267,7 +1409,10 @@ hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t n
   a.width = p.width;
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
   const dim3 grid(p.width * p.n_rg);
-  switch (p.variant) {
+  if (fp8) {
+    if (p.variant == V_COLS16) hipLaunchKernelGGL((attn_cols_kernel<1, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((attn_cols_kernel<2, true>), grid, dim3(256), 0, stream, a);
+  } else switch (p.variant) {
     case V_ROWS128:
       hipLaunchKernelGGL(attn_own_kernel, grid, dim3(256), 0, stream, a);
       break;
@@ -1285,6 +1430,24 @@ hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t n
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)B * (unsigned)((a.rows + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t num_blocks,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
+                              float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
+                              hipStream_t stream) {
+  return launch_attention(q, pool, nullptr, num_blocks, block_table, max_blocks, seq_lens, B, Lq, H,
+                          softmax_scale, o_lat, lse, workspace, stream);
+}
+
+hipError_t launch_decode_attn_fp8(const uint16_t* q, const uint8_t* pool8, const float* pool_scale,
+                                  int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
+                                  float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
+                                  hipStream_t stream) {
+  return launch_attention(q, pool8, pool_scale, num_blocks, block_table, max_blocks, seq_lens, B, Lq, H,
+                          softmax_scale, o_lat, lse, workspace, stream);
 }
 
 }  // namespace mla

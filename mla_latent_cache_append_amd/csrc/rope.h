@@ -94,6 +94,15 @@ __device__ __forceinline__ uint32_t rope_rotate_bf16(uint32_t x_pair, double c, 
   return (uint32_t)f64_to_bf16(y0) | ((uint32_t)f64_to_bf16(y1) << 16);
 }
 
+// Rotate the bf16 pair packed in x_pair by (c, s); one rounding to fp32 each
+// (the precision the FP8 quantizer starts from).
+__device__ __forceinline__ void rope_rotate_f32(uint32_t x_pair, double c, double s, float& y0, float& y1) {
+  const double x0 = (double)bf16_to_f32((uint16_t)(x_pair & 0xffffu));
+  const double x1 = (double)bf16_to_f32((uint16_t)(x_pair >> 16));
+  y0 = (float)(x0 * c - x1 * s);
+  y1 = (float)(x1 * c + x0 * s);
+}
+
 __device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t x_pair, int pos, double inv_freq) {
   double c, s;
   rope_cos_sin(pos, inv_freq, c, s);

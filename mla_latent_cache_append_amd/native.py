@@ -57,6 +57,9 @@ _SIG = {
     "mla_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaDims), _I32, _I32]),
     "mla_decode_attn": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _I64, _P, _I32, _P, _I32, _I32,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_cache_append_fp8": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _P, _I64, _I32, _P]),
+    "mla_decode_attn_fp8": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I64, _P, _I32, _P, _I32,
+                                           _I32, _P, _P, _P, ctypes.c_size_t, _P]),
     "mla_out_up": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I32, _P]),
     "mla_linear": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _P]),
 }
@@ -165,6 +168,50 @@ def mla_decode_attn(dims: MlaDims, q, pool, block_table, seq_lens, Lq: int, o_la
     _check("workspace", workspace, torch.uint8)
     _ok("mla_decode_attn", lib().mla_decode_attn(
         ctypes.byref(dims), _ptr(q), _ptr(pool), pool.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), B, Lq, _ptr(o_lat), _ptr(lse), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+
+
+def _check_fp8_pool(pool8, pool_scale):
+    _check("pool8", pool8, torch.uint8)
+    if pool8.dim() != 3 or tuple(pool8.shape[1:]) != (BLOCK, D_K):
+        raise ValueError("pool8 must be [num_blocks, 64, 576] uint8")
+    _check("pool_scale", pool_scale, torch.float32, (pool8.shape[0], BLOCK))
+
+
+def mla_cache_append_fp8(dims: MlaDims, c_kv, k_pe, pos, slot_mapping, pool8, pool_scale, stream=None):
+    """Write E4M3 codes of [c_kv | RoPE(k_pe, pos)] / scale into ``pool8`` and
+    each token's scale into ``pool_scale`` at ``slot_mapping``."""
+    T = c_kv.shape[0]
+    _check("c_kv", c_kv, torch.bfloat16, (T, D_C))
+    _check("k_pe", k_pe, torch.bfloat16, (T, D_ROPE))
+    _check("pos", pos, torch.int32, (T,))
+    _check("slot_mapping", slot_mapping, torch.int64, (T,))
+    _check_fp8_pool(pool8, pool_scale)
+    _ok("mla_cache_append_fp8", lib().mla_cache_append_fp8(
+        ctypes.byref(dims), _ptr(c_kv), _ptr(k_pe), _ptr(pos), _ptr(slot_mapping), _ptr(pool8),
+        _ptr(pool_scale), pool8.shape[0], T, _stream(stream)))
+
+
+def mla_decode_attn_fp8(dims: MlaDims, q, pool8, pool_scale, block_table, seq_lens, Lq: int, o_lat,
+                        lse=None, workspace=None, stream=None):
+    """Latent attention of ``q`` [B*Lq, H, 576] over the FP8 paged cache."""
+    H = dims.num_heads
+    B = seq_lens.shape[0]
+    _check("q", q, torch.bfloat16, (B * Lq, H, D_K))
+    _check_fp8_pool(pool8, pool_scale)
+    _check("block_table", block_table, torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _check("seq_lens", seq_lens, torch.int32, (B,))
+    _check("o_lat", o_lat, torch.bfloat16, (B * Lq, H, D_C))
+    if lse is not None:
+        _check("lse", lse, torch.float32, (B * Lq, H))
+    if workspace is None:
+        raise ValueError("workspace is required (mla_decode_workspace_size bytes, uint8)")
+    _check("workspace", workspace, torch.uint8)
+    _ok("mla_decode_attn_fp8", lib().mla_decode_attn_fp8(
+        ctypes.byref(dims), _ptr(q), _ptr(pool8), _ptr(pool_scale), pool8.shape[0], _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), B, Lq, _ptr(o_lat), _ptr(lse), _ptr(workspace),
         workspace.numel(), _stream(stream)))
 

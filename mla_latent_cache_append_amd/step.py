@@ -20,13 +20,16 @@ class DecodeStep:
     ``pool`` [num_blocks, 64, 576] bf16, ``block_table`` [B, max_blocks] int32 and
     ``seq_lens`` [B] int32 (keys including the new tokens) stay owned by the
     caller; the step writes the new tokens' cache rows before attending.
+    With ``pool_scale`` ([num_blocks, 64] fp32) the pool is the FP8 cache
+    ([num_blocks, 64, 576] uint8 E4M3 codes) and the step uses the FP8 calls.
     """
 
     def __init__(self, H: int, B: int, Lq: int, pool, block_table, seq_lens, w_uk, w_uv,
-                 device="cuda"):
+                 device="cuda", pool_scale=None):
         self.dims = nat.mla_dims_default(H)
         self.H, self.B, self.Lq, self.N = H, B, Lq, B * Lq
         self.pool, self.block_table, self.seq_lens = pool, block_table, seq_lens
+        self.pool_scale = pool_scale
         self.w_uk, self.w_uv = w_uk, w_uv
         N = self.N
         self.q = torch.empty(N, H, nat.D_K, dtype=torch.bfloat16, device=device)
@@ -37,12 +40,23 @@ class DecodeStep:
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
 
     def append(self, c_kv, k_pe, pos, slots):
-        nat.mla_cache_append(self.dims, c_kv, k_pe, pos, slots, self.pool)
+        if self.pool_scale is None:
+            nat.mla_cache_append(self.dims, c_kv, k_pe, pos, slots, self.pool)
+        else:
+            nat.mla_cache_append_fp8(self.dims, c_kv, k_pe, pos, slots, self.pool, self.pool_scale)
+
+    def decode_attn(self):
+        """The attention call alone, over the absorbed queries in ``self.q``."""
+        if self.pool_scale is None:
+            nat.mla_decode_attn(self.dims, self.q, self.pool, self.block_table, self.seq_lens, self.Lq,
+                                self.o_lat, self.lse, self.workspace)
+        else:
+            nat.mla_decode_attn_fp8(self.dims, self.q, self.pool, self.pool_scale, self.block_table,
+                                    self.seq_lens, self.Lq, self.o_lat, self.lse, self.workspace)
 
     def attend(self, q_nope, q_pe, q_pos):
         nat.mla_absorb_q(self.dims, q_nope, q_pe, q_pos, self.w_uk, self.q)
-        nat.mla_decode_attn(self.dims, self.q, self.pool, self.block_table, self.seq_lens, self.Lq,
-                            self.o_lat, self.lse, self.workspace)
+        self.decode_attn()
         nat.mla_out_up(self.dims, self.o_lat, self.w_uv, self.o)
 
     def __call__(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots):

@@ -90,6 +90,29 @@ def test_invalid_arguments_return_status(nat):
     assert lib.mla_cache_append(None, fake, fake, fake, fake, fake, 4, 1, null) == nat.MLA_ERR_INVALID_ARG
 
 
+def test_fp8_calls_check_arguments_on_the_host(nat):
+    lib = nat.lib()
+    d = nat.mla_dims_default(16)
+    P = ctypes.c_void_p
+    fake, null = P(0x1000), P(0)
+    # missing scale array, zero tokens
+    assert lib.mla_cache_append_fp8(ctypes.byref(d), fake, fake, fake, fake, fake, null, 4, 1,
+                                    null) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append_fp8(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 4, 0,
+                                    null) == nat.MLA_ERR_INVALID_ARG
+    # missing scale array; workspace too small; heads not a multiple of 16
+    assert lib.mla_decode_attn_fp8(ctypes.byref(d), fake, fake, null, 4, fake, 2, fake, 2, 1, fake, null,
+                                   fake, 1 << 30, null) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_attn_fp8(ctypes.byref(d), fake, fake, fake, 4, fake, 2, fake, 2, 1, fake, null,
+                                   fake, 16, null) == nat.MLA_ERR_WORKSPACE
+    d24 = nat.mla_dims_default(24)
+    assert lib.mla_decode_attn_fp8(ctypes.byref(d24), fake, fake, fake, 4, fake, 2, fake, 2, 1, fake, null,
+                                   fake, 1 << 30, null) == nat.MLA_ERR_UNSUPPORTED
+    d.block_size = 32
+    assert lib.mla_cache_append_fp8(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 4, 1,
+                                    null) == nat.MLA_ERR_UNSUPPORTED
+
+
 def test_probe_library_exports_its_two_probes(nat):
     # the stream-read and MFMA-loop probes bench.py reports as achievable peaks
     from mla_latent_cache_append_amd import build
