@@ -52,7 +52,7 @@ def parse():
                          "the calibration of the traffic counters")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="parse two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench "
-                         "with --copy-calib into profiles/traffic_decode_attn.json, then exit")
+                         "with --copy-calib into profiles/traffic_<cache>_<workload>.json, then exit")
     return ap.parse_args()
 
 
@@ -269,7 +269,8 @@ def main():
     args = parse()
     if args.traffic_from:
         t = traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
-        out = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_decode_attn.json")
+        t["cache"] = args.cache
+        out = traffic_path(args.cache, args.workload)
         json.dump(t, open(out, "w"), indent=1)
         print(json.dumps(t))
         return
@@ -412,7 +413,7 @@ def main():
     achieved_gbps = alg["attn_bytes"] / attn_s / 1e9
     tflops = alg["attn_flops"] / attn_s / 1e12
     traffic = None
-    tf = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_decode_attn.json")
+    tf = traffic_path(args.cache, w.name)
     if os.path.exists(tf):
         try:
             t = json.load(open(tf))
@@ -483,6 +484,11 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def traffic_path(cache: str, workload: str) -> str:
+    """Stored HBM traffic of the attention call for one cache format and workload."""
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"traffic_{cache}_{workload}.json")
 
 
 def kernel_hash() -> str:
