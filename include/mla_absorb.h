@@ -149,6 +149,20 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_append_absorb — mla_cache_append and mla_absorb_q of one decode step in
+ * a single launch, for the usual case where the step's N new tokens are its N
+ * queries: new token n (c_kv[n], k_pe[n]) sits at position pos[n] and goes
+ * to slot_mapping[n], and query n (q_nope[n], q_pe[n]) is absorbed at the
+ * same position. Results are bit-identical to the two separate calls;
+ * arguments, layouts, slot handling and errors as there (T = N). Both parts
+ * only read their inputs and write disjoint outputs.
+ */
+int mla_append_absorb(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                      const int64_t* slot_mapping, uint16_t* pool, int64_t num_blocks,
+                      const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                      const uint16_t* w_uk, uint16_t* q_out, int32_t N, void* stream);
+
+/*
  * FP8 latent cache ([AUDIT] §6.1: FlashMLA's support matrix pairs its
  * MQA-mode kernels with an FP8 KV cache; the pages name the format only).
  * Reading used here: the same 576-element row per token, stored as OCP FP8
@@ -172,6 +186,16 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
 int mla_cache_append_fp8(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
                          const int32_t* pos, const int64_t* slot_mapping, uint8_t* pool8,
                          float* pool_scale, int64_t num_blocks, int32_t T, void* stream);
+
+/*
+ * mla_append_absorb_fp8 — mla_append_absorb into the FP8 pool (the append
+ * part as mla_cache_append_fp8).
+ */
+int mla_append_absorb_fp8(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                          const int64_t* slot_mapping, uint8_t* pool8, float* pool_scale,
+                          int64_t num_blocks, const uint16_t* q_nope, const uint16_t* q_pe,
+                          const int32_t* pos, const uint16_t* w_uk, uint16_t* q_out, int32_t N,
+                          void* stream);
 
 /*
  * mla_decode_attn_fp8 — mla_decode_attn over the FP8 pool: C_t is the row the

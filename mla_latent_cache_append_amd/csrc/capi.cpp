@@ -97,6 +97,35 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
                                                (hipStream_t)stream));
 }
 
+int mla_append_absorb(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                      const int64_t* slot_mapping, uint16_t* pool, int64_t num_blocks,
+                      const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                      const uint16_t* w_uk, uint16_t* q_out, int32_t N, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!c_kv || !k_pe || !slot_mapping || !pool || num_blocks <= 0 || !q_nope || !q_pe || !pos || !w_uk ||
+      !q_out || N <= 0)
+    return MLA_ERR_INVALID_ARG;
+  return launch_status(mla::launch_append_absorb(c_kv, k_pe, slot_mapping, pool, nullptr, num_blocks, q_nope,
+                                                 q_pe, pos, w_uk, q_out, N, dims->num_heads,
+                                                 (double)dims->rope_base, (hipStream_t)stream));
+}
+
+int mla_append_absorb_fp8(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                          const int64_t* slot_mapping, uint8_t* pool8, float* pool_scale,
+                          int64_t num_blocks, const uint16_t* q_nope, const uint16_t* q_pe,
+                          const int32_t* pos, const uint16_t* w_uk, uint16_t* q_out, int32_t N,
+                          void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!c_kv || !k_pe || !slot_mapping || !pool8 || !pool_scale || num_blocks <= 0 || !q_nope || !q_pe ||
+      !pos || !w_uk || !q_out || N <= 0)
+    return MLA_ERR_INVALID_ARG;
+  return launch_status(mla::launch_append_absorb(c_kv, k_pe, slot_mapping, pool8, pool_scale, num_blocks,
+                                                 q_nope, q_pe, pos, w_uk, q_out, N, dims->num_heads,
+                                                 (double)dims->rope_base, (hipStream_t)stream));
+}
+
 int mla_cache_append_fp8(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
                          const int32_t* pos, const int64_t* slot_mapping, uint8_t* pool8,
                          float* pool_scale, int64_t num_blocks, int32_t T, void* stream) {

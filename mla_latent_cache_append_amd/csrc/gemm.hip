@@ -14,6 +14,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "rope.h"
+#include "append.h"
 
 namespace mla {
 
@@ -33,13 +34,14 @@ __device__ __forceinline__ int aq_swz(int j) { return 2 * (j & 3) + 8 * ((j >> 3
 // and the contraction runs over j, its row index: the MFMA A operand
 // (8 consecutive j of one column c) comes from two transposing LDS reads
 // (ds_read_b64_tr_b16) of the row-major slice.
-__global__ __launch_bounds__(256) void absorb_q_kernel(
-    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
+constexpr int AQ_LDS = D_NOPE * AQ_COLS * 2;   // 32 KiB weight slice
+
+__device__ __forceinline__ void absorb_q_block(
+    int blk, char* wl, const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const int32_t* __restrict__ pos, const uint16_t* __restrict__ w_uk,
-    uint16_t* __restrict__ q_out, int N, int H, RopeFreqs fr) {
-  __shared__ __attribute__((aligned(16))) char wl[D_NOPE * AQ_COLS * 2];
-  const int h = blockIdx.x / AQ_CHUNKS;
-  const int chunk = blockIdx.x % AQ_CHUNKS;
+    uint16_t* __restrict__ q_out, int N, int H, const RopeFreqs& fr) {
+  const int h = blk / AQ_CHUNKS;
+  const int chunk = blk % AQ_CHUNKS;
   const int c0 = chunk * AQ_COLS;
   const uint16_t* w = w_uk + (int64_t)h * D_NOPE * D_C + c0;
   __attribute__((address_space(3))) char* wls = (__attribute__((address_space(3))) char*)wl;
@@ -122,6 +124,54 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(
     }
   }
 }
+
+__global__ __launch_bounds__(256) void absorb_q_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
+    const int32_t* __restrict__ pos, const uint16_t* __restrict__ w_uk,
+    uint16_t* __restrict__ q_out, int N, int H, RopeFreqs fr) {
+  __shared__ __attribute__((aligned(16))) char wl[AQ_LDS];
+  absorb_q_block(blockIdx.x, wl, q_nope, q_pe, pos, w_uk, q_out, N, H, fr);
+}
+
+// The step's first two calls in one launch: workgroups 0 .. H*4-1 absorb the
+// N queries (as absorb_q_kernel), the rest append the same N new tokens to
+// the cache, one wave per token (as the append kernels). Both read only their
+// inputs and write disjoint outputs, so they share a launch; the attention
+// that needs both follows on the stream.
+template <bool FP8>
+__global__ __launch_bounds__(256) void append_absorb_kernel(
+    const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
+    const int64_t* __restrict__ slot_mapping, void* __restrict__ pool, float* __restrict__ pool_scale,
+    int64_t num_slots, const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
+    const int32_t* __restrict__ pos, const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_out,
+    int N, int H, RopeFreqs fr) {
+  __shared__ __attribute__((aligned(16))) char wl[AQ_LDS];
+  const int n_absorb = H * AQ_CHUNKS;
+  if ((int)blockIdx.x < n_absorb) {
+    absorb_q_block(blockIdx.x, wl, q_nope, q_pe, pos, w_uk, q_out, N, H, fr);
+  } else {
+    const int j = ((int)blockIdx.x - n_absorb) * 4 + (int)(threadIdx.x >> 6);
+    if constexpr (FP8)
+      append_token_fp8(j, c_kv, k_pe, pos, slot_mapping, (uint8_t*)pool, pool_scale, num_slots, N, fr);
+    else
+      append_token(j, c_kv, k_pe, pos, slot_mapping, (uint16_t*)pool, num_slots, N, fr);
+  }
+}
+
+hipError_t launch_append_absorb(const uint16_t* c_kv, const uint16_t* k_pe, const int64_t* slot_mapping,
+                                void* pool, float* pool_scale, int64_t num_blocks, const uint16_t* q_nope,
+                                const uint16_t* q_pe, const int32_t* pos, const uint16_t* w_uk,
+                                uint16_t* q_out, int32_t N, int32_t H, double rope_base, hipStream_t stream) {
+  const dim3 grid(H * AQ_CHUNKS + (N + 3) / 4);
+  if (pool_scale)
+    hipLaunchKernelGGL(append_absorb_kernel<true>, grid, dim3(256), 0, stream, c_kv, k_pe, slot_mapping, pool,
+                       pool_scale, num_blocks * BLOCK, q_nope, q_pe, pos, w_uk, q_out, N, H, rope_freqs(rope_base));
+  else
+    hipLaunchKernelGGL(append_absorb_kernel<false>, grid, dim3(256), 0, stream, c_kv, k_pe, slot_mapping, pool,
+                       pool_scale, num_blocks * BLOCK, q_nope, q_pe, pos, w_uk, q_out, N, H, rope_freqs(rope_base));
+  return hipGetLastError();
+}
+
 
 constexpr int OU_ROWS = 64;                 // W_UV rows (output features) per workgroup
 constexpr int OU_CHUNKS = D_V / OU_ROWS;    // 2 workgroups per head

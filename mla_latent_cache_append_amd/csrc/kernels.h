@@ -28,6 +28,13 @@ hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_pe, const i
                            const uint16_t* w_uk, uint16_t* q_out, int32_t N, int32_t H,
                            double rope_base, hipStream_t stream);
 
+// append (bf16 pool, or FP8 codes when pool_scale is non-null) and absorb in one launch;
+// new token n sits at pos[n] and is also query n
+hipError_t launch_append_absorb(const uint16_t* c_kv, const uint16_t* k_pe, const int64_t* slot_mapping,
+                                void* pool, float* pool_scale, int64_t num_blocks, const uint16_t* q_nope,
+                                const uint16_t* q_pe, const int32_t* pos, const uint16_t* w_uk,
+                                uint16_t* q_out, int32_t N, int32_t H, double rope_base, hipStream_t stream);
+
 hipError_t launch_out_up(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int32_t N,
                          int32_t H, hipStream_t stream);
 

@@ -57,6 +57,10 @@ _SIG = {
     "mla_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaDims), _I32, _I32]),
     "mla_decode_attn": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _I64, _P, _I32, _P, _I32, _I32,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_append_absorb": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
+                                         _I32, _P]),
+    "mla_append_absorb_fp8": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
+                                             _P, _I32, _P]),
     "mla_cache_append_fp8": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _P, _I64, _I32, _P]),
     "mla_decode_attn_fp8": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I64, _P, _I32, _P, _I32,
                                            _I32, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -170,6 +174,33 @@ def mla_decode_attn(dims: MlaDims, q, pool, block_table, seq_lens, Lq: int, o_la
         ctypes.byref(dims), _ptr(q), _ptr(pool), pool.shape[0], _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), B, Lq, _ptr(o_lat), _ptr(lse), _ptr(workspace),
         workspace.numel(), _stream(stream)))
+
+
+def mla_append_absorb(dims: MlaDims, c_kv, k_pe, slot_mapping, pool, q_nope, q_pe, pos, w_uk, q_out,
+                      pool_scale=None, stream=None):
+    """Append the N new tokens and absorb the N queries of the same tokens in one
+    launch (FP8 pool when ``pool_scale`` is given)."""
+    N, H = q_nope.shape[0], dims.num_heads
+    _check("c_kv", c_kv, torch.bfloat16, (N, D_C))
+    _check("k_pe", k_pe, torch.bfloat16, (N, D_ROPE))
+    _check("slot_mapping", slot_mapping, torch.int64, (N,))
+    _check("q_nope", q_nope, torch.bfloat16, (N, H, D_NOPE))
+    _check("q_pe", q_pe, torch.bfloat16, (N, H, D_ROPE))
+    _check("pos", pos, torch.int32, (N,))
+    _check("w_uk", w_uk, torch.bfloat16, (H, D_NOPE, D_C))
+    _check("q_out", q_out, torch.bfloat16, (N, H, D_K))
+    if pool_scale is None:
+        _check("pool", pool, torch.bfloat16)
+        if pool.dim() != 3 or tuple(pool.shape[1:]) != (BLOCK, D_K):
+            raise ValueError("pool must be [num_blocks, 64, 576]")
+        _ok("mla_append_absorb", lib().mla_append_absorb(
+            ctypes.byref(dims), _ptr(c_kv), _ptr(k_pe), _ptr(slot_mapping), _ptr(pool), pool.shape[0],
+            _ptr(q_nope), _ptr(q_pe), _ptr(pos), _ptr(w_uk), _ptr(q_out), N, _stream(stream)))
+    else:
+        _check_fp8_pool(pool, pool_scale)
+        _ok("mla_append_absorb_fp8", lib().mla_append_absorb_fp8(
+            ctypes.byref(dims), _ptr(c_kv), _ptr(k_pe), _ptr(slot_mapping), _ptr(pool), _ptr(pool_scale),
+            pool.shape[0], _ptr(q_nope), _ptr(q_pe), _ptr(pos), _ptr(w_uk), _ptr(q_out), N, _stream(stream)))
 
 
 def _check_fp8_pool(pool8, pool_scale):

@@ -60,13 +60,16 @@ class DecodeStep:
         nat.mla_out_up(self.dims, self.o_lat, self.w_uv, self.o)
 
     def __call__(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots):
-        """Append the N new tokens (row n = b*Lq + i at position q_pos[n]), then attend."""
-        self.append(c_kv, k_pe, q_pos, slots)
-        self.attend(q_nope, q_pe, q_pos)
+        """Append the N new tokens (row n = b*Lq + i at position q_pos[n]), then
+        attend: append and absorb share one launch, then attention and out_up."""
+        nat.mla_append_absorb(self.dims, c_kv, k_pe, slots, self.pool, q_nope, q_pe, q_pos, self.w_uk, self.q,
+                              pool_scale=self.pool_scale)
+        self.decode_attn()
+        nat.mla_out_up(self.dims, self.o_lat, self.w_uv, self.o)
         return self.o
 
     def capture(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots):
-        """Record one whole step (five kernels, no allocation, no memset) as a
+        """Record one whole step (four kernels, no allocation, no memset) as a
         HIP graph over these input tensors; returns the graph, whose replay()
         reruns the step on whatever the tensors then hold."""
         return _capture(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots)
@@ -127,6 +130,6 @@ class LayerStep:
         return self.out
 
     def capture(self, h, q_pos, slots):
-        """Record the whole layer (twelve kernels) as a HIP graph over these
+        """Record the whole layer (ten kernels) as a HIP graph over these
         input tensors; replay() reruns it on whatever they then hold."""
         return _capture(self, h, q_pos, slots)

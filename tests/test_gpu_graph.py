@@ -25,21 +25,22 @@ def _lib():
     native.lib()
 
 
-@pytest.mark.parametrize("H,lens", [(128, [700, 33, 1500, 64]), (16, [300, 1, 129])])
-def test_graph_replays_match_eager(H, lens):
+@pytest.mark.parametrize("H,lens,fp8", [(128, [700, 33, 1500, 64], False), (16, [300, 1, 129], False),
+                                       (16, [300, 1, 129], True)])
+def test_graph_replays_match_eager(H, lens, fp8):
     w = workloads.Workload("graph", len(lens), H, 1, lens, "permuted", seed=11)
-    print(f"\n[case] graph replay: H={H} lens={lens}", flush=True)
-    run = hz.GpuRun(w)
+    print(f"\n[case] graph replay: H={H} lens={lens} fp8={fp8}", flush=True)
+    run = hz.GpuRun(w, fp8=fp8)
     ckv, kpe, qpos, slot = run.new
     qn, qp = hz.to_dev(run.q_nope), hz.to_dev(run.q_pe)
     step = run.step
     step(ckv, kpe, qn, qp, qpos, slot)
     torch.cuda.synchronize()
     eager = {k: getattr(step, k).clone() for k in ("q", "o_lat", "lse", "o")}
+    out = dict(q=hz.bits_of(eager["q"]), o_lat=hz.bits_of(eager["o_lat"]),
+               lse=eager["lse"].cpu().numpy().astype(np.float64), o=hz.bits_of(eager["o"]))
     for b in (0, len(lens) - 1):
-        hz.check_seq("eager", w, dict(q=hz.bits_of(eager["q"]), o_lat=hz.bits_of(eager["o_lat"]),
-                                      lse=eager["lse"].cpu().numpy().astype(np.float64),
-                                      o=hz.bits_of(eager["o"])), b)
+        hz.check_seq("eager", w, out, b, ref=hz.oracle_seq_fp8(w, b) if fp8 else None)
     g = step.capture(ckv, kpe, qn, qp, qpos, slot)
     torch.cuda.synchronize()
     for rep in range(3):

@@ -90,6 +90,22 @@ def test_invalid_arguments_return_status(nat):
     assert lib.mla_cache_append(None, fake, fake, fake, fake, fake, 4, 1, null) == nat.MLA_ERR_INVALID_ARG
 
 
+def test_fused_append_absorb_checks_arguments_on_the_host(nat):
+    lib = nat.lib()
+    d = nat.mla_dims_default(16)
+    P = ctypes.c_void_p
+    fake, null = P(0x1000), P(0)
+    assert lib.mla_append_absorb(ctypes.byref(d), fake, fake, fake, fake, 4, fake, fake, fake, fake, null, 2,
+                                 null) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_absorb(ctypes.byref(d), fake, fake, fake, fake, 4, fake, fake, fake, fake, fake, 0,
+                                 null) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_absorb_fp8(ctypes.byref(d), fake, fake, fake, fake, null, 4, fake, fake, fake, fake,
+                                     fake, 2, null) == nat.MLA_ERR_INVALID_ARG
+    d.block_size = 32
+    assert lib.mla_append_absorb(ctypes.byref(d), fake, fake, fake, fake, 4, fake, fake, fake, fake, fake, 2,
+                                 null) == nat.MLA_ERR_UNSUPPORTED
+
+
 def test_fp8_calls_check_arguments_on_the_host(nat):
     lib = nat.lib()
     d = nat.mla_dims_default(16)
