@@ -385,7 +385,8 @@ __device__ __forceinline__ void fp8_tile_load(const uint8_t* pool8, const float*
                                               int n_valid, int tid, Fp8Stage& st) {
   const uint8_t* base = pool8 + (int64_t)blk * TILE_BYTES8;
 #pragma unroll
-  for (int i = 0; i < FP8_LOADS; ++i) st.v[i] = *(const u32x4*)(base + 16 * (tid + 256 * i));
+  for (int i = 0; i < FP8_LOADS; ++i)   // read once per call: non-temporal
+    st.v[i] = __builtin_nontemporal_load((const u32x4*)(base + 16 * (tid + 256 * i)));
   st.sc = *(const f32x4*)(scales + (int64_t)blk * BLOCK + 4 * (tid & (BLOCK / 4 - 1)));
   st.n_valid = n_valid;
 }

