@@ -407,22 +407,31 @@ def main():
             cold[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
     del flush
 
-    # graph steps: the whole step recorded once as a HIP graph and replayed, the
-    # way a decode loop issues it; this is the timed throughput
-    graph = step.capture(*[args_step[i] for i in (0, 1, 2, 3, 4, 5)])
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    g1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = max(wall * 1e3, g0.elapsed_time(g1)) / args.steps
+    # graph steps: S whole steps recorded as one HIP graph and replayed, the
+    # way a decode loop captured ahead of time issues them; exactly args.steps
+    # steps are timed (S divides it). This is the timed throughput. One step
+    # per graph is timed as well, for reference.
+    spg = next(k for k in (10, 8, 5, 4, 2, 1) if args.steps % k == 0)
+
+    def time_graph(reps):
+        graph = step.capture(*[args_step[i] for i in (0, 1, 2, 3, 4, 5)], reps=reps)
+        for _ in range(max(1, args.warmup // reps)):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g0.record()
+        for _ in range(args.steps // reps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del graph
+        return max(wall * 1e3, g0.elapsed_time(g1)) / args.steps
+
+    ms_per_step_1 = time_graph(1)
+    ms_per_step = time_graph(spg)
 
     layer = layer_timing(torch, nat, workloads, w, step, args, to_dev, qpos, slot_n) if args.layer else None
     ach = achievable_peaks(torch, dev)
@@ -483,8 +492,10 @@ def main():
         "cold_cache": {"steps": args.cold_steps,
                        "call_us_median": {n: float(np.median(v)) for n, v in cold.items()},
                        "decode_attn_GBps": alg["attn_bytes"] / (float(np.median(cold["decode_attn"])) * 1e-6) / 1e9},
-        "step_mode": "hip_graph replay of the whole step, append and absorb fused in one launch "
-                     "(eager per-call events give call_us_median)",
+        "step_mode": f"hip_graph replays of {spg} whole steps per graph, append and absorb fused in one "
+                     "launch (eager per-call events give call_us_median)",
+        "steps_per_graph": spg,
+        "ms_per_step_one_step_graphs": ms_per_step_1,
         "eager_ms_per_step": eager_wall * 1e3 / args.steps,
         "eager_step_us_median_events": float(np.median(step_us)),
         "fill": {"tokens": int(w.lens.sum()) - w.N, "append_kernel_s": fill_events * 1e-3,

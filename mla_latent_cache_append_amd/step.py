@@ -68,15 +68,18 @@ class DecodeStep:
         nat.mla_out_up(self.dims, self.o_lat, self.w_uv, self.o)
         return self.o
 
-    def capture(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots):
-        """Record one whole step (four kernels, no allocation, no memset) as a
-        HIP graph over these input tensors; returns the graph, whose replay()
-        reruns the step on whatever the tensors then hold."""
-        return _capture(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots)
+    def capture(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots, reps: int = 1):
+        """Record ``reps`` whole steps in a row (four kernels each, no
+        allocation, no memset) as one HIP graph over these input tensors;
+        returns the graph, whose replay() reruns them on whatever the tensors
+        then hold. Several steps per graph amortise the graph launch, as a
+        decode loop captured ahead of time does."""
+        return _capture(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots, reps=reps)
 
 
-def _capture(fn, *args):
-    """HIP graph of one call fn(*args), after one eager call on a side stream."""
+def _capture(fn, *args, reps: int = 1):
+    """HIP graph of ``reps`` calls fn(*args) in a row, after one eager call on
+    a side stream."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):       # one eager run initialises the stream state
@@ -84,7 +87,8 @@ def _capture(fn, *args):
     torch.cuda.current_stream().wait_stream(side)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        fn(*args)
+        for _ in range(reps):
+            fn(*args)
     return g
 
 

@@ -25,11 +25,13 @@ def _lib():
     native.lib()
 
 
-@pytest.mark.parametrize("H,lens,fp8", [(128, [700, 33, 1500, 64], False), (16, [300, 1, 129], False),
-                                       (16, [300, 1, 129], True)])
-def test_graph_replays_match_eager(H, lens, fp8):
+@pytest.mark.parametrize("H,lens,fp8,reps", [(128, [700, 33, 1500, 64], False, 1), (16, [300, 1, 129], False, 1),
+                                            (16, [300, 1, 129], True, 1), (128, [700, 33, 1500, 64], False, 3)])
+def test_graph_replays_match_eager(H, lens, fp8, reps):
+    """reps > 1: several whole steps in one graph (the step is idempotent: it
+    rewrites the same cache rows and recomputes the same outputs)."""
     w = workloads.Workload("graph", len(lens), H, 1, lens, "permuted", seed=11)
-    print(f"\n[case] graph replay: H={H} lens={lens} fp8={fp8}", flush=True)
+    print(f"\n[case] graph replay: H={H} lens={lens} fp8={fp8} steps per graph={reps}", flush=True)
     run = hz.GpuRun(w, fp8=fp8)
     ckv, kpe, qpos, slot = run.new
     qn, qp = hz.to_dev(run.q_nope), hz.to_dev(run.q_pe)
@@ -41,7 +43,7 @@ def test_graph_replays_match_eager(H, lens, fp8):
                lse=eager["lse"].cpu().numpy().astype(np.float64), o=hz.bits_of(eager["o"]))
     for b in (0, len(lens) - 1):
         hz.check_seq("eager", w, out, b, ref=hz.oracle_seq_fp8(w, b) if fp8 else None)
-    g = step.capture(ckv, kpe, qn, qp, qpos, slot)
+    g = step.capture(ckv, kpe, qn, qp, qpos, slot, reps=reps)
     torch.cuda.synchronize()
     for rep in range(3):
         for k in ("q", "o_lat", "o"):
