@@ -275,6 +275,35 @@ def test_special_cases():
     assert rel(a["o_lat"][0, 0], case["c_kv"][7]) <= 1e-6
 
 
+def check_large_L_tilting():
+    """Gaussian exponential tilting: for keys c ~ N(0, I) the softmax-weighted
+    mean sum_t p_t c_t with p_t proportional to exp(a . c_t) tends to a as L
+    grows (E[c e^{a.c}] / E[e^{a.c}] = a). Here a = scale * q_lat, with the
+    rope part of the score an independent Gaussian factor that cancels. At
+    L = 50,000 and |a| = 1 the effective sample is ~L/e, so the projection of
+    o_lat on a is 1 within ~0.01 and its angle to a small."""
+    rng = np.random.default_rng(23)
+    L = 50_000
+    c_kv = rng.standard_normal((L, 512))
+    k_r = rng.standard_normal((L, 64))
+    scale = mla.default_scale()
+    q_lat = rng.standard_normal((1, 1, 512))
+    q_lat *= 1.0 / (scale * np.linalg.norm(q_lat))          # |scale * q_lat| = 1
+    q_r = rng.standard_normal((1, 1, 64)) * 0.5 / (scale * 8.0)
+    o_lat, _ = mla.latent_attention(q_lat, q_r, c_kv, k_r, np.array([L - 1]), scale)
+    a = scale * q_lat[0, 0]
+    o = o_lat[0, 0]
+    proj = float(o @ a / (a @ a))
+    cos = float(o @ a / (np.linalg.norm(o) * np.linalg.norm(a)))
+    assert abs(proj - 1.0) < 0.03, proj
+    assert cos > 0.95, cos
+    return proj, cos
+
+
+def test_large_L_tilting_limit():
+    check_large_L_tilting()
+
+
 def test_rope_on_content_breaks_absorption():
     """Negative control ([MLA80] §4: RoPE on K_C makes absorption diverge by
     1.03e+01): the checker must see an O(1) difference."""
@@ -346,3 +375,12 @@ def test_planted_merge_without_weights(monkeypatch):
         return acc / l[..., None], np.log(l)
     monkeypatch.setattr(mla, "merge_partials", bad)
     assert err_partition(mla, rand_case(24, 4, 1, 150)) > 1e-3
+
+
+def test_planted_softmax_temperature(monkeypatch):
+    """A softmax taken at the wrong temperature (scores halved inside the
+    weights) fails the large-L tilting limit."""
+    real = mla.masked_softmax
+    monkeypatch.setattr(mla, "masked_softmax", lambda s_, mask: real(0.5 * s_, mask))
+    with pytest.raises(AssertionError):
+        check_large_L_tilting()
