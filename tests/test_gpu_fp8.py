@@ -155,13 +155,14 @@ def test_fp8_bad_block_id_poisons_only_its_sequence():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["v2lite_b64_h16_l4096", "v3_b32_h128_l16384"])
+@pytest.mark.parametrize("name", ["v2lite_b64_h16_l4096", "v3_b32_h128_l16384", "ragged_b128_h128_l1to32768",
+                                  "causal8_b16_h128_l65544"])
 def test_fp8_full_size_sampled(name):
     w = workloads.make(name, seed=0)
     _say(f"fp8 full size {name}: B={w.B} H={w.H} Lq={w.Lq} total keys={int(w.lens.sum())}")
     run = hz.GpuRun(w, fp8=True)
     out = run.run()
-    for b in sorted({0, w.B // 2, w.B - 1}):
+    for b in sorted({0, w.B // 2, w.B - 1, int(np.argmax(w.lens)), int(np.argmin(w.lens))}):
         ref = hz.oracle_seq_fp8(w, b)
         check_codes(name, run, w, b, ref["codes"], ref["scale"])
         check_outputs(name, w, out, b, ref)
