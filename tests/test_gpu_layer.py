@@ -27,6 +27,8 @@ def _lib():
 @pytest.mark.parametrize("N,K,M,resid", [
     (1, 2048, 2048, False), (32, 2048, 512, True), (33, 1536, 2048, True), (7, 96, 12, False),
     (1, 32, 4, True), (200, 512, 64, False),
+    # wide maps take 32 features per workgroup (at least 128 workgroups): even and ragged M, ragged N
+    (32, 1024, 8192, True), (40, 512, 4100, False),
 ], ids=lambda v: str(v))
 def test_linear_matches_oracle(N, K, M, resid):
     from mla_latent_cache_append_amd import native as nat
