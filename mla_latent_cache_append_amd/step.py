@@ -101,7 +101,10 @@ class LayerStep:
         h_out = h + Wo [o_0 | ... | o_{H-1}]
 
     Weights are [out, in] bf16 device tensors; every product runs in
-    ``mla_linear`` (the residual add is fused into the last one)."""
+    ``mla_linear`` (the residual add is fused into the last one). The maps
+    that do not depend on each other run on side streams: Wdkv and Wkr each
+    beside Wdq, then Wqr beside Wuq (narrow maps fill a few workgroups each,
+    so side by side they share the chip); the decode waits for all of them."""
 
     def __init__(self, decode: DecodeStep, w_dq, w_uq, w_qr, w_dkv, w_kr, w_o, device="cuda"):
         self.decode = decode
@@ -121,14 +124,28 @@ class LayerStep:
         self.c_kv = torch.empty(N, nat.D_C, **bf)
         self.k_pe = torch.empty(N, nat.D_ROPE, **bf)
         self.out = torch.empty(N, d_model, **bf)
+        # side streams at the default priority
+        self.side_kv = torch.cuda.Stream(device=device)
+        self.side_kr = torch.cuda.Stream(device=device)
+        self.side_qr = torch.cuda.Stream(device=device)
 
     def __call__(self, h, q_pos, slots):
         N = self.decode.N
-        nat.mla_linear(h, self.w_dkv, self.c_kv)
-        nat.mla_linear(h, self.w_kr, self.k_pe)
+        main = torch.cuda.current_stream()
+        self.side_kv.wait_stream(main)
+        self.side_kr.wait_stream(main)
+        with torch.cuda.stream(self.side_kv):
+            nat.mla_linear(h, self.w_dkv, self.c_kv)
+        with torch.cuda.stream(self.side_kr):
+            nat.mla_linear(h, self.w_kr, self.k_pe)
         nat.mla_linear(h, self.w_dq, self.qz)
+        self.side_qr.wait_stream(main)
+        with torch.cuda.stream(self.side_qr):
+            nat.mla_linear(self.qz, self.w_qr, self.q_pe.view(N, -1))
         nat.mla_linear(self.qz, self.w_uq, self.q_nope.view(N, -1))
-        nat.mla_linear(self.qz, self.w_qr, self.q_pe.view(N, -1))
+        main.wait_stream(self.side_kv)
+        main.wait_stream(self.side_kr)
+        main.wait_stream(self.side_qr)
         self.decode(self.c_kv, self.k_pe, self.q_nope, self.q_pe, q_pos, slots)
         nat.mla_linear(self.decode.o.view(N, -1), self.w_o, self.out, residual=h)
         return self.out

@@ -113,9 +113,10 @@ def test_layer_stack_error_growth():
 
 
 def test_layer_graph_replays_match_eager():
-    """The whole layer (projections, decode step, residual output projection)
-    recorded as one HIP graph replays bit for bit to the eager layer, with
-    eager work that overwrites the outputs between replays."""
+    """The whole layer (projections, two of them on side streams, decode step,
+    residual output projection) recorded as one HIP graph replays bit for bit
+    to the eager layer, with eager work that overwrites every buffer the layer
+    writes between replays."""
     from mla_latent_cache_append_amd.step import LayerStep
     H, d_model, d_cq = 16, 2048, 1536
     w = workloads.Workload("layer_graph", 3, H, 1, [70, 600, 1500], "permuted", seed=300)
@@ -130,8 +131,9 @@ def test_layer_graph_replays_match_eager():
     g = st.capture(h, qpos, slot)
     torch.cuda.synchronize()
     for rep in range(3):
-        st.out.fill_(float("nan"))
-        st.decode.o.fill_(float("nan"))
+        # every buffer the layer writes, the side-stream projections' included
+        for buf in (st.out, st.decode.o, st.c_kv, st.k_pe, st.qz, st.q_nope, st.q_pe):
+            buf.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
