@@ -90,6 +90,30 @@ def test_invalid_arguments_return_status(nat):
     assert lib.mla_cache_append(None, fake, fake, fake, fake, fake, 4, 1, null) == nat.MLA_ERR_INVALID_ARG
 
 
+def test_size_limits_return_unsupported(nat):
+    # rows of one sequence (Lq * H) above 2^20, a block table spanning more than
+    # 2^30 keys, and more merge workgroups than a grid holds: refused on the host
+    lib = nat.lib()
+    d = nat.mla_dims_default(16)
+    P = ctypes.c_void_p
+    fake, null = P(0x1000), P(0)
+    for fn in (lib.mla_decode_attn, ):
+        assert fn(ctypes.byref(d), fake, fake, 4, fake, 2, fake, 1, (1 << 16) + 1, fake, null, fake, 1 << 40,
+                  null) == nat.MLA_ERR_UNSUPPORTED
+        assert fn(ctypes.byref(d), fake, fake, 4, fake, (1 << 24) + 1, fake, 1, 1, fake, null, fake, 1 << 40,
+                  null) == nat.MLA_ERR_UNSUPPORTED
+        assert fn(ctypes.byref(d), fake, fake, 4, fake, 2, fake, 1 << 30, 1 << 16, fake, null, fake, 1 << 40,
+                  null) == nat.MLA_ERR_UNSUPPORTED
+    assert lib.mla_decode_attn_fp8(ctypes.byref(d), fake, fake, fake, 4, fake, 2, fake, 1, (1 << 16) + 1, fake,
+                                   null, fake, 1 << 40, null) == nat.MLA_ERR_UNSUPPORTED
+    assert lib.mla_decode_attn_fp8(ctypes.byref(d), fake, fake, fake, 4, fake, (1 << 24) + 1, fake, 1, 1, fake,
+                                   null, fake, 1 << 40, null) == nat.MLA_ERR_UNSUPPORTED
+    # heads above 128
+    d200 = nat.mla_dims_default(144)
+    assert lib.mla_decode_attn(ctypes.byref(d200), fake, fake, 4, fake, 2, fake, 1, 1, fake, null, fake, 1 << 40,
+                               null) == nat.MLA_ERR_UNSUPPORTED
+
+
 def test_fused_append_absorb_checks_arguments_on_the_host(nat):
     lib = nat.lib()
     d = nat.mla_dims_default(16)
