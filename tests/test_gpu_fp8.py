@@ -112,6 +112,9 @@ def test_fp8_append_skips_out_of_range_slots_and_zero_row():
     (128, 1, [1, 64, 65, 700]),
     (128, 8, [8, 9, 71, 200]),
     (16, 3, [3, 4, 64, 66, 190]),
+    # prefill chunks over the FP8 cache: many query tokens, causal among themselves
+    (128, 64, [64, 100, 1000]),
+    (16, 203, [203, 777]),
 ], ids=lambda v: str(v))
 def test_fp8_decode_small(H, Lq, lens):
     w = workloads.Workload(f"fp8_h{H}_lq{Lq}", len(lens), H, Lq, lens,
