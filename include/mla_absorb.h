@@ -1,6 +1,7 @@
 /*
  * libmla_absorb — weight-absorbed Multi-head Latent Attention (MLA) decode
- * over a paged bf16 latent cache, for AMD MI355X (gfx950).
+ * over a paged latent cache (bf16 rows, or FP8 codes with a per-token scale),
+ * for AMD MI355X (gfx950).
  *
  * Sources, cited by title and section:
  *   [AUDIT]  llm-atlas page "DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界"
@@ -9,6 +10,8 @@
  *
  * One decode step of one attention layer is four calls on one stream:
  *   mla_cache_append  -> mla_absorb_q -> mla_decode_attn -> mla_out_up
+ * (the first two may be one launch, mla_append_absorb; the _fp8 calls take
+ * the FP8 cache in place of the bf16 pool).
  *
  * Conventions shared by every call
  *   - bf16 tensors are passed as uint16_t bit patterns; every tensor is dense
