@@ -161,8 +161,8 @@ def layer_timing(torch, nat, workloads, w, step, args, to_dev, qpos, slots) -> d
     q_nope = Wuq qz, q_pe = Wqr qz, the decode step, h_out = h + Wo o. Model
     widths: d_model 2048 at 16 heads (V2-Lite), 7168 at 128 heads (V3); query
     latent 1536. Weights N(0, 1/in), hidden states N(0, 1). Per call: HIP
-    events around replays of a graph of 20 calls; the whole layer as HIP-graph
-    replays."""
+    events around replays of a graph of 20 calls; the whole layer as replays
+    of HIP graphs of ten layers (and of one layer)."""
     from mla_latent_cache_append_amd.step import LayerStep
     d_model = 2048 if w.H <= 16 else 7168
     d_cq = 1536
@@ -171,12 +171,12 @@ def layer_timing(torch, nat, workloads, w, step, args, to_dev, qpos, slots) -> d
     h = to_dev(workloads.hidden_states(args.seed, w.N, d_model))
     N = w.N
     calls = {
-        "w_dkv": lambda: nat.mla_linear(h, ls.w_dkv, ls.c_kv),
-        "w_kr": lambda: nat.mla_linear(h, ls.w_kr, ls.k_pe),
-        "w_dq": lambda: nat.mla_linear(h, ls.w_dq, ls.qz),
-        "w_uq": lambda: nat.mla_linear(ls.qz, ls.w_uq, ls.q_nope.view(N, -1)),
-        "w_qr": lambda: nat.mla_linear(ls.qz, ls.w_qr, ls.q_pe.view(N, -1)),
-        "w_o": lambda: nat.mla_linear(step.o.view(N, -1), ls.w_o, ls.out, residual=h),
+        "w_dkv": lambda: nat.mla_linear(h, ls.w_dkv, ls.c_kv, workspace=ls.ws["dkv"]),
+        "w_kr": lambda: nat.mla_linear(h, ls.w_kr, ls.k_pe, workspace=ls.ws["kr"]),
+        "w_dq": lambda: nat.mla_linear(h, ls.w_dq, ls.qz, workspace=ls.ws["dq"]),
+        "w_uq": lambda: nat.mla_linear(ls.qz, ls.w_uq, ls.q_nope.view(N, -1), workspace=ls.ws["uq"]),
+        "w_qr": lambda: nat.mla_linear(ls.qz, ls.w_qr, ls.q_pe.view(N, -1), workspace=ls.ws["qr"]),
+        "w_o": lambda: nat.mla_linear(step.o.view(N, -1), ls.w_o, ls.out, residual=h, workspace=ls.ws["o"]),
     }
     ls(h, qpos, slots)
     torch.cuda.synchronize()
@@ -199,25 +199,32 @@ def layer_timing(torch, nat, workloads, w, step, args, to_dev, qpos, slots) -> d
             e1.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e3 / 20)
         per[name] = float(np.median(ts))
-    g = ls.capture(h, qpos, slots)
-    for _ in range(5):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = max(args.steps // 4, 10)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    layer_us = e0.elapsed_time(e1) * 1e3 / reps
+    def layer_graph_us(per_graph):
+        g = ls.capture(h, qpos, slots, reps=per_graph)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(args.steps // 4, 10)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+
+    # ten layers per graph, as a model's stack of layers is captured (the
+    # graph launch amortised); one layer per graph beside it
+    layer_us = layer_graph_us(10)
+    layer_us_one = layer_graph_us(1)
     wbytes = {k: int(v.numel()) * 2 for k, v in lw.items()}
     io = lambda k: N * (lw[k].shape[0] + lw[k].shape[1]) * 2      # activations in and out
     gbps = {k: (wbytes[k] + io(k)) / (per[k] * 1e-6) / 1e9 for k in calls}
     return {"d_model": d_model, "d_cq": d_cq, "call_us_median": per,
             "weight_bytes": wbytes, "GBps": gbps,
             "w_o_frac_of_8TBps": gbps["w_o"] / HBM_PEAK_GBPS,
-            "layer_us_graph": layer_us, "layer_tokens_per_s": N / (layer_us * 1e-6)}
+            "layer_us_graph": layer_us, "layers_per_graph": 10, "layer_us_one_layer_graphs": layer_us_one,
+            "layer_tokens_per_s": N / (layer_us * 1e-6)}
 
 
 def algorithmic(w, fp8: bool = False):

@@ -228,21 +228,39 @@ int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv
                int32_t N, void* stream);
 
 /*
+ * mla_linear_workspace_size — bytes of fp32 device workspace with which
+ * mla_linear splits the contraction of an [N][K] -> [N][M] map over several
+ * workgroups (maps with few output tiles, e.g. K = 7168 -> M = 512 at 32
+ * tokens). 0 when the map is never split, or the sizes are not supported.
+ */
+size_t mla_linear_workspace_size(int32_t N, int32_t K, int32_t M);
+
+/*
  * mla_linear — a bias-free linear map, for the projections around the
  * attention ([MLA80] §2: Wdq, Wuq, Wqr, Wdkv, Wkr and the output projection
  * Wo are nn.Linear(bias=False) maps of the layer).
  * y[n] = W x[n] (+ residual[n])
- *   x         device [N][K] bf16
- *   w         device [M][K] bf16 (nn.Linear weight layout: [out][in])
- *   residual  device [N][M] bf16, or NULL; may be the same buffer as y
- *   y         device [N][M] bf16
+ *   x          device [N][K] bf16
+ *   w          device [M][K] bf16 (nn.Linear weight layout: [out][in])
+ *   residual   device [N][M] bf16, or NULL; may be the same buffer as y
+ *   y          device [N][M] bf16
+ *   workspace  device, 16-byte aligned, or NULL; caller-owned; overlaps none
+ *              of the other buffers, and calls that may run at the same
+ *              time (other streams) each need their own
+ *   workspace_bytes  its size; when it is at least
+ *              mla_linear_workspace_size(N, K, M) (and that is > 0) the
+ *              contraction is split and the fp32 partial sums are added
+ *              in a fixed order by a second kernel; otherwise the call runs
+ *              unsplit and leaves the workspace untouched
  * fp32 accumulation (bf16 MFMA), the residual added in fp32, one rounding to
  * bf16. K must be a multiple of 32 and M of 4, N at most 2,097,120
- * (MLA_ERR_UNSUPPORTED otherwise); null pointers or sizes <= 0 give
- * MLA_ERR_INVALID_ARG. Deterministic (fixed summation order).
+ * (MLA_ERR_UNSUPPORTED otherwise); null pointers, sizes <= 0 or a misaligned
+ * workspace give MLA_ERR_INVALID_ARG. Deterministic: calls with the same
+ * sizes and the same choice (split or not) give the same bits; split and
+ * unsplit results differ only in fp32 summation order.
  */
 int mla_linear(const uint16_t* x, const uint16_t* w, const uint16_t* residual, uint16_t* y,
-               int32_t N, int32_t K, int32_t M, void* stream);
+               int32_t N, int32_t K, int32_t M, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -169,11 +169,18 @@ int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv
       mla::launch_out_up(o_lat, w_uv, o, N, dims->num_heads, (hipStream_t)stream));
 }
 
+size_t mla_linear_workspace_size(int32_t N, int32_t K, int32_t M) {
+  if (N <= 0 || K <= 0 || M <= 0 || K % 32 != 0 || M % 4 != 0 || N > 65535 * 32) return 0;
+  return mla::plan_linear(N, K, M).ws_bytes;
+}
+
 int mla_linear(const uint16_t* x, const uint16_t* w, const uint16_t* residual, uint16_t* y,
-               int32_t N, int32_t K, int32_t M, void* stream) {
+               int32_t N, int32_t K, int32_t M, void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !w || !y || N <= 0 || K <= 0 || M <= 0) return MLA_ERR_INVALID_ARG;
+  if (workspace && ((uintptr_t)workspace % 16 != 0)) return MLA_ERR_INVALID_ARG;
   if (K % 32 != 0 || M % 4 != 0 || N > 65535 * 32) return MLA_ERR_UNSUPPORTED;
-  return launch_status(mla::launch_linear(x, w, residual, y, N, K, M, (hipStream_t)stream));
+  return launch_status(mla::launch_linear(x, w, residual, y, workspace, workspace ? workspace_bytes : 0, N, K, M,
+                                          (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -38,8 +38,19 @@ hipError_t launch_append_absorb(const uint16_t* c_kv, const uint16_t* k_pe, cons
 hipError_t launch_out_up(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int32_t N,
                          int32_t H, hipStream_t stream);
 
-hipError_t launch_linear(const uint16_t* x, const uint16_t* w, const uint16_t* r, uint16_t* y,
-                         int32_t N, int32_t K, int32_t M, hipStream_t stream);
+// Shape of a linear map's launch: step width, features per workgroup, and
+// the number of contraction slices (ks > 1 needs ws_bytes of fp32 workspace).
+struct LinearPlan {
+  bool wide;        // 128-wide contraction steps (K % 128 == 0, K <= 8192)
+  int mt;           // 16-feature tiles per workgroup (1 or 2)
+  int ks;           // contraction slices, each its own workgroups
+  size_t ws_bytes;  // ks * N * M * 4 when ks > 1, else 0
+};
+LinearPlan plan_linear(int32_t N, int32_t K, int32_t M);
+
+// Splits only when workspace holds at least plan_linear(...).ws_bytes.
+hipError_t launch_linear(const uint16_t* x, const uint16_t* w, const uint16_t* r, uint16_t* y, void* workspace,
+                         size_t workspace_bytes, int32_t N, int32_t K, int32_t M, hipStream_t stream);
 
 // Split-KV plan shared by the host (workspace sizing, grid) and the kernels.
 struct AttnPlan {

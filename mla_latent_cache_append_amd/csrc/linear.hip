@@ -8,16 +8,28 @@
 //
 // Decode multiplies a few tokens by a large weight, so the kernel is built
 // to stream the weight once: a workgroup owns 16 MT output features x 32
-// tokens and its sixteen waves take the 32-wide contraction steps in turn (wave w
-// steps w, w + 16, ...; the loads of four steps in flight per wave), so that
-// at any moment the workgroup reads one contiguous window of each weight
-// row. The sixteen partial sums meet in the LDS and 256 MT threads add them
-// up. MT = 2 (two 16-feature tiles on each weight step, so each workgroup
-// reads the activations once for twice the features) when that still gives
-// at least 128 workgroups; MT = 1 otherwise, so that narrow maps keep more
-// workgroups. Measured on Wo (7168 x 16384, 32 tokens): 62.7 us with MT = 2
-// against 92.8 us with MT = 1; on 512 x 7168, MT = 1 is faster (25.8 us
-// against 32.9 us).
+// tokens and its sixteen waves take contraction steps in turn, so that at
+// any moment the workgroup reads one contiguous window of each weight row.
+// The sixteen partial sums meet in the LDS and 256 MT threads add them up.
+// Two step shapes (the MFMA contracts over any 32 indices, as long as both
+// operands use the same ones):
+//   narrow steps: step s covers indices 32 s .. 32 s + 31, lane group g the 8
+//     at 32 s + 8 g; four steps' loads in flight per wave;
+//   wide steps (K a multiple of 128, up to 8192): step s covers 128 indices,
+//     lane group g reads the 64 contiguous bytes at 128 s + 32 g and feeds
+//     them to four MFMAs.
+// Maps with few workgroups also split the contraction over KS workgroups
+// (grid z) when the caller gives a workspace: each writes its fp32 partial
+// sums, and a second kernel adds the KS slices in a fixed order, adds the
+// residual and rounds once. MT = 2 (two 16-feature tiles on each weight
+// step, so each workgroup reads the activations once for twice the features)
+// for wide outputs.
+// Measured at 32 tokens (HIP-graph replays of 20 calls, us per call):
+//   Wdkv 7168 -> 512: 23.3 narrow -> 9.3 wide, KS = 6
+//   Wkr 7168 -> 64: 23.2 narrow -> ~9 wide, KS = 16-18
+//   Wdq 7168 -> 1536: 23.6 narrow -> 12.1 wide, MT = 2, KS = 4
+//   Wuq 1536 -> 16384: 19.1 narrow -> 17.8 wide; Wqr 1536 -> 8192: 10.0 -> 8.5
+//   Wo 16384 -> 7168: 59.3 narrow, MT = 2 (76.7 wide, hence the K bound)
 // The output is computed transposed, y^T = W x^T: lane results are
 // consecutive features of one token.
 #include "common.h"
@@ -27,48 +39,79 @@ namespace mla {
 
 constexpr int LIN_N = 32;      // tokens per workgroup (two 16-token MFMA tiles)
 constexpr int LIN_WAVES = 16;  // waves per workgroup, each a slice of the contraction
-constexpr int LIN_U = 4;       // steps per wave whose loads are in flight together
+constexpr int LIN_U = 4;       // narrow steps per wave whose loads are in flight together
 
-// x [N][K], w [M][K], r and y [N][M], all bf16. K is a multiple of 32 and M
-// of 4. Rows past the last feature or token load a valid row (clamped); their
-// results are not stored.
-template <int LIN_MT>
-__global__ __launch_bounds__(64 * LIN_WAVES) void linear_kernel(const uint16_t* __restrict__ x,
-                                                                const uint16_t* __restrict__ w,
-                                                                const uint16_t* r, uint16_t* y, int N,
-                                                                int K, int M) {
+// x [N][K], w [M][K], r and y [N][M], all bf16; ws [KS][N][M] fp32 when
+// SPLIT. K is a multiple of the step width (32 or 128) and M of 4; split z
+// takes steps [z S / KS, (z + 1) S / KS), never empty (KS <= S). Rows past
+// the last feature or token load a valid row (clamped); their results are
+// not stored.
+template <int LIN_MT, bool WIDE, bool SPLIT>
+__global__ __launch_bounds__(64 * LIN_WAVES) __attribute__((amdgpu_waves_per_eu(4, 4))) void linear_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* r, uint16_t* y, float* ws,
+    int N, int K, int M, int KS) {
   constexpr int LIN_M = 16 * LIN_MT;   // output features per workgroup
+  constexpr int STEP = WIDE ? 128 : 32;
   __shared__ float part[LIN_WAVES][8 * LIN_MT][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
-  const int m0 = blockIdx.x * LIN_M, n0 = blockIdx.y * LIN_N;
-  // A = W rows m0 + 16 mt + c, features 32 s + 8 g .. +7; B = x^T of tokens n0 + 16 t + c
+  const int m0 = blockIdx.x * LIN_M, n0 = blockIdx.y * LIN_N, z = blockIdx.z;
+  const int S = K / STEP;
+  const int s_lo = (int)((int64_t)z * S / KS), s_hi = (int)((int64_t)(z + 1) * S / KS);
+  // A = W rows m0 + 16 mt + c; B = x^T of tokens n0 + 16 t + c; lane group g's
+  // first index within a step
+  const int goff = WIDE ? 32 * g : 8 * g;
   const uint16_t* wa[LIN_MT];
 #pragma unroll
-  for (int mt = 0; mt < LIN_MT; ++mt) wa[mt] = w + (int64_t)min(m0 + 16 * mt + c, M - 1) * K + 8 * g;
-  const uint16_t* xb0 = x + (int64_t)min(n0 + c, N - 1) * K + 8 * g;
-  const uint16_t* xb1 = x + (int64_t)min(n0 + 16 + c, N - 1) * K + 8 * g;
-  const int S = K / 32;
+  for (int mt = 0; mt < LIN_MT; ++mt) wa[mt] = w + (int64_t)min(m0 + 16 * mt + c, M - 1) * K + goff;
+  const uint16_t* xb0 = x + (int64_t)min(n0 + c, N - 1) * K + goff;
+  const uint16_t* xb1 = x + (int64_t)min(n0 + 16 + c, N - 1) * K + goff;
   // two accumulators per token tile, alternating, so consecutive MFMAs do
   // not wait on each other's results
   f32x4 acc[LIN_MT][2][2] = {};
-  for (int base = wave; base < S; base += LIN_WAVES * LIN_U) {
-    u32x4 a[LIN_U][LIN_MT], b0[LIN_U], b1[LIN_U];
+  if constexpr (WIDE) {
+    for (int ss = s_lo + wave; ss < s_hi; ss += LIN_WAVES) {
+      u32x4 a[LIN_MT][4], b0[4], b1[4];
 #pragma unroll
-    for (int u = 0; u < LIN_U; ++u) {
-      const int ss = min(base + LIN_WAVES * u, S - 1);   // past the end: a valid step, not accumulated
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int mt = 0; mt < LIN_MT; ++mt) a[u][mt] = *(const u32x4*)(wa[mt] + 32 * ss);
-      b0[u] = *(const u32x4*)(xb0 + 32 * ss);
-      b1[u] = *(const u32x4*)(xb1 + 32 * ss);
-    }
+        for (int mt = 0; mt < LIN_MT; ++mt) a[mt][j] = *(const u32x4*)(wa[mt] + STEP * ss + 8 * j);
+        b0[j] = *(const u32x4*)(xb0 + STEP * ss + 8 * j);
+        b1[j] = *(const u32x4*)(xb1 + STEP * ss + 8 * j);
+      }
 #pragma unroll
-    for (int u = 0; u < LIN_U; ++u) {
-      if (base + LIN_WAVES * u < S) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int mt = 0; mt < LIN_MT; ++mt) {
-          acc[mt][0][u & 1] = mfma16x16x32(as_bf16x8(a[u][mt]), as_bf16x8(b0[u]), acc[mt][0][u & 1]);
-          acc[mt][1][u & 1] = mfma16x16x32(as_bf16x8(a[u][mt]), as_bf16x8(b1[u]), acc[mt][1][u & 1]);
+          acc[mt][0][j & 1] = mfma16x16x32(as_bf16x8(a[mt][j]), as_bf16x8(b0[j]), acc[mt][0][j & 1]);
+          acc[mt][1][j & 1] = mfma16x16x32(as_bf16x8(a[mt][j]), as_bf16x8(b1[j]), acc[mt][1][j & 1]);
+        }
+    }
+  } else {
+    for (int base = s_lo + wave; base < s_hi; base += LIN_WAVES * LIN_U) {
+      u32x4 a[LIN_U][LIN_MT], b0[LIN_U], b1[LIN_U];
+#pragma unroll
+      for (int u = 0; u < LIN_U; ++u) {
+        const int ss = min(base + LIN_WAVES * u, s_hi - 1);   // past the end: a valid step, not accumulated
+#pragma unroll
+        for (int mt = 0; mt < LIN_MT; ++mt) a[u][mt] = *(const u32x4*)(wa[mt] + STEP * ss);
+        b0[u] = *(const u32x4*)(xb0 + STEP * ss);
+        b1[u] = *(const u32x4*)(xb1 + STEP * ss);
+      }
+      // Every product is issued; a step past the end multiplies zeros (both
+      // operands, so an inf in the clamped step's values adds nothing). A
+      // branch here would let the compiler split the loads over the branches
+      // and wait for each group in turn.
+#pragma unroll
+      for (int u = 0; u < LIN_U; ++u) {
+        const bool live = base + LIN_WAVES * u < s_hi;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const u32x4 x0 = live ? b0[u] : zero, x1 = live ? b1[u] : zero;
+#pragma unroll
+        for (int mt = 0; mt < LIN_MT; ++mt) {
+          const u32x4 wv = live ? a[u][mt] : zero;
+          acc[mt][0][u & 1] = mfma16x16x32(as_bf16x8(wv), as_bf16x8(x0), acc[mt][0][u & 1]);
+          acc[mt][1][u & 1] = mfma16x16x32(as_bf16x8(wv), as_bf16x8(x1), acc[mt][1][u & 1]);
         }
       }
     }
@@ -95,23 +138,88 @@ __global__ __launch_bounds__(64 * LIN_WAVES) void linear_kernel(const uint16_t* 
   const int n = n0 + 16 * t + (l & 15), m = m0 + 16 * mt + 4 * (l >> 4) + 2 * p;
   if (n >= N || m >= M) return;
   const int64_t off = (int64_t)n * M + m;
+  if constexpr (SPLIT) {
+    *(float2*)(ws + (int64_t)z * N * M + off) = float2{s0, s1};
+  } else {
+    if (r) {
+      const uint32_t rv = *(const uint32_t*)(r + off);
+      s0 += bf16_to_f32((uint16_t)(rv & 0xffffu));
+      s1 += bf16_to_f32((uint16_t)(rv >> 16));
+    }
+    *(uint32_t*)(y + off) = pack_bf16x2(s0, s1);
+  }
+}
+
+// y = sum over z of ws[z] (z = 0, 1, ... in order) + r, one rounding; two
+// features per thread. r may alias y (each element is read before it is
+// written, by the same thread).
+__global__ __launch_bounds__(256) void linear_reduce_kernel(const float* ws, const uint16_t* r, uint16_t* y,
+                                                            int64_t NM, int KS) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+  if (i >= NM) return;
+  float s0 = 0.f, s1 = 0.f;
+  for (int z = 0; z < KS; ++z) {
+    const float2 v = *(const float2*)(ws + z * NM + i);
+    s0 += v.x;
+    s1 += v.y;
+  }
   if (r) {
-    const uint32_t rv = *(const uint32_t*)(r + off);
+    const uint32_t rv = *(const uint32_t*)(r + i);
     s0 += bf16_to_f32((uint16_t)(rv & 0xffffu));
     s1 += bf16_to_f32((uint16_t)(rv >> 16));
   }
-  *(uint32_t*)(y + off) = pack_bf16x2(s0, s1);
+  *(uint32_t*)(y + i) = pack_bf16x2(s0, s1);
 }
 
-hipError_t launch_linear(const uint16_t* x, const uint16_t* w, const uint16_t* r, uint16_t* y,
-                         int32_t N, int32_t K, int32_t M, hipStream_t stream) {
-  const unsigned ny = (unsigned)((N + LIN_N - 1) / LIN_N);
-  const unsigned nx2 = (unsigned)((M + 31) / 32);
-  if ((int64_t)nx2 * ny >= 128) {
-    hipLaunchKernelGGL(linear_kernel<2>, dim3(nx2, ny), dim3(64 * LIN_WAVES), 0, stream, x, w, r, y, N, K, M);
+LinearPlan plan_linear(int32_t N, int32_t K, int32_t M) {
+  LinearPlan p;
+  const int64_t ny = (N + LIN_N - 1) / LIN_N;
+  p.wide = K % 128 == 0 && K <= 8192;
+  if (!p.wide) {
+    // narrow steps: MT = 2 when that still leaves >= 128 workgroups
+    p.mt = ((int64_t)((M + 31) / 32) * ny >= 128) ? 2 : 1;
+    p.ks = 1;
   } else {
-    const dim3 grid((unsigned)((M + 15) / 16), ny);
-    hipLaunchKernelGGL(linear_kernel<1>, grid, dim3(64 * LIN_WAVES), 0, stream, x, w, r, y, N, K, M);
+    p.mt = M >= 1024 ? 2 : 1;
+    const int64_t nwg = (int64_t)((M + 16 * p.mt - 1) / (16 * p.mt)) * ny;
+    p.ks = 1;
+    if (nwg < 128) {
+      // about 192 workgroups, each split keeping at least three steps
+      const int64_t want = (192 + nwg - 1) / nwg, most = (K / 128) / 3;
+      p.ks = (int)std::max<int64_t>(1, std::min(want, most));
+    }
+  }
+  p.ws_bytes = p.ks > 1 ? (size_t)p.ks * (size_t)N * (size_t)M * sizeof(float) : 0;
+  return p;
+}
+
+template <int MT, bool WIDE>
+static void launch_linear_t(const uint16_t* x, const uint16_t* w, const uint16_t* r, uint16_t* y, float* ws,
+                            int32_t N, int32_t K, int32_t M, int ks, hipStream_t stream) {
+  const dim3 grid((unsigned)((M + 16 * MT - 1) / (16 * MT)), (unsigned)((N + LIN_N - 1) / LIN_N), (unsigned)ks);
+  if (ks == 1) {
+    hipLaunchKernelGGL((linear_kernel<MT, WIDE, false>), grid, dim3(64 * LIN_WAVES), 0, stream, x, w, r, y,
+                       nullptr, N, K, M, 1);
+  } else {
+    hipLaunchKernelGGL((linear_kernel<MT, WIDE, true>), grid, dim3(64 * LIN_WAVES), 0, stream, x, w, r, y, ws,
+                       N, K, M, ks);
+    const int64_t NM = (int64_t)N * M;
+    hipLaunchKernelGGL(linear_reduce_kernel, dim3((unsigned)((NM / 2 + 255) / 256)), dim3(256), 0, stream, ws, r,
+                       y, NM, ks);
+  }
+}
+
+hipError_t launch_linear(const uint16_t* x, const uint16_t* w, const uint16_t* r, uint16_t* y, void* workspace,
+                         size_t workspace_bytes, int32_t N, int32_t K, int32_t M, hipStream_t stream) {
+  LinearPlan p = plan_linear(N, K, M);
+  if (p.ks > 1 && (workspace == nullptr || workspace_bytes < p.ws_bytes)) p.ks = 1;   // no room: unsplit
+  float* ws = (float*)workspace;
+  if (p.wide) {
+    if (p.mt == 2) launch_linear_t<2, true>(x, w, r, y, ws, N, K, M, p.ks, stream);
+    else launch_linear_t<1, true>(x, w, r, y, ws, N, K, M, p.ks, stream);
+  } else {
+    if (p.mt == 2) launch_linear_t<2, false>(x, w, r, y, ws, N, K, M, 1, stream);
+    else launch_linear_t<1, false>(x, w, r, y, ws, N, K, M, 1, stream);
   }
   return hipGetLastError();
 }

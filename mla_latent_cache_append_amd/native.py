@@ -65,7 +65,8 @@ _SIG = {
     "mla_decode_attn_fp8": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I64, _P, _I32, _P, _I32,
                                            _I32, _P, _P, _P, ctypes.c_size_t, _P]),
     "mla_out_up": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I32, _P]),
-    "mla_linear": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "mla_linear_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "mla_linear": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -257,8 +258,14 @@ def mla_out_up(dims: MlaDims, o_lat, w_uv, o, stream=None):
         ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), _ptr(o), N, _stream(stream)))
 
 
-def mla_linear(x, w, y, residual=None, stream=None):
-    """y[n] = W x[n] (+ residual[n]); x [N, K], w [M, K], y [N, M] bf16."""
+def mla_linear_workspace_size(N: int, K: int, M: int) -> int:
+    return int(lib().mla_linear_workspace_size(int(N), int(K), int(M)))
+
+
+def mla_linear(x, w, y, residual=None, workspace=None, stream=None):
+    """y[n] = W x[n] (+ residual[n]); x [N, K], w [M, K], y [N, M] bf16.
+    ``workspace`` (uint8, optional): with mla_linear_workspace_size(N, K, M)
+    bytes or more the contraction is split over more workgroups."""
     N, K = x.shape
     M = w.shape[0]
     _check("x", x, torch.bfloat16, (N, K))
@@ -266,7 +273,10 @@ def mla_linear(x, w, y, residual=None, stream=None):
     _check("y", y, torch.bfloat16, (N, M))
     if residual is not None:
         _check("residual", residual, torch.bfloat16, (N, M))
-    _ok("mla_linear", lib().mla_linear(_ptr(x), _ptr(w), _ptr(residual), _ptr(y), N, K, M, _stream(stream)))
+    if workspace is not None:
+        _check("workspace", workspace, torch.uint8)
+    _ok("mla_linear", lib().mla_linear(_ptr(x), _ptr(w), _ptr(residual), _ptr(y), N, K, M, _ptr(workspace),
+                                       workspace.numel() if workspace is not None else 0, _stream(stream)))
 
 
 def default_scale() -> float:

@@ -101,10 +101,11 @@ class LayerStep:
         h_out = h + Wo [o_0 | ... | o_{H-1}]
 
     Weights are [out, in] bf16 device tensors; every product runs in
-    ``mla_linear`` (the residual add is fused into the last one). The maps
-    that do not depend on each other run on side streams: Wdkv and Wkr each
-    beside Wdq, then Wqr beside Wuq (narrow maps fill a few workgroups each,
-    so side by side they share the chip); the decode waits for all of them."""
+    ``mla_linear`` (the residual add is fused into the last one); each map
+    has its own slice of one workspace, so maps with few output tiles split
+    their contraction over more workgroups. The maps that do not depend on
+    each other run on side streams: Wdkv and Wkr each beside Wdq, then Wqr
+    beside Wuq; the decode waits for all of them."""
 
     def __init__(self, decode: DecodeStep, w_dq, w_uq, w_qr, w_dkv, w_kr, w_o, device="cuda"):
         self.decode = decode
@@ -124,6 +125,17 @@ class LayerStep:
         self.c_kv = torch.empty(N, nat.D_C, **bf)
         self.k_pe = torch.empty(N, nat.D_ROPE, **bf)
         self.out = torch.empty(N, d_model, **bf)
+        # one workspace, a 256-byte-aligned slice per map: maps on different
+        # streams run at the same time and must not share partial sums
+        shapes = {"dkv": (d_model, nat.D_C), "kr": (d_model, nat.D_ROPE), "dq": (d_model, d_cq),
+                  "uq": (d_cq, H * nat.D_NOPE), "qr": (d_cq, H * nat.D_ROPE), "o": (H * nat.D_V, d_model)}
+        sizes = {k: nat.mla_linear_workspace_size(N, K, M) for k, (K, M) in shapes.items()}
+        offs, total = {}, 0
+        for k, sz in sizes.items():
+            offs[k] = total
+            total += (sz + 255) // 256 * 256
+        self.workspace = torch.empty(max(total, 1), dtype=torch.uint8, device=device)
+        self.ws = {k: (self.workspace[offs[k]:offs[k] + sz] if sz else None) for k, sz in sizes.items()}
         # side streams at the default priority
         self.side_kv = torch.cuda.Stream(device=device)
         self.side_kr = torch.cuda.Stream(device=device)
@@ -135,22 +147,24 @@ class LayerStep:
         self.side_kv.wait_stream(main)
         self.side_kr.wait_stream(main)
         with torch.cuda.stream(self.side_kv):
-            nat.mla_linear(h, self.w_dkv, self.c_kv)
+            nat.mla_linear(h, self.w_dkv, self.c_kv, workspace=self.ws["dkv"])
         with torch.cuda.stream(self.side_kr):
-            nat.mla_linear(h, self.w_kr, self.k_pe)
-        nat.mla_linear(h, self.w_dq, self.qz)
+            nat.mla_linear(h, self.w_kr, self.k_pe, workspace=self.ws["kr"])
+        nat.mla_linear(h, self.w_dq, self.qz, workspace=self.ws["dq"])
         self.side_qr.wait_stream(main)
         with torch.cuda.stream(self.side_qr):
-            nat.mla_linear(self.qz, self.w_qr, self.q_pe.view(N, -1))
-        nat.mla_linear(self.qz, self.w_uq, self.q_nope.view(N, -1))
+            nat.mla_linear(self.qz, self.w_qr, self.q_pe.view(N, -1), workspace=self.ws["qr"])
+        nat.mla_linear(self.qz, self.w_uq, self.q_nope.view(N, -1), workspace=self.ws["uq"])
         main.wait_stream(self.side_kv)
         main.wait_stream(self.side_kr)
         main.wait_stream(self.side_qr)
         self.decode(self.c_kv, self.k_pe, self.q_nope, self.q_pe, q_pos, slots)
-        nat.mla_linear(self.decode.o.view(N, -1), self.w_o, self.out, residual=h)
+        nat.mla_linear(self.decode.o.view(N, -1), self.w_o, self.out, residual=h, workspace=self.ws["o"])
         return self.out
 
-    def capture(self, h, q_pos, slots):
-        """Record the whole layer (ten kernels) as a HIP graph over these
-        input tensors; replay() reruns it on whatever they then hold."""
-        return _capture(self, h, q_pos, slots)
+    def capture(self, h, q_pos, slots, reps: int = 1):
+        """Record ``reps`` whole layers in a row as one HIP graph over these
+        input tensors; replay() reruns them on whatever they then hold (the
+        layer rewrites the same cache rows and outputs, so a repeat gives
+        the same result)."""
+        return _capture(self, h, q_pos, slots, reps=reps)

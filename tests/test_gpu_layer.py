@@ -29,8 +29,17 @@ def _lib():
     (1, 32, 4, True), (200, 512, 64, False),
     # wide maps take 32 features per workgroup (at least 128 workgroups): even and ragged M, ragged N
     (32, 1024, 8192, True), (40, 512, 4100, False),
+    # the 128-head layer's narrow maps (contraction split over 6, 18 and 4 slices with a workspace),
+    # a ragged token count, and a contraction past 8192 (32-wide steps)
+    (32, 7168, 512, False), (32, 7168, 64, True), (32, 7168, 1536, True), (19, 4096, 256, True),
+    (3, 16384, 1024, True),
 ], ids=lambda v: str(v))
 def test_linear_matches_oracle(N, K, M, resid):
+    """Unsplit (no workspace) and, where the map splits, split (workspace of
+    mla_linear_workspace_size bytes, filled with 0xff first): both against
+    the fp64 oracle; the split call repeated gives the same bits; a workspace
+    one slice short gives the unsplit bits; in place (residual = output)
+    gives the same bits as out of place."""
     from mla_latent_cache_append_amd import native as nat
     print(f"\n[case] linear N={N} K={K} M={M} residual={resid}", flush=True)
     x = workloads.normal_bf16((7, 1, N, K), (N, K))
@@ -38,15 +47,36 @@ def test_linear_matches_oracle(N, K, M, resid):
     r = workloads.normal_bf16((7, 3, N, M), (N, M)) if resid else None
     f = orc.bf16_bits_to_f64
     ref = orc.linear(f(x), f(w)) + (f(r) if resid else 0.0)
-    y = torch.full((N, M), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xd, wd = hz.to_dev(x), hz.to_dev(w)
     rd = hz.to_dev(r) if resid else None
-    nat.mla_linear(hz.to_dev(x), hz.to_dev(w), y, residual=rd)
-    torch.cuda.synchronize()
-    hz.assert_parity("linear", hz.f64_of(y), ref)
-    if resid:      # in place: the residual buffer is the output
-        nat.mla_linear(hz.to_dev(x), hz.to_dev(w), rd, residual=rd)
+
+    def run(ws=None, in_place=False):
+        if in_place:
+            out = rd.clone()
+            nat.mla_linear(xd, wd, out, residual=out, workspace=ws)
+        else:
+            out = torch.full((N, M), float("nan"), dtype=torch.bfloat16, device="cuda")
+            nat.mla_linear(xd, wd, out, residual=rd, workspace=ws)
         torch.cuda.synchronize()
-        assert torch.equal(rd.view(torch.int16), y.view(torch.int16))
+        return out
+
+    bits = lambda t: t.view(torch.int16)
+    y = run()
+    hz.assert_parity("linear", hz.f64_of(y), ref)
+    if resid:
+        assert torch.equal(bits(run(in_place=True)), bits(y))
+    nbytes = nat.mla_linear_workspace_size(N, K, M)
+    print(f"  split workspace: {nbytes} bytes", flush=True)
+    if nbytes == 0:
+        return
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    ys = run(ws)
+    hz.assert_parity("linear split", hz.f64_of(ys), ref)
+    assert torch.equal(bits(run(ws)), bits(ys))
+    if resid:
+        assert torch.equal(bits(run(ws, in_place=True)), bits(ys))
+    short = ws[:nbytes - N * M * 4]
+    assert torch.equal(bits(run(short)), bits(y))
 
 
 def test_linear_rejects_unsupported_shapes():
@@ -97,7 +127,7 @@ def test_layer_stack_error_growth():
     for l, st in enumerate(steps):
         _, _, qpos, slot = runs[l].new
         h = st(h, qpos, slot).clone()
-        nat.mla_linear(st.decode.o.view(B, -1), st.w_o, y)
+        nat.mla_linear(st.decode.o.view(B, -1), st.w_o, y, workspace=st.ws["o"])
         gpu_h.append(hz.f64_of(h))
         gpu_y.append(hz.f64_of(y))
     torch.cuda.synchronize()
@@ -112,11 +142,13 @@ def test_layer_stack_error_growth():
         prev_r = ref_h[l]
 
 
-def test_layer_graph_replays_match_eager():
-    """The whole layer (projections, two of them on side streams, decode step,
-    residual output projection) recorded as one HIP graph replays bit for bit
-    to the eager layer, with eager work that overwrites every buffer the layer
-    writes between replays."""
+@pytest.mark.parametrize("reps", [1, 3])
+def test_layer_graph_replays_match_eager(reps):
+    """The whole layer (projections, three of them on side streams, the split
+    ones with their reduce kernels, decode step, residual output projection)
+    recorded as one HIP graph (``reps`` layers in a row) replays bit for bit
+    to the eager layer, with eager work that overwrites every buffer the
+    layer writes between replays."""
     from mla_latent_cache_append_amd.step import LayerStep
     H, d_model, d_cq = 16, 2048, 1536
     w = workloads.Workload("layer_graph", 3, H, 1, [70, 600, 1500], "permuted", seed=300)
@@ -125,15 +157,16 @@ def test_layer_graph_replays_match_eager():
     st = LayerStep(run.step, **{k: hz.to_dev(v) for k, v in lw.items()})
     h = hz.to_dev(workloads.hidden_states(300, w.B, d_model))
     _, _, qpos, slot = run.new
-    print("\n[case] layer graph: H=16, lens [70, 600, 1500]", flush=True)
+    print(f"\n[case] layer graph: H=16, lens [70, 600, 1500], layers per graph {reps}", flush=True)
     eager = st(h, qpos, slot).clone()
     torch.cuda.synchronize()
-    g = st.capture(h, qpos, slot)
+    g = st.capture(h, qpos, slot, reps=reps)
     torch.cuda.synchronize()
     for rep in range(3):
         # every buffer the layer writes, the side-stream projections' included
         for buf in (st.out, st.decode.o, st.c_kv, st.k_pe, st.qz, st.q_nope, st.q_pe):
             buf.fill_(float("nan"))
+        st.workspace.fill_(0xFF)    # the split maps' fp32 partial sums
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()

@@ -31,7 +31,7 @@ def nat():
 def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("mla_cache_append", "mla_absorb_q", "mla_decode_attn", "mla_out_up", "mla_linear",
-              "mla_decode_workspace_size", "mla_status_str", "mla_dims_default"):
+              "mla_linear_workspace_size", "mla_decode_workspace_size", "mla_status_str", "mla_dims_default"):
         assert n in names
 
 
@@ -88,6 +88,54 @@ def test_invalid_arguments_return_status(nat):
     d.softmax_scale = 0.0
     assert lib.mla_out_up(ctypes.byref(d), fake, fake, fake, 1, null) == nat.MLA_ERR_INVALID_ARG
     assert lib.mla_cache_append(None, fake, fake, fake, fake, fake, 4, 1, null) == nat.MLA_ERR_INVALID_ARG
+
+
+def split_slices(N, K, M):
+    """The documented split rule, restated: 128-wide steps need K % 128 == 0
+    and K <= 8192; 32 features per workgroup when M >= 1024; with fewer than
+    128 workgroups the contraction is cut into ceil(192 / workgroups) slices,
+    at most a third of the 128-wide steps."""
+    if K % 128 or K > 8192:
+        return 1
+    mt = 2 if M >= 1024 else 1
+    nwg = -(-M // (16 * mt)) * -(-N // 32)
+    if nwg >= 128:
+        return 1
+    return max(1, min(-(-192 // nwg), (K // 128) // 3))
+
+
+@pytest.mark.parametrize("N,K,M", [(32, 7168, 512), (32, 7168, 64), (32, 7168, 1536), (32, 1536, 16384),
+                                   (32, 16384, 7168), (1, 2048, 2048), (200, 512, 64), (33, 1536, 2048),
+                                   (7, 96, 12), (32, 2048, 512)])
+def test_linear_workspace_size_is_the_split_rule(nat, N, K, M):
+    ks = split_slices(N, K, M)
+    assert nat.mla_linear_workspace_size(N, K, M) == (ks * N * M * 4 if ks > 1 else 0)
+
+
+def test_linear_layer_maps_split_as_measured(nat):
+    # the 128-head layer's narrow maps at 32 tokens: Wdkv 6 slices, Wkr 18, Wdq 4; Wuq, Wqr, Wo unsplit
+    assert nat.mla_linear_workspace_size(32, 7168, 512) == 6 * 32 * 512 * 4
+    assert nat.mla_linear_workspace_size(32, 7168, 64) == 18 * 32 * 64 * 4
+    assert nat.mla_linear_workspace_size(32, 7168, 1536) == 4 * 32 * 1536 * 4
+    for K, M in ((1536, 16384), (1536, 8192), (16384, 7168)):
+        assert nat.mla_linear_workspace_size(32, K, M) == 0
+    # unsupported sizes report no workspace
+    for N, K, M in ((0, 7168, 512), (32, 48, 512), (32, 7168, 6), (65535 * 32 + 1, 128, 4)):
+        assert nat.mla_linear_workspace_size(N, K, M) == 0
+
+
+def test_linear_checks_arguments_on_the_host(nat):
+    lib = nat.lib()
+    P = ctypes.c_void_p
+    fake, null = P(0x1000), P(0)
+    call = lambda x, y, N, K, M, ws, wsb: lib.mla_linear(x, fake, null, y, N, K, M, ws, wsb, null)
+    assert call(null, fake, 32, 7168, 512, null, 0) == nat.MLA_ERR_INVALID_ARG
+    assert call(fake, null, 32, 7168, 512, null, 0) == nat.MLA_ERR_INVALID_ARG
+    assert call(fake, fake, 0, 7168, 512, null, 0) == nat.MLA_ERR_INVALID_ARG
+    assert call(fake, fake, 32, 7168, 512, P(0x1008), 1 << 20) == nat.MLA_ERR_INVALID_ARG   # misaligned
+    assert call(fake, fake, 32, 48, 512, null, 0) == nat.MLA_ERR_UNSUPPORTED
+    assert call(fake, fake, 32, 7168, 6, null, 0) == nat.MLA_ERR_UNSUPPORTED
+    assert call(fake, fake, 65535 * 32 + 1, 7168, 512, null, 0) == nat.MLA_ERR_UNSUPPORTED
 
 
 def test_size_limits_return_unsupported(nat):
