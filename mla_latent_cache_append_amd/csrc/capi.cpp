@@ -171,7 +171,7 @@ int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv
 
 size_t mla_linear_workspace_size(int32_t N, int32_t K, int32_t M) {
   if (N <= 0 || K <= 0 || M <= 0 || K % 32 != 0 || M % 4 != 0 || N > 65535 * 32) return 0;
-  return mla::plan_linear(N, K, M).ws_bytes;
+  return mla::plan_linear(N, K, M, true).ws_bytes;
 }
 
 int mla_linear(const uint16_t* x, const uint16_t* w, const uint16_t* residual, uint16_t* y,

@@ -42,13 +42,16 @@ hipError_t launch_out_up(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* 
 // the number of contraction slices (ks > 1 needs ws_bytes of fp32 workspace).
 struct LinearPlan {
   bool wide;        // 128-wide contraction steps (K % 128 == 0, K <= 8192)
-  int mt;           // 16-feature tiles per workgroup (1 or 2)
+  int mt;           // 16-feature tiles per workgroup (1, 2 or 4)
+  int u;            // 32-wide steps per wave with loads in flight together
   int ks;           // contraction slices, each its own workgroups
   size_t ws_bytes;  // ks * N * M * 4 when ks > 1, else 0
 };
-LinearPlan plan_linear(int32_t N, int32_t K, int32_t M);
+// can_split = false: the best plan with ks = 1 (no workspace).
+LinearPlan plan_linear(int32_t N, int32_t K, int32_t M, bool can_split);
 
-// Splits only when workspace holds at least plan_linear(...).ws_bytes.
+// Splits only when workspace holds at least plan_linear(..., true).ws_bytes;
+// otherwise runs plan_linear(..., false).
 hipError_t launch_linear(const uint16_t* x, const uint16_t* w, const uint16_t* r, uint16_t* y, void* workspace,
                          size_t workspace_bytes, int32_t N, int32_t K, int32_t M, hipStream_t stream);
 

@@ -18,18 +18,27 @@
 //   wide steps (K a multiple of 128, up to 8192): step s covers 128 indices,
 //     lane group g reads the 64 contiguous bytes at 128 s + 32 g and feeds
 //     them to four MFMAs.
+// Features per workgroup (16 MT): each workgroup streams its weight rows and
+// the whole activation block, at a rate per workgroup that sets the time of
+// these maps, so MT = 4 (64 features: half the activation bytes per weight
+// byte of MT = 2) whenever that still leaves >= 224 workgroups; otherwise
+// MT = 2 for wide outputs and MT = 1 for narrow ones.
 // Maps with few workgroups also split the contraction over KS workgroups
 // (grid z) when the caller gives a workspace: each writes its fp32 partial
 // sums, and a second kernel adds the KS slices in a fixed order, adds the
-// residual and rounds once. MT = 2 (two 16-feature tiles on each weight
-// step, so each workgroup reads the activations once for twice the features)
-// for wide outputs.
-// Measured at 32 tokens (HIP-graph replays of 20 calls, us per call):
-//   Wdkv 7168 -> 512: 23.3 narrow -> 9.3 wide, KS = 6
-//   Wkr 7168 -> 64: 23.2 narrow -> ~9 wide, KS = 16-18
-//   Wdq 7168 -> 1536: 23.6 narrow -> 12.1 wide, MT = 2, KS = 4
-//   Wuq 1536 -> 16384: 19.1 narrow -> 17.8 wide; Wqr 1536 -> 8192: 10.0 -> 8.5
-//   Wo 16384 -> 7168: 59.3 narrow, MT = 2 (76.7 wide, hence the K bound)
+// residual and rounds once. A long contraction on narrow steps (K >= 8192)
+// takes MT = 4 with KS = 2 when that reaches 224 workgroups.
+// Measured at 32 tokens (HIP-graph replays of 20 calls, us per call; the
+// first figure is narrow steps, MT = 1 or 2, unsplit):
+//   Wdkv 7168 -> 512: 23.3 -> 9.1 (wide steps, MT = 1, KS = 6)
+//   Wkr 7168 -> 64: 23.2 -> ~9 (wide steps, MT = 1, KS = 18)
+//   Wdq 7168 -> 1536: 23.6 -> 12.1 (wide steps, MT = 2, KS = 4)
+//   Wuq 1536 -> 16384: 19.1 -> 11.8 (narrow steps, MT = 4, three in flight)
+//   Wqr 1536 -> 8192: 10.0 -> 8.5 (wide steps, MT = 2; MT = 4 leaves 128
+//     workgroups: 11.2)
+//   Wo 16384 -> 7168: 59.3 -> 49.1 (narrow steps, MT = 4, KS = 2; unsplit
+//     MT = 4 takes 88.6, so without a workspace it keeps MT = 2; wide
+//     steps take 65-80, hence their bound on K)
 // The output is computed transposed, y^T = W x^T: lane results are
 // consecutive features of one token.
 #include "common.h"
@@ -39,14 +48,14 @@ namespace mla {
 
 constexpr int LIN_N = 32;      // tokens per workgroup (two 16-token MFMA tiles)
 constexpr int LIN_WAVES = 16;  // waves per workgroup, each a slice of the contraction
-constexpr int LIN_U = 4;       // narrow steps per wave whose loads are in flight together
 
 // x [N][K], w [M][K], r and y [N][M], all bf16; ws [KS][N][M] fp32 when
-// SPLIT. K is a multiple of the step width (32 or 128) and M of 4; split z
+// SPLIT. LIN_U narrow steps per wave have their loads in flight together.
+// K is a multiple of the step width (32 or 128) and M of 4; split z
 // takes steps [z S / KS, (z + 1) S / KS), never empty (KS <= S). Rows past
 // the last feature or token load a valid row (clamped); their results are
 // not stored.
-template <int LIN_MT, bool WIDE, bool SPLIT>
+template <int LIN_MT, bool WIDE, bool SPLIT, int LIN_U>
 __global__ __launch_bounds__(64 * LIN_WAVES) __attribute__((amdgpu_waves_per_eu(4, 4))) void linear_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* r, uint16_t* y, float* ws,
     int N, int K, int M, int KS) {
@@ -67,8 +76,10 @@ __global__ __launch_bounds__(64 * LIN_WAVES) __attribute__((amdgpu_waves_per_eu(
   const uint16_t* xb0 = x + (int64_t)min(n0 + c, N - 1) * K + goff;
   const uint16_t* xb1 = x + (int64_t)min(n0 + 16 + c, N - 1) * K + goff;
   // two accumulators per token tile, alternating, so consecutive MFMAs do
-  // not wait on each other's results
-  f32x4 acc[LIN_MT][2][2] = {};
+  // not wait on each other's results (with four feature tiles there are
+  // eight independent chains already, and one each keeps the registers)
+  constexpr int NA = LIN_MT >= 4 ? 1 : 2;
+  f32x4 acc[LIN_MT][2][NA] = {};
   if constexpr (WIDE) {
     for (int ss = s_lo + wave; ss < s_hi; ss += LIN_WAVES) {
       u32x4 a[LIN_MT][4], b0[4], b1[4];
@@ -83,8 +94,8 @@ __global__ __launch_bounds__(64 * LIN_WAVES) __attribute__((amdgpu_waves_per_eu(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int mt = 0; mt < LIN_MT; ++mt) {
-          acc[mt][0][j & 1] = mfma16x16x32(as_bf16x8(a[mt][j]), as_bf16x8(b0[j]), acc[mt][0][j & 1]);
-          acc[mt][1][j & 1] = mfma16x16x32(as_bf16x8(a[mt][j]), as_bf16x8(b1[j]), acc[mt][1][j & 1]);
+          acc[mt][0][j % NA] = mfma16x16x32(as_bf16x8(a[mt][j]), as_bf16x8(b0[j]), acc[mt][0][j % NA]);
+          acc[mt][1][j % NA] = mfma16x16x32(as_bf16x8(a[mt][j]), as_bf16x8(b1[j]), acc[mt][1][j % NA]);
         }
     }
   } else {
@@ -110,8 +121,8 @@ __global__ __launch_bounds__(64 * LIN_WAVES) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int mt = 0; mt < LIN_MT; ++mt) {
           const u32x4 wv = live ? a[u][mt] : zero;
-          acc[mt][0][u & 1] = mfma16x16x32(as_bf16x8(wv), as_bf16x8(x0), acc[mt][0][u & 1]);
-          acc[mt][1][u & 1] = mfma16x16x32(as_bf16x8(wv), as_bf16x8(x1), acc[mt][1][u & 1]);
+          acc[mt][0][u % NA] = mfma16x16x32(as_bf16x8(wv), as_bf16x8(x0), acc[mt][0][u % NA]);
+          acc[mt][1][u % NA] = mfma16x16x32(as_bf16x8(wv), as_bf16x8(x1), acc[mt][1][u % NA]);
         }
       }
     }
@@ -123,7 +134,8 @@ __global__ __launch_bounds__(64 * LIN_WAVES) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[wave][8 * mt + 4 * t + i][lane] = acc[mt][t][0][i] + acc[mt][t][1][i];
+      for (int i = 0; i < 4; ++i)
+        part[wave][8 * mt + 4 * t + i][lane] = NA == 2 ? acc[mt][t][0][i] + acc[mt][t][NA - 1][i] : acc[mt][t][0][i];
   __syncthreads();
   if (threadIdx.x >= 256 * LIN_MT) return;
   // thread (p, mt, t, l): features i = 2p, 2p+1 of slot lane l, feature tile mt, token tile t
@@ -171,21 +183,35 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* ws, con
   *(uint32_t*)(y + i) = pack_bf16x2(s0, s1);
 }
 
-LinearPlan plan_linear(int32_t N, int32_t K, int32_t M) {
+LinearPlan plan_linear(int32_t N, int32_t K, int32_t M, bool can_split) {
   LinearPlan p;
   const int64_t ny = (N + LIN_N - 1) / LIN_N;
-  p.wide = K % 128 == 0 && K <= 8192;
-  if (!p.wide) {
-    // narrow steps: MT = 2 when that still leaves >= 128 workgroups
-    p.mt = ((int64_t)((M + 31) / 32) * ny >= 128) ? 2 : 1;
-    p.ks = 1;
+  auto wgs = [&](int mt) { return (int64_t)((M + 16 * mt - 1) / (16 * mt)) * ny; };
+  p.ks = 1;
+  if (wgs(4) >= 224) {
+    // wide outputs: 64 features per workgroup halve the activation bytes
+    // each workgroup streams per weight byte; all of a wave's steps in one
+    // batch of loads when they fit three
+    p.wide = false;
+    p.mt = 4;
+    p.u = K / 32 <= 3 * LIN_WAVES ? 3 : 2;
+  } else if (K % 128 != 0 || K > 8192) {
+    p.wide = false;
+    if (can_split && K >= 8192 && 2 * wgs(4) >= 224) {
+      p.mt = 4;     // long contraction: 64 features, halves of it on their own workgroups
+      p.ks = 2;
+      p.u = 2;
+    } else {
+      p.mt = wgs(2) >= 128 ? 2 : 1;
+      p.u = 4;
+    }
   } else {
+    p.wide = true;
     p.mt = M >= 1024 ? 2 : 1;
-    const int64_t nwg = (int64_t)((M + 16 * p.mt - 1) / (16 * p.mt)) * ny;
-    p.ks = 1;
-    if (nwg < 128) {
-      // about 192 workgroups, each split keeping at least three steps
-      const int64_t want = (192 + nwg - 1) / nwg, most = (K / 128) / 3;
+    p.u = 1;
+    if (can_split && wgs(p.mt) < 128) {
+      // about 192 workgroups, each slice keeping at least three steps
+      const int64_t want = (192 + wgs(p.mt) - 1) / wgs(p.mt), most = (K / 128) / 3;
       p.ks = (int)std::max<int64_t>(1, std::min(want, most));
     }
   }
@@ -193,15 +219,15 @@ LinearPlan plan_linear(int32_t N, int32_t K, int32_t M) {
   return p;
 }
 
-template <int MT, bool WIDE>
+template <int MT, bool WIDE, int U>
 static void launch_linear_t(const uint16_t* x, const uint16_t* w, const uint16_t* r, uint16_t* y, float* ws,
                             int32_t N, int32_t K, int32_t M, int ks, hipStream_t stream) {
   const dim3 grid((unsigned)((M + 16 * MT - 1) / (16 * MT)), (unsigned)((N + LIN_N - 1) / LIN_N), (unsigned)ks);
   if (ks == 1) {
-    hipLaunchKernelGGL((linear_kernel<MT, WIDE, false>), grid, dim3(64 * LIN_WAVES), 0, stream, x, w, r, y,
+    hipLaunchKernelGGL((linear_kernel<MT, WIDE, false, U>), grid, dim3(64 * LIN_WAVES), 0, stream, x, w, r, y,
                        nullptr, N, K, M, 1);
   } else {
-    hipLaunchKernelGGL((linear_kernel<MT, WIDE, true>), grid, dim3(64 * LIN_WAVES), 0, stream, x, w, r, y, ws,
+    hipLaunchKernelGGL((linear_kernel<MT, WIDE, true, U>), grid, dim3(64 * LIN_WAVES), 0, stream, x, w, r, y, ws,
                        N, K, M, ks);
     const int64_t NM = (int64_t)N * M;
     hipLaunchKernelGGL(linear_reduce_kernel, dim3((unsigned)((NM / 2 + 255) / 256)), dim3(256), 0, stream, ws, r,
@@ -211,15 +237,19 @@ static void launch_linear_t(const uint16_t* x, const uint16_t* w, const uint16_t
 
 hipError_t launch_linear(const uint16_t* x, const uint16_t* w, const uint16_t* r, uint16_t* y, void* workspace,
                          size_t workspace_bytes, int32_t N, int32_t K, int32_t M, hipStream_t stream) {
-  LinearPlan p = plan_linear(N, K, M);
-  if (p.ks > 1 && (workspace == nullptr || workspace_bytes < p.ws_bytes)) p.ks = 1;   // no room: unsplit
+  LinearPlan p = plan_linear(N, K, M, true);
+  if (p.ks > 1 && (workspace == nullptr || workspace_bytes < p.ws_bytes)) p = plan_linear(N, K, M, false);
   float* ws = (float*)workspace;
+  const int ks = p.ks;
   if (p.wide) {
-    if (p.mt == 2) launch_linear_t<2, true>(x, w, r, y, ws, N, K, M, p.ks, stream);
-    else launch_linear_t<1, true>(x, w, r, y, ws, N, K, M, p.ks, stream);
+    if (p.mt == 2) launch_linear_t<2, true, 1>(x, w, r, y, ws, N, K, M, ks, stream);
+    else launch_linear_t<1, true, 1>(x, w, r, y, ws, N, K, M, ks, stream);
+  } else if (p.mt == 4) {
+    if (p.u == 3) launch_linear_t<4, false, 3>(x, w, r, y, ws, N, K, M, ks, stream);
+    else launch_linear_t<4, false, 2>(x, w, r, y, ws, N, K, M, ks, stream);
   } else {
-    if (p.mt == 2) launch_linear_t<2, false>(x, w, r, y, ws, N, K, M, 1, stream);
-    else launch_linear_t<1, false>(x, w, r, y, ws, N, K, M, 1, stream);
+    if (p.mt == 2) launch_linear_t<2, false, 4>(x, w, r, y, ws, N, K, M, ks, stream);
+    else launch_linear_t<1, false, 4>(x, w, r, y, ws, N, K, M, ks, stream);
   }
   return hipGetLastError();
 }

@@ -33,6 +33,9 @@ def _lib():
     # a ragged token count, and a contraction past 8192 (32-wide steps)
     (32, 7168, 512, False), (32, 7168, 64, True), (32, 7168, 1536, True), (19, 4096, 256, True),
     (3, 16384, 1024, True),
+    # 64 features per workgroup: unsplit with three (K = 1536) and two (K = 2048) steps in flight;
+    # a long contraction not a multiple of 128 split in two (ragged M tile, three token tiles)
+    (64, 1536, 7168, False), (64, 2048, 7168, True), (90, 8224, 2420, True),
 ], ids=lambda v: str(v))
 def test_linear_matches_oracle(N, K, M, resid):
     """Unsplit (no workspace) and, where the map splits, split (workspace of

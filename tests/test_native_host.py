@@ -91,33 +91,41 @@ def test_invalid_arguments_return_status(nat):
 
 
 def split_slices(N, K, M):
-    """The documented split rule, restated: 128-wide steps need K % 128 == 0
-    and K <= 8192; 32 features per workgroup when M >= 1024; with fewer than
-    128 workgroups the contraction is cut into ceil(192 / workgroups) slices,
-    at most a third of the 128-wide steps."""
+    """The documented split rule, restated: 64 features per workgroup alone
+    when that gives >= 224 workgroups (unsplit); a contraction that is not a
+    multiple of 128 or longer than 8192 splits in two when K >= 8192 and two
+    halves of 64-feature workgroups reach 224; otherwise 128-wide steps with
+    32 features when M >= 1024 (else 16), cut into ceil(192 / workgroups)
+    slices, at most a third of the 128-wide steps, when fewer than 128
+    workgroups remain."""
+    ny = -(-N // 32)
+    wgs = lambda mt: -(-M // (16 * mt)) * ny
+    if wgs(4) >= 224:
+        return 1
     if K % 128 or K > 8192:
-        return 1
+        return 2 if K >= 8192 and 2 * wgs(4) >= 224 else 1
     mt = 2 if M >= 1024 else 1
-    nwg = -(-M // (16 * mt)) * -(-N // 32)
-    if nwg >= 128:
+    if wgs(mt) >= 128:
         return 1
-    return max(1, min(-(-192 // nwg), (K // 128) // 3))
+    return max(1, min(-(-192 // wgs(mt)), (K // 128) // 3))
 
 
 @pytest.mark.parametrize("N,K,M", [(32, 7168, 512), (32, 7168, 64), (32, 7168, 1536), (32, 1536, 16384),
                                    (32, 16384, 7168), (1, 2048, 2048), (200, 512, 64), (33, 1536, 2048),
-                                   (7, 96, 12), (32, 2048, 512)])
+                                   (7, 96, 12), (32, 2048, 512), (90, 8224, 2420), (64, 1536, 7168),
+                                   (3, 16384, 1024), (32, 8192, 7168)])
 def test_linear_workspace_size_is_the_split_rule(nat, N, K, M):
     ks = split_slices(N, K, M)
     assert nat.mla_linear_workspace_size(N, K, M) == (ks * N * M * 4 if ks > 1 else 0)
 
 
 def test_linear_layer_maps_split_as_measured(nat):
-    # the 128-head layer's narrow maps at 32 tokens: Wdkv 6 slices, Wkr 18, Wdq 4; Wuq, Wqr, Wo unsplit
+    # the 128-head layer's maps at 32 tokens: Wdkv 6 slices, Wkr 18, Wdq 4, Wo 2; Wuq and Wqr unsplit
     assert nat.mla_linear_workspace_size(32, 7168, 512) == 6 * 32 * 512 * 4
     assert nat.mla_linear_workspace_size(32, 7168, 64) == 18 * 32 * 64 * 4
     assert nat.mla_linear_workspace_size(32, 7168, 1536) == 4 * 32 * 1536 * 4
-    for K, M in ((1536, 16384), (1536, 8192), (16384, 7168)):
+    assert nat.mla_linear_workspace_size(32, 16384, 7168) == 2 * 32 * 7168 * 4
+    for K, M in ((1536, 16384), (1536, 8192)):
         assert nat.mla_linear_workspace_size(32, K, M) == 0
     # unsupported sizes report no workspace
     for N, K, M in ((0, 7168, 512), (32, 48, 512), (32, 7168, 6), (65535 * 32 + 1, 128, 4)):
