@@ -103,9 +103,11 @@ class LayerStep:
     Weights are [out, in] bf16 device tensors; every product runs in
     ``mla_linear`` (the residual add is fused into the last one); each map
     has its own slice of one workspace, so maps with few output tiles split
-    their contraction over more workgroups. The maps that do not depend on
-    each other run on side streams: Wdkv and Wkr each beside Wdq, then Wqr
-    beside Wuq; the decode waits for all of them."""
+    their contraction over more workgroups. Wdkv and Wkr run one after the
+    other on a side stream beside Wdq, Wqr and Wuq (the decode waits for
+    both streams); measured against three side streams (Wdkv, Wkr, Wqr each
+    on its own) and against one stream, this is ~5 us per layer faster at
+    128 heads."""
 
     def __init__(self, decode: DecodeStep, w_dq, w_uq, w_qr, w_dkv, w_kr, w_o, device="cuda"):
         self.decode = decode
@@ -136,28 +138,20 @@ class LayerStep:
             total += (sz + 255) // 256 * 256
         self.workspace = torch.empty(max(total, 1), dtype=torch.uint8, device=device)
         self.ws = {k: (self.workspace[offs[k]:offs[k] + sz] if sz else None) for k, sz in sizes.items()}
-        # side streams at the default priority
+        # side stream at the default priority
         self.side_kv = torch.cuda.Stream(device=device)
-        self.side_kr = torch.cuda.Stream(device=device)
-        self.side_qr = torch.cuda.Stream(device=device)
 
     def __call__(self, h, q_pos, slots):
         N = self.decode.N
         main = torch.cuda.current_stream()
         self.side_kv.wait_stream(main)
-        self.side_kr.wait_stream(main)
         with torch.cuda.stream(self.side_kv):
             nat.mla_linear(h, self.w_dkv, self.c_kv, workspace=self.ws["dkv"])
-        with torch.cuda.stream(self.side_kr):
             nat.mla_linear(h, self.w_kr, self.k_pe, workspace=self.ws["kr"])
         nat.mla_linear(h, self.w_dq, self.qz, workspace=self.ws["dq"])
-        self.side_qr.wait_stream(main)
-        with torch.cuda.stream(self.side_qr):
-            nat.mla_linear(self.qz, self.w_qr, self.q_pe.view(N, -1), workspace=self.ws["qr"])
+        nat.mla_linear(self.qz, self.w_qr, self.q_pe.view(N, -1), workspace=self.ws["qr"])
         nat.mla_linear(self.qz, self.w_uq, self.q_nope.view(N, -1), workspace=self.ws["uq"])
         main.wait_stream(self.side_kv)
-        main.wait_stream(self.side_kr)
-        main.wait_stream(self.side_qr)
         self.decode(self.c_kv, self.k_pe, self.q_nope, self.q_pe, q_pos, slots)
         nat.mla_linear(self.decode.o.view(N, -1), self.w_o, self.out, residual=h, workspace=self.ws["o"])
         return self.out

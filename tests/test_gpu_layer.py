@@ -147,7 +147,7 @@ def test_layer_stack_error_growth():
 
 @pytest.mark.parametrize("reps", [1, 3])
 def test_layer_graph_replays_match_eager(reps):
-    """The whole layer (projections, three of them on side streams, the split
+    """The whole layer (projections, two of them on a side stream, the split
     ones with their reduce kernels, decode step, residual output projection)
     recorded as one HIP graph (``reps`` layers in a row) replays bit for bit
     to the eager layer, with eager work that overwrites every buffer the
@@ -166,7 +166,7 @@ def test_layer_graph_replays_match_eager(reps):
     g = st.capture(h, qpos, slot, reps=reps)
     torch.cuda.synchronize()
     for rep in range(3):
-        # every buffer the layer writes, the side-stream projections' included
+        # every buffer the layer writes, the side stream's projections' included
         for buf in (st.out, st.decode.o, st.c_kv, st.k_pe, st.qz, st.q_nope, st.q_pe):
             buf.fill_(float("nan"))
         st.workspace.fill_(0xFF)    # the split maps' fp32 partial sums
