@@ -163,20 +163,30 @@ __global__ __launch_bounds__(64 * LIN_WAVES) __attribute__((amdgpu_waves_per_eu(
 }
 
 // y = sum over z of ws[z] (z = 0, 1, ... in order) + r, one rounding; two
-// features per thread. r may alias y (each element is read before it is
-// written, by the same thread).
+// features per thread. The slices are loaded eight at a time (indices past
+// the last slice reload it and are not added), so a reduce of KS slices
+// waits for ceil(KS / 8) memory round trips instead of KS. r may alias y
+// (each element is read before it is written, by the same thread).
 __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* ws, const uint16_t* r, uint16_t* y,
                                                             int64_t NM, int KS) {
+  constexpr int RB = 8;
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
   if (i >= NM) return;
+  const uint32_t rv = r ? *(const uint32_t*)(r + i) : 0u;   // issued with the first slices
   float s0 = 0.f, s1 = 0.f;
-  for (int z = 0; z < KS; ++z) {
-    const float2 v = *(const float2*)(ws + z * NM + i);
-    s0 += v.x;
-    s1 += v.y;
+  for (int z0 = 0; z0 < KS; z0 += RB) {
+    float2 v[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) v[u] = *(const float2*)(ws + (int64_t)min(z0 + u, KS - 1) * NM + i);
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      if (z0 + u < KS) {
+        s0 += v[u].x;
+        s1 += v[u].y;
+      }
+    }
   }
   if (r) {
-    const uint32_t rv = *(const uint32_t*)(r + i);
     s0 += bf16_to_f32((uint16_t)(rv & 0xffffu));
     s1 += bf16_to_f32((uint16_t)(rv >> 16));
   }
