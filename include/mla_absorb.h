@@ -136,7 +136,9 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t Lq);
  *   o_lat        device [B*Lq][H][512] bf16
  *   lse          device [B*Lq][H] float32, or NULL
  *   workspace    device, at least mla_decode_workspace_size(dims, B, Lq) bytes
- * Lq may be a whole prefill chunk (many new tokens per sequence). Returns
+ * Lq may be a whole prefill chunk (many new tokens per sequence). q, pool,
+ * o_lat and workspace must be 16-byte aligned and lse 4-byte aligned
+ * (MLA_ERR_INVALID_ARG otherwise). Returns
  * MLA_ERR_UNSUPPORTED when H is not a multiple of 16, Lq*H exceeds 2^20, the
  * table spans more than 2^30 keys, or B*ceil(Lq*H/4) exceeds 2^31-1.
  * Device-value handling: a length above max_blocks_per_seq*64 or a block id
@@ -205,10 +207,10 @@ int mla_append_absorb_fp8(const mla_dims* dims, const uint16_t* c_kv, const uint
  * codes stand for, code value x pool_scale of its slot. Scores are formed
  * from the exact code values in bf16 MFMAs and multiplied by the token scale
  * in fp32; probabilities are multiplied by the token scale before their bf16
- * rounding for the weighted sum (the row sum takes them unscaled). Every
- * other argument, the workspace (the same mla_decode_workspace_size), the
- * error codes, the device-value handling and determinism are as for
- * mla_decode_attn.
+ * rounding for the weighted sum (the row sum takes them unscaled). pool8 and
+ * pool_scale must be 16-byte aligned. Every other argument, the workspace
+ * (the same mla_decode_workspace_size), the alignment rules, the error codes,
+ * the device-value handling and determinism are as for mla_decode_attn.
  */
 int mla_decode_attn_fp8(const mla_dims* dims, const uint16_t* q, const uint8_t* pool8,
                         const float* pool_scale, int64_t num_blocks, const int32_t* block_table,

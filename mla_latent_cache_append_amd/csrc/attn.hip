@@ -1136,7 +1136,7 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
                    : OWN_OPS_Q_OUT
                    : [qv] "v"(qv), [qr] "s"(qr), [mb0] "s"(mb0), [rs0] "s"(rs0), [mb1] "s"(mb1), [rs1] "s"(rs1),
                      [mb2] "s"(mb2), [rs2] "s"(rs2), [go] "v"(goff), OWN_OPS_SO
-                   : "m0", "memory");
+                   : "m0", "scc", "memory");
     }
     lds_barrier();                         // every wave's copies of e0 are in the LDS
     k_addr(e0);
@@ -1147,7 +1147,7 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
       asm volatile(OWN_ASM_PRO
                    : OWN_OPS_S_OUT, [mrun] "+v"(m_run), [alpha] "=&v"(alpha), [mref] "=&v"(mref)
                    : OWN_OPS_Q, OWN_OPS_KA, [lr] "v"(lr), [scale] "s"(a.scale_log2)
-                   : OWN_CLOB, "vcc", "memory");
+                   : OWN_CLOB, "vcc", "scc", "memory");
     }
     // Half tile e+3 goes into the stage of e-1; its nine copies are spread
     // over the iteration's instruction sequence, which keeps the vector
@@ -1177,7 +1177,7 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
                  [mref] "+v"(mref)                                                                    \
                : OWN_OPS_Q, OWN_OPS_KA, OWN_OPS_VA, [lr] "v"(lr), [scale] "s"(a.scale_log2),          \
                  [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO                               \
-               : OWN_CLOB, "vcc", "m0", "memory")
+               : OWN_CLOB, "vcc", "m0", "scc", "memory")
       if constexpr (FIRST)
         OWN_ITER(OWN_ASM_IT_FIRST, OWN_OPS_O_OUT);
       else

@@ -21,6 +21,16 @@ int check_dims(const mla_dims* d) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
 
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// The attention kernels move 16 bytes per lane through q, the cache, o_lat
+// and the workspace, and read token scales four at a time.
+bool attn_aligned(const void* q, const void* pool, const void* pool_scale, const void* o_lat,
+                  const float* lse, const void* workspace) {
+  return aligned(q, 16) && aligned(pool, 16) && aligned(pool_scale, 16) && aligned(o_lat, 16) &&
+         aligned(lse, 4) && aligned(workspace, 16);
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +94,7 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
   if (!q || !pool || !block_table || !seq_lens || !o_lat || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || B <= 0 || Lq <= 0)
     return MLA_ERR_INVALID_ARG;
+  if (!attn_aligned(q, pool, nullptr, o_lat, lse, workspace)) return MLA_ERR_INVALID_ARG;
   // rows of one sequence index 32-bit offsets inside the kernels
   if ((int64_t)Lq * dims->num_heads > (1 << 20) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
     return MLA_ERR_UNSUPPORTED;
@@ -149,6 +160,7 @@ int mla_decode_attn_fp8(const mla_dims* dims, const uint16_t* q, const uint8_t* 
   if (!q || !pool8 || !pool_scale || !block_table || !seq_lens || !o_lat || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || B <= 0 || Lq <= 0)
     return MLA_ERR_INVALID_ARG;
+  if (!attn_aligned(q, pool8, pool_scale, o_lat, lse, workspace)) return MLA_ERR_INVALID_ARG;
   if ((int64_t)Lq * dims->num_heads > (1 << 20) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
     return MLA_ERR_UNSUPPORTED;
   if ((int64_t)B * (((int64_t)Lq * dims->num_heads + 3) / 4) > 0x7fffffff) return MLA_ERR_UNSUPPORTED;

@@ -12,7 +12,6 @@ ABI takes as uint16_t).
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -277,7 +276,3 @@ def mla_linear(x, w, y, residual=None, workspace=None, stream=None):
         _check("workspace", workspace, torch.uint8)
     _ok("mla_linear", lib().mla_linear(_ptr(x), _ptr(w), _ptr(residual), _ptr(y), N, K, M, _ptr(workspace),
                                        workspace.numel() if workspace is not None else 0, _stream(stream)))
-
-
-def default_scale() -> float:
-    return 1.0 / math.sqrt(D_NOPE + D_ROPE)

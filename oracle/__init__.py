@@ -16,8 +16,10 @@ Sources (cited by title and section throughout):
 
 Every function in :mod:`oracle.mla` is pinned by ``tests/test_oracle_*.py``
 against facts the pages or mathematics fix (printed byte counts, the
-absorption identity, a library SDPA, brute force, closed forms). Parity is
-pinned for every function; no function here is "parity unpinned". The
+absorption identity, a library SDPA, brute force, closed forms), and the
+input decoder ``bf16_bits_to_f64`` against torch's bfloat16 -> float64
+conversion on all 65,536 bit patterns (``tests/test_oracle_decode_inputs.py``,
+with a planted binary16 misreading it must catch). The
 real-weight error tables of [AUDIT] §5 are the only page figures this oracle
 cannot reproduce (the checkpoint and prompt are not available), and nothing
 here claims to.

@@ -217,3 +217,25 @@ def test_probe_library_exports_its_two_probes(nat):
     lib = ctypes.CDLL(build.PROBE_LIB)
     for n in ("mla_probe_stream_read", "mla_probe_mfma"):
         assert hasattr(lib, n), n
+
+
+def test_attention_calls_reject_misaligned_buffers(nat):
+    """q, pool, o_lat and the workspace carry 16-byte accesses in the kernels
+    (pool_scale too for the FP8 call), lse 4-byte ones: a misaligned pointer is
+    an invalid argument, caught on the host before any launch."""
+    lib = nat.lib()
+    d = nat.mla_dims_default(16)
+    P = ctypes.c_void_p
+    ok, odd, null = P(0x1000), P(0x1008), P(0)
+    big = 1 << 30
+
+    def attn(q=ok, pool=ok, o=ok, lse=null, ws=ok):
+        return lib.mla_decode_attn(ctypes.byref(d), q, pool, 4, ok, 2, ok, 2, 1, o, lse, ws, big, null)
+
+    def attn8(q=ok, pool=ok, sc=ok, o=ok, lse=null, ws=ok):
+        return lib.mla_decode_attn_fp8(ctypes.byref(d), q, pool, sc, 4, ok, 2, ok, 2, 1, o, lse, ws, big, null)
+
+    for kw in ({"q": odd}, {"pool": odd}, {"o": odd}, {"ws": odd}, {"lse": P(0x1002)}):
+        assert attn(**kw) == nat.MLA_ERR_INVALID_ARG, kw
+        assert attn8(**kw) == nat.MLA_ERR_INVALID_ARG, kw
+    assert attn8(sc=odd) == nat.MLA_ERR_INVALID_ARG
