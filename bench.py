@@ -41,8 +41,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="v3_b32_h128_l16384")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cache", choices=("bf16", "fp8"), default="bf16",
-                    help="latent cache format: bf16 rows, or E4M3 codes with one fp32 scale per token")
+    ap.add_argument("--cache", choices=("bf16", "fp8", "kvpe"), default="bf16",
+                    help="latent cache: the paged pool of bf16 rows, the paged pool of E4M3 codes with one "
+                         "fp32 scale per token, or the two-buffer bf16 layout kv_cache [B, max_seq, 512] + "
+                         "pe_cache [B, max_seq, 64]")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -308,14 +310,30 @@ def main():
     # ---- setup (untimed): weights, paged pool filled through mla_cache_append
     wuk, wuv = w.weights()
     fp8 = args.cache == "fp8"
-    pool = torch.empty((w.num_blocks, 64, 576), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    kvpe = args.cache == "kvpe"
+    pe_cache = None
+    if kvpe:
+        # two-buffer layout: room for the longest sequence in every row of the batch
+        max_seq = int(w.lens.max())
+        pool = torch.empty((w.B, max_seq, 512), dtype=torch.bfloat16, device=dev)
+        pe_cache = torch.empty((w.B, max_seq, 64), dtype=torch.bfloat16, device=dev)
+    else:
+        pool = torch.empty((w.num_blocks, 64, 576), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
     pool_scale = torch.empty((w.num_blocks, 64), dtype=torch.float32, device=dev) if fp8 else None
     block_table = torch.from_numpy(w.block_table).to(dev)
     seq_lens = torch.from_numpy(w.lens.astype(np.int32)).to(dev)
-    step = DecodeStep(w.H, w.B, w.Lq, pool, block_table, seq_lens, to_dev(wuk), to_dev(wuv), pool_scale=pool_scale)
+    step = DecodeStep(w.H, w.B, w.Lq, pool, block_table, seq_lens, to_dev(wuk), to_dev(wuv), pool_scale=pool_scale,
+                      pe_cache=pe_cache)
+
+    def slots_of(b, p):
+        """Where positions p of sequence b go: pool slots, or (two-buffer
+        layout) the sequence index of each token."""
+        p = np.asarray(p)
+        return np.full(p.shape, b, np.int32) if kvpe else w.slots(b, p)
+
     new_ckv = np.zeros((w.N, 512), np.uint16)
     new_kpe = np.zeros((w.N, 64), np.uint16)
-    new_slot = np.zeros(w.N, np.int64)
+    new_slot = np.zeros(w.N, np.int32 if kvpe else np.int64)
     fill_events = 0.0
     t_fill = time.perf_counter()
     for b in range(w.B):
@@ -327,7 +345,7 @@ def main():
             p = np.arange(s0, s1)
             c, k = to_dev(ckv[s0:s1]), to_dev(kpe[s0:s1])
             pos = torch.from_numpy(p.astype(np.int32)).to(dev)
-            sl = torch.from_numpy(w.slots(b, p)).to(dev)
+            sl = torch.from_numpy(slots_of(b, p)).to(dev)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             step.append(c, k, pos, sl)
@@ -337,7 +355,7 @@ def main():
         for i in range(w.Lq):
             p = L - w.Lq + i
             n = b * w.Lq + i
-            new_ckv[n], new_kpe[n], new_slot[n] = ckv[p], kpe[p], w.slots(b, [p])[0]
+            new_ckv[n], new_kpe[n], new_slot[n] = ckv[p], kpe[p], slots_of(b, [p])[0]
         if b % 8 == 0:
             print(f"[bench] filled sequence {b}/{w.B}", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -388,19 +406,21 @@ def main():
     # the step's first two calls fused into one launch (what the captured step
     # runs): 20 launches recorded as one HIP graph (so host overhead stays out),
     # replayed five times between two events
-    fused_graph = _capture_graph(torch, lambda: [nat.mla_append_absorb(
-        step.dims, ckv_n, kpe_n, slot_n, step.pool, qn, qp, qpos, step.w_uk, step.q,
-        pool_scale=step.pool_scale) for _ in range(20)])
-    fused = []
-    for _ in range(5):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        fused_graph.replay()
-        e1.record()
-        e1.synchronize()
-        fused.append(e0.elapsed_time(e1) * 1e3 / 20)
-    fused_us = float(np.median(fused))
-    del fused_graph
+    fused_us = None
+    if not kvpe:   # the two-buffer step runs append and absorb as two launches
+        fused_graph = _capture_graph(torch, lambda: [nat.mla_append_absorb(
+            step.dims, ckv_n, kpe_n, slot_n, step.pool, qn, qp, qpos, step.w_uk, step.q,
+            pool_scale=step.pool_scale) for _ in range(20)])
+        fused = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fused_graph.replay()
+            e1.record()
+            e1.synchronize()
+            fused.append(e0.elapsed_time(e1) * 1e3 / 20)
+        fused_us = float(np.median(fused))
+        del fused_graph
 
     # the attention call in steady state: 20 back-to-back calls recorded as
     # one HIP graph, replayed; per call = replay time / 20. No host work sits
@@ -503,9 +523,10 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq,
                    "keys_per_seq": int(w.lens.max()) if w.lens.min() == w.lens.max() else "ragged",
                    "total_keys": int(w.lens.sum()), "block_table": w.table_kind, "seed": args.seed,
-                   "cache": "fp8-e4m3 (per-token fp32 scale)" if fp8 else "bf16"},
+                   "cache": "fp8-e4m3 (per-token fp32 scale)" if fp8 else
+                            "bf16 two-buffer kv_cache + pe_cache" if kvpe else "bf16"},
         "roofline": dict(roof, traffic=traffic,
-                         kernel=("mla_decode_attn_fp8" if fp8 else "mla_decode_attn")
+                         kernel=("mla_decode_attn_fp8" if fp8 else "mla_decode_attn_kvpe" if kvpe else "mla_decode_attn")
                          + " call (split kernel + combine kernel)",
                          algorithmic_bytes_per_launch=alg["attn_bytes"],
                          algorithmic_flops_per_launch=alg["attn_flops"],
@@ -528,8 +549,9 @@ def main():
         "cold_cache": {"steps": args.cold_steps,
                        "call_us_median": {n: float(np.median(v)) for n, v in cold.items()},
                        "decode_attn_GBps": alg["attn_bytes"] / (float(np.median(cold["decode_attn"])) * 1e-6) / 1e9},
-        "step_mode": f"hip_graph replays of {spg} whole steps per graph, append and absorb fused in one "
-                     "launch (eager per-call events give call_us_median)",
+        "step_mode": f"hip_graph replays of {spg} whole steps per graph, append and absorb "
+                     + ("as two launches" if kvpe else "fused in one launch")
+                     + " (eager per-call events give call_us_median)",
         "steps_per_graph": spg,
         "ms_per_step_one_step_graphs": ms_per_step_1,
         "eager_ms_per_step": eager_wall * 1e3 / args.steps,

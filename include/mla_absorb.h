@@ -219,6 +219,45 @@ int mla_decode_attn_fp8(const mla_dims* dims, const uint16_t* q, const uint8_t* 
                         void* stream);
 
 /*
+ * Two-buffer latent cache ([AUDIT] §0: the V3 reference's absorbed decode
+ * keeps kv_cache [1,32,512] and pe_cache [1,32,64]; §4.2: a 32-slot buffer,
+ * 32,768 + 4,096 = 36,864 bytes allocated for 26 active tokens). The same
+ * 576-element row per token as the paged pool, split in two arrays indexed by
+ * [sequence][position], with room for max_seq positions per sequence:
+ *   kv_cache  device [B][max_seq][512] bf16   c_kv of each token
+ *   pe_cache  device [B][max_seq][64]  bf16   RoPE(k_pe) of each token
+ */
+
+/*
+ * mla_cache_append_kvpe — mla_cache_append into the two-buffer cache: token j
+ * goes to [seq_idx[j]][pos[j]] of both arrays (c_kv[j] bit-exactly into
+ * kv_cache, RoPE(k_pe[j], pos[j]) rounded once to bf16 into pe_cache). A
+ * sequence index outside [0, B) or a position outside [0, max_seq) skips the
+ * token (no write).
+ *   seq_idx  device [T] int32  sequence of each new token
+ * Other arguments as mla_cache_append. MLA_ERR_INVALID_ARG for a null
+ * pointer or B, max_seq, T <= 0.
+ */
+int mla_cache_append_kvpe(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                          const int32_t* pos, const int32_t* seq_idx, uint16_t* kv_cache, uint16_t* pe_cache,
+                          int32_t B, int32_t max_seq, int32_t T, void* stream);
+
+/*
+ * mla_decode_attn_kvpe — mla_decode_attn over the two-buffer cache: key t of
+ * sequence b is C_t = [kv_cache[b][t] | pe_cache[b][t]] (the V3 reference
+ * forms the score as the latent product plus the rope product, [AUDIT] §0).
+ * No block table; seq_lens[b] <= max_seq (a longer sequence gets NaN
+ * outputs, never a read past its rows). q, kv_cache, pe_cache, o_lat and
+ * workspace 16-byte aligned, lse 4-byte aligned. The workspace size, the
+ * other arguments, the error codes and determinism are as for
+ * mla_decode_attn; MLA_ERR_UNSUPPORTED also when max_seq exceeds 2^30.
+ */
+int mla_decode_attn_kvpe(const mla_dims* dims, const uint16_t* q, const uint16_t* kv_cache,
+                         const uint16_t* pe_cache, int32_t max_seq, const int32_t* seq_lens, int32_t B,
+                         int32_t Lq, uint16_t* o_lat, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * mla_out_up — expand the latent context through W_UV per head.
  * o[n][h] = W_UV[h] o_lat[n][h]   ([AUDIT] §2.3: sum_t p_t (W_V c_t) = W_V (sum_t p_t c_t))
  *   o_lat  device [N][H][512] bf16

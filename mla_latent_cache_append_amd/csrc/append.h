@@ -32,6 +32,28 @@ __device__ __forceinline__ void append_token(int j,
   if (lane < D_ROPE / 2) *(uint32_t*)(row + D_C + 2 * lane) = y;
 }
 
+// Two-buffer layout ([AUDIT] §0 and §4.2: V3's absorbed decode writes the
+// latent into kv_cache [B][max_seq][512] and the rotated rope key into
+// pe_cache [B][max_seq][64] at [sequence][position]): the same row split in
+// two, token j to [seq_idx[j]][pos[j]]. A sequence index outside [0, B) or a
+// position outside [0, max_seq) skips the token.
+__device__ __forceinline__ void append_token_kvpe(int j,
+    const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ seq_idx,
+    uint16_t* __restrict__ kv_cache, uint16_t* __restrict__ pe_cache, int B, int max_seq, int T, RopeFreqs fr) {
+  const int lane = threadIdx.x & 63;
+  if (j >= T) return;
+  const int b = seq_idx[j], p = pos[j];
+  const u32x4 lat = *(const u32x4*)(c_kv + (int64_t)j * D_C + lane * 8);
+  const int rl = lane & (D_ROPE / 2 - 1);
+  const uint32_t x = *(const uint32_t*)(k_pe + (int64_t)j * D_ROPE + 2 * rl);
+  const uint32_t y = rope_pair_bf16(x, p, fr.f[rl]);
+  if (b < 0 || b >= B || p < 0 || p >= max_seq) return;   // outside the caches: no write
+  const int64_t row = (int64_t)b * max_seq + p;
+  *(u32x4*)(kv_cache + row * D_C + lane * 8) = lat;
+  if (lane < D_ROPE / 2) *(uint32_t*)(pe_cache + row * D_ROPE + 2 * lane) = y;
+}
+
 // fp32 -> E4M3 ("e4m3fn": exponent bias 7, 3 mantissa bits, largest finite
 // 448, 0x7f NaN), nearest value with ties to the even mantissa, magnitudes
 // above 448 saturated. Normal range (|u| >= 2^-6): round the fp32 mantissa

@@ -44,6 +44,23 @@ hipError_t launch_cache_append_fp8(const uint16_t* c_kv, const uint16_t* k_pe, c
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void cache_append_kvpe_kernel(
+    const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ seq_idx,
+    uint16_t* __restrict__ kv_cache, uint16_t* __restrict__ pe_cache, int B, int max_seq, int T, RopeFreqs fr) {
+  append_token_kvpe(blockIdx.x * 4 + (threadIdx.x >> 6), c_kv, k_pe, pos, seq_idx, kv_cache, pe_cache, B,
+                    max_seq, T, fr);
+}
+
+hipError_t launch_cache_append_kvpe(const uint16_t* c_kv, const uint16_t* k_pe, const int32_t* pos,
+                                    const int32_t* seq_idx, uint16_t* kv_cache, uint16_t* pe_cache, int32_t B,
+                                    int32_t max_seq, int32_t T, double rope_base, hipStream_t stream) {
+  const int grid = (T + 3) / 4;
+  hipLaunchKernelGGL(cache_append_kvpe_kernel, dim3(grid), dim3(256), 0, stream, c_kv, k_pe, pos, seq_idx,
+                     kv_cache, pe_cache, B, max_seq, T, rope_freqs(rope_base));
+  return hipGetLastError();
+}
+
 hipError_t launch_cache_append(const uint16_t* c_kv, const uint16_t* k_pe, const int32_t* pos,
                                const int64_t* slot_mapping, uint16_t* pool, int64_t num_blocks,
                                int32_t T, double rope_base, hipStream_t stream) {

@@ -134,8 +134,11 @@ struct AttnArgs {
   float* lse;                   // [B*rows] or null
   float* ws_ml;                 // [slots][rows][2]: (m, l) of each partial, fp32
   uint16_t* ws_acc;             // [slots][rows][512]: partial o_lat normalized by its l, bf16
+  const uint16_t* pe;           // two-buffer layout: pe_cache [B][max_seq][64] (pool = kv_cache
+                                //   [B][max_seq][512]); null for the paged pool
   int64_t num_blocks;
-  int max_blocks;
+  int max_blocks;               // tiles a sequence may span (two-buffer layout: ceil(max_seq / 64))
+  int max_keys;                 // keys a sequence may hold: max_blocks * 64, or max_seq
   int B, Lq, H, rows;
   int n_rg, width;
   float scale_log2;             // softmax scale * log2(e)
@@ -160,23 +163,62 @@ __device__ __forceinline__ uint32_t lds_chunk_off(int t, int c) {
   return (uint32_t)((((t >> 3) * 9 + (c >> 3)) * 64 + (t & 7) * 8 + ((c & 7) ^ swz(t))) * 16);
 }
 
-// Copy one cache block into an LDS tile buffer; wave w issues the 72 / NW
-// instructions j = w*72/NW .. (w+1)*72/NW - 1. Buffer loads with an LDS
-// destination: the per-lane offset is one of two VGPRs, the per-instruction
-// offset an SGPR, and the hardware bound-checks every lane against the
-// descriptor's size. The size covers only the block's first n_valid tokens:
-// rows past the end of the sequence (never written, arbitrary bits) arrive as
-// zeros, so a masked probability of 0 never meets a NaN in the PV product.
+// Where the rows of a run of tokens of one sequence come from. Paged pool:
+// one 1,152-byte row per token inside a 64-token block. Two-buffer layout
+// ([AUDIT] §0 and §4.2: V3's absorbed decode keeps kv_cache [B][max_seq][512]
+// and pe_cache [B][max_seq][64]): a 1,024-byte latent row and a 128-byte rope
+// row per token, in two arrays. The descriptors cover only the run's first
+// n_valid tokens: rows past the end of the sequence (never written, arbitrary
+// bits) arrive as zeros, so a masked probability of 0 never meets a NaN in
+// the PV product.
+struct TileSrc {
+  sgpr_x4 main;   // pool rows, or the latent rows
+  sgpr_x4 pe;     // rope rows (two-buffer layout)
+  int stride;     // bytes per token of `main`
+};
+
+__device__ __forceinline__ TileSrc tile_src(const AttnArgs& a, int b, int blk, int tok0, int n_valid) {
+  TileSrc s;
+  if (a.pe) {
+    const int64_t row = (int64_t)b * a.max_keys + tok0;
+    s.main = buffer_rsrc((const char*)a.pool + row * (D_C * 2), n_valid * (D_C * 2));
+    s.pe = buffer_rsrc((const char*)a.pe + row * (D_ROPE * 2), n_valid * (D_ROPE * 2));
+    s.stride = D_C * 2;
+  } else {
+    s.main = buffer_rsrc((const char*)a.pool + (int64_t)blk * TILE_BYTES + (tok0 % BLOCK) * ROW_BYTES,
+                         n_valid * ROW_BYTES);
+    s.pe = s.main;
+    s.stride = ROW_BYTES;
+  }
+  return s;
+}
+
+// One 1-KiB line: the 128-byte column group cg (features 64 cg .. +63; cg = 8
+// is the rope part) of the 8 tokens tok .. tok + 7 of a tile source. Lane l
+// reads token tok + l / 8, 16-byte chunk `chunk` of the group (the swizzled
+// chunk the LDS slot l expects); the line lands at LDS address dst.
+__device__ __forceinline__ void copy_line(const TileSrc& s, bool two_buf, int lane, uint32_t chunk, int tok,
+                                          int cg, uint32_t dst) {
+  const int tl = lane >> 3;
+  if (two_buf && cg == 8)
+    buffer_load_lds_16(s.pe, (uint32_t)(tl * (D_ROPE * 2)) + chunk, (uint32_t)(tok * (D_ROPE * 2)), dst);
+  else
+    buffer_load_lds_16(s.main, (uint32_t)(tl * s.stride) + chunk, (uint32_t)(tok * s.stride + cg * 128), dst);
+}
+
+// Copy one 64-token tile into an LDS tile buffer; wave w issues the 72 / NW
+// line copies j = w*72/NW .. (w+1)*72/NW - 1. Buffer loads with an LDS
+// destination: the per-lane offset is a VGPR, the per-instruction offset an
+// SGPR, and the hardware bound-checks every lane against the descriptor's size.
 template <int NW>
-__device__ __forceinline__ void load_tile(const uint16_t* pool, int blk, int n_valid, lds_char* dst,
-                                          int wave, const uint32_t (&goff_lane)[2]) {
+__device__ __forceinline__ void load_tile(const TileSrc& src, bool two_buf, lds_char* dst, int wave, int lane) {
   constexpr int PER_WAVE = (BLOCK / 8) * 9 / NW;
-  const sgpr_x4 rsrc = buffer_rsrc((const char*)pool + (int64_t)blk * TILE_BYTES, n_valid * ROW_BYTES);
 #pragma unroll
   for (int jj = 0; jj < PER_WAVE; ++jj) {
     const int j = wave * PER_WAVE + jj;
     const int tg = j / 9, cg = j - 9 * (j / 9);
-    buffer_load_lds_16(rsrc, goff_lane[tg & 1], tg * 8 * ROW_BYTES + cg * 128, lds_addr(dst + j * 1024));
+    const uint32_t chunk = (uint32_t)(((lane & 7) ^ (((lane >> 3) >> 1) | ((tg & 1) << 2))) * 16);
+    copy_line(src, two_buf, lane, chunk, tg * 8, cg, lds_addr(dst + j * 1024));
   }
 }
 
@@ -473,13 +515,7 @@ __global__ __launch_bounds__(256, 1) void attn_cols_kernel(AttnArgs a) {
 
   const int row_base = rg * RG + (CS ? 0 : wave * RB * 16);  // first row of this wave
 
-  // Per-lane parts of every LDS / global tile offset; the rest are immediates.
-  uint32_t goff_lane[2];
-#pragma unroll
-  for (int odd = 0; odd < 2; ++odd) {
-    const int tl = lane >> 3;
-    goff_lane[odd] = (uint32_t)(tl * ROW_BYTES + ((lane & 7) ^ ((tl >> 1) | (odd << 2))) * 16);
-  }
+  const bool two_buf = a.pe != nullptr;   // kv_cache + pe_cache instead of the paged pool
   // K fragment (token 16 tb + c16, chunk 4 ks + g) = kbase[ks & 1] + tb*18432 + (ks >> 1)*1024
   const int ktok = c16 + (CS ? 16 * wave : 0);
   const uint32_t kbase[2] = {lds_chunk_off(ktok, g), lds_chunk_off(ktok, 4 + g)};
@@ -498,16 +534,20 @@ __global__ __launch_bounds__(256, 1) void attn_cols_kernel(AttnArgs a) {
     const int k_first = (int)(x - seq_start);
     const int k_last = (int)(seg_end - seq_start);  // exclusive
     const bool whole = (x == seq_start) && (seg_end == seq_start + ntiles);
-    bool bad = L > a.max_blocks * BLOCK;
+    bool bad = L > a.max_keys;
+    const int Lc = min(L, a.max_keys);             // keys that exist in the cache
     // scalar loads (lgkmcnt): reading a block id never waits on the tile loads
     const __attribute__((address_space(4))) int32_t* bt =
         (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)b * a.max_blocks);
+    auto blk_at = [&](int k) { return two_buf ? 0 : (int)bt[k]; };
+    auto blk_bad = [&](int blk) { return !two_buf && (blk < 0 || blk >= a.num_blocks); };
     Fp8Stage stage;
     {
-      const int blk = bt[k_first];
-      if (blk < 0 || blk >= a.num_blocks) bad = true;
-      else if constexpr (FP8) fp8_tile_load(pool8, a.pool_scale, blk, min(BLOCK, L - k_first * BLOCK), threadIdx.x, stage);
-      else load_tile<NW>(a.pool, blk, min(BLOCK, L - k_first * BLOCK), tiles, wave, goff_lane);
+      const int blk = blk_at(k_first);
+      const int nv = min(BLOCK, Lc - k_first * BLOCK);
+      if (blk_bad(blk)) bad = true;
+      else if constexpr (FP8) fp8_tile_load(pool8, a.pool_scale, blk, nv, threadIdx.x, stage);
+      else load_tile<NW>(tile_src(a, b, blk, k_first * BLOCK, nv), two_buf, tiles, wave, lane);
     }
 
     // ---- query fragments: B operand of S^T (lane: row c16, features 32ks + 8g .. +7)
@@ -543,11 +583,11 @@ __global__ __launch_bounds__(256, 1) void attn_cols_kernel(AttnArgs a) {
       wait_vmem();
       lds_barrier();
       if (k + 1 < k_last) {
-        const int blk = bt[k + 1];
-        if (blk < 0 || blk >= a.num_blocks) bad = true;
+        const int blk = blk_at(k + 1);
+        if (blk_bad(blk)) bad = true;
         else
-          load_tile<NW>(a.pool, blk, min(BLOCK, L - (k + 1) * BLOCK),
-                        tiles + ((k + 1 - k_first) & 1) * TILE_BYTES, wave, goff_lane);
+          load_tile<NW>(tile_src(a, b, blk, (k + 1) * BLOCK, min(BLOCK, Lc - (k + 1) * BLOCK)), two_buf,
+                        tiles + ((k + 1 - k_first) & 1) * TILE_BYTES, wave, lane);
       }
       return tiles + ((k - k_first) & 1) * TILE_BYTES;
     };
@@ -560,9 +600,9 @@ __global__ __launch_bounds__(256, 1) void attn_cols_kernel(AttnArgs a) {
         const int nb = (k + 1 - k_first) & 1;
         bool more = k + 1 < k_last;
         if (more) {
-          const int blk = bt[k + 1];
-          if (blk < 0 || blk >= a.num_blocks) { bad = true; more = false; }
-          else fp8_tile_load(pool8, a.pool_scale, blk, min(BLOCK, L - (k + 1) * BLOCK), threadIdx.x, stage);
+          const int blk = blk_at(k + 1);
+          if (blk_bad(blk)) { bad = true; more = false; }
+          else fp8_tile_load(pool8, a.pool_scale, blk, min(BLOCK, Lc - (k + 1) * BLOCK), threadIdx.x, stage);
         }
         const int cb = (k - k_first) & 1;
         cols_tile<RB, decltype(mask)::value, true>(tiles + cb * TILE_BYTES, sbuf, tscale + cb * BLOCK, qf, o,
@@ -726,8 +766,9 @@ __global__ __launch_bounds__(256 * NH, 1) void attn_rows_kernel(AttnArgs a) {
     for (int q = 0; q < 4; ++q)
       vbase[q] = ht_off(t, 16 * r4 + 2 * q + e) + 8 * (c16 & 1);   // chunk 16 r4 = column 128 r4
   }
-  const uint32_t goff = (uint32_t)((lane >> 3) * ROW_BYTES + ((lane & 7) ^ swz2(8 * r4 + (lane >> 3))) * 16);
+  const uint32_t gchunk = (uint32_t)(((lane & 7) ^ swz2(8 * r4 + (lane >> 3))) * 16);
   const bool dma_wave = hw == 0;                    // half 0's four waves copy the tiles
+  const bool two_buf = a.pe != nullptr;             // kv_cache + pe_cache instead of the paged pool
 
   int64_t x = x_begin;
   while (x < x_end && b < a.B) {
@@ -737,8 +778,9 @@ __global__ __launch_bounds__(256 * NH, 1) void attn_rows_kernel(AttnArgs a) {
     const int k_first = (int)(x - seq_start);
     const int k_last = (int)(seg_end - seq_start);
     const bool whole = (x == seq_start) && (seg_end == seq_start + ntiles);
-    bool bad = L > a.max_blocks * BLOCK;
-    const int key_end = min(k_last * BLOCK, L);
+    bool bad = L > a.max_keys;
+    const int Lc = min(L, a.max_keys);              // keys that exist in the cache
+    const int key_end = min(k_last * BLOCK, Lc);
     const int e0 = 2 * k_first, e1 = (key_end + HT_TOK - 1) / HT_TOK;
 
     // query fragments: B operand of S^T (lane: row r_s, features 32 ks + 8 g .. +7);
@@ -768,29 +810,27 @@ __global__ __launch_bounds__(256 * NH, 1) void attn_rows_kernel(AttnArgs a) {
     // block ids through scalar loads, one tile ahead
     const __attribute__((address_space(4))) int32_t* bt =
         (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)b * a.max_blocks);
+    auto blk_at = [&](int k) { return two_buf ? 0 : (k < ntiles ? (int)bt[k] : -1); };
     int kq = k_first;
-    int blk_q = bt[kq];
-    int blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
+    int blk_q = blk_at(kq);
+    int blk_q1 = blk_at(kq + 1);
     auto issue = [&](int e) {
       const int k = e >> 1;
       if (k != kq) {
         kq = k;
         blk_q = blk_q1;
-        blk_q1 = kq + 1 < ntiles ? bt[kq + 1] : -1;
+        blk_q1 = blk_at(kq + 1);
       }
       const int blk = blk_q;
-      if (blk < 0 || blk >= a.num_blocks) {
+      if (!two_buf && (blk < 0 || blk >= a.num_blocks)) {
         bad = true;
         return;
       }
       if (!dma_wave) return;
-      const int n_valid = min(HT_TOK, L - e * HT_TOK);
-      const sgpr_x4 rsrc =
-          buffer_rsrc((const char*)a.pool + (int64_t)blk * TILE_BYTES + (e & 1) * HT_BYTES, n_valid * ROW_BYTES);
+      const TileSrc src = tile_src(a, b, blk, e * HT_TOK, min(HT_TOK, Lc - e * HT_TOK));
       const uint32_t dst = lds_addr(stages + (e % RSTAGE) * HT_BYTES + r4 * 9 * 1024);
 #pragma unroll
-      for (int cg = 0; cg < 9; ++cg)
-        buffer_load_lds_16(rsrc, goff, r4 * 8 * ROW_BYTES + cg * 128, dst + cg * 1024);
+      for (int cg = 0; cg < 9; ++cg) copy_line(src, two_buf, lane, gchunk, 8 * r4, cg, dst + cg * 1024);
     };
 
     // Scores of half tile e for this wave's 16 rows, online softmax, and P^T /
@@ -1054,7 +1094,7 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     const int k_first = (int)(x - seq_start);
     const int k_last = (int)(seg_end - seq_start);
     const bool whole = (x == seq_start) && (seg_end == seq_start + ntiles);
-    bool bad = L > a.max_blocks * BLOCK;
+    bool bad = L > a.max_keys;
     const int key_end = min(k_last * BLOCK, L);
     const int e0 = 2 * k_first, e1 = (key_end + HT_TOK - 1) / HT_TOK;
 
@@ -1367,11 +1407,26 @@ AttnPlan plan_attention_fp8(int32_t B, int32_t Lq, int32_t H) {
   return p;
 }
 
+// Two-buffer layout (kv_cache + pe_cache): the column kernel up to 47 rows
+// per sequence, the 64-row kernel above (the 128-row kernel's copy sequences
+// are written for the paged pool's 1,152-byte rows).
+AttnPlan plan_attention_kvpe(int32_t B, int32_t Lq, int32_t H) {
+  AttnPlan p = plan_attention(B, Lq, H);
+  if (p.variant == V_ROWS128) {
+    p.variant = V_ROWS64;
+    p.rg_rows = 64;
+    p.n_rg = (Lq * H + 63) / 64;
+    p.width = (TARGET_WGS + p.n_rg - 1) / p.n_rg;
+  }
+  return p;
+}
+
 // Workspace: (m, l) of every partial in fp32, then the partials themselves
 // in bf16, normalized by their l, starting on a 256-byte boundary. Sized for
-// the wider of the two plans, so one workspace serves both cache formats.
+// the widest of the plans, so one workspace serves every cache format and layout.
 static size_t ws_slots(int32_t B, int32_t Lq, int32_t H) {
-  const int w = max(plan_attention(B, Lq, H).width, plan_attention_fp8(B, Lq, H).width);
+  const int w = max(max(plan_attention(B, Lq, H).width, plan_attention_fp8(B, Lq, H).width),
+                    plan_attention_kvpe(B, Lq, H).width);
   return (size_t)w + (size_t)B;
 }
 static size_t ws_ml_bytes(int32_t B, int32_t Lq, int32_t H) {
@@ -1383,17 +1438,21 @@ size_t attention_workspace_bytes(int32_t B, int32_t Lq, int32_t H) {
   return ws_ml_bytes(B, Lq, H) + ws_slots(B, Lq, H) * (size_t)Lq * (size_t)H * D_C * sizeof(uint16_t);
 }
 
-static hipError_t launch_attention(const uint16_t* q, const void* pool, const float* pool_scale,
-                                   int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
-                                   const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
-                                   float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
-                                   hipStream_t stream) {
+// pe != null: the two-buffer layout, pool = kv_cache, max_keys = max_seq
+// (max_blocks = ceil(max_seq / 64), no block table); otherwise the paged pool
+// (max_keys = max_blocks * 64).
+static hipError_t launch_attention(const uint16_t* q, const void* pool, const uint16_t* pe,
+                                   const float* pool_scale, int64_t num_blocks, const int32_t* block_table,
+                                   int32_t max_blocks, int32_t max_keys, const int32_t* seq_lens, int32_t B,
+                                   int32_t Lq, int32_t H, float softmax_scale, uint16_t* o_lat, float* lse,
+                                   void* workspace, hipStream_t stream) {
   const bool fp8 = pool_scale != nullptr;
-  const AttnPlan p = fp8 ? plan_attention_fp8(B, Lq, H) : plan_attention(B, Lq, H);
+  const AttnPlan p = fp8 ? plan_attention_fp8(B, Lq, H) : pe ? plan_attention_kvpe(B, Lq, H) : plan_attention(B, Lq, H);
   AttnArgs a;
   a.q = q;
   a.pool = (const uint16_t*)pool;
   a.pool_scale = pool_scale;
+  a.pe = pe;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.o_lat = o_lat;
@@ -1402,6 +1461,7 @@ static hipError_t launch_attention(const uint16_t* q, const void* pool, const fl
   a.ws_acc = (uint16_t*)((char*)workspace + ws_ml_bytes(B, Lq, H));
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks;
+  a.max_keys = max_keys;
   a.B = B;
   a.Lq = Lq;
   a.H = H;
@@ -1438,8 +1498,16 @@ hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t n
                               const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
                               float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
                               hipStream_t stream) {
-  return launch_attention(q, pool, nullptr, num_blocks, block_table, max_blocks, seq_lens, B, Lq, H,
-                          softmax_scale, o_lat, lse, workspace, stream);
+  return launch_attention(q, pool, nullptr, nullptr, num_blocks, block_table, max_blocks, max_blocks * BLOCK,
+                          seq_lens, B, Lq, H, softmax_scale, o_lat, lse, workspace, stream);
+}
+
+hipError_t launch_decode_attn_kvpe(const uint16_t* q, const uint16_t* kv_cache, const uint16_t* pe_cache,
+                                   int32_t max_seq, const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
+                                   float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
+                                   hipStream_t stream) {
+  return launch_attention(q, kv_cache, pe_cache, nullptr, 0, nullptr, (max_seq + BLOCK - 1) / BLOCK, max_seq,
+                          seq_lens, B, Lq, H, softmax_scale, o_lat, lse, workspace, stream);
 }
 
 hipError_t launch_decode_attn_fp8(const uint16_t* q, const uint8_t* pool8, const float* pool_scale,
@@ -1447,8 +1515,8 @@ hipError_t launch_decode_attn_fp8(const uint16_t* q, const uint8_t* pool8, const
                                   const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
                                   float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
                                   hipStream_t stream) {
-  return launch_attention(q, pool8, pool_scale, num_blocks, block_table, max_blocks, seq_lens, B, Lq, H,
-                          softmax_scale, o_lat, lse, workspace, stream);
+  return launch_attention(q, pool8, nullptr, pool_scale, num_blocks, block_table, max_blocks, max_blocks * BLOCK,
+                          seq_lens, B, Lq, H, softmax_scale, o_lat, lse, workspace, stream);
 }
 
 }  // namespace mla

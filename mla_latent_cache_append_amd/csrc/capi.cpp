@@ -172,6 +172,36 @@ int mla_decode_attn_fp8(const mla_dims* dims, const uint16_t* q, const uint8_t* 
                                                    workspace, (hipStream_t)stream));
 }
 
+int mla_cache_append_kvpe(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                          const int32_t* pos, const int32_t* seq_idx, uint16_t* kv_cache, uint16_t* pe_cache,
+                          int32_t B, int32_t max_seq, int32_t T, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!c_kv || !k_pe || !pos || !seq_idx || !kv_cache || !pe_cache || B <= 0 || max_seq <= 0 || T <= 0)
+    return MLA_ERR_INVALID_ARG;
+  return launch_status(mla::launch_cache_append_kvpe(c_kv, k_pe, pos, seq_idx, kv_cache, pe_cache, B, max_seq, T,
+                                                     (double)dims->rope_base, (hipStream_t)stream));
+}
+
+int mla_decode_attn_kvpe(const mla_dims* dims, const uint16_t* q, const uint16_t* kv_cache,
+                         const uint16_t* pe_cache, int32_t max_seq, const int32_t* seq_lens, int32_t B,
+                         int32_t Lq, uint16_t* o_lat, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (dims->num_heads % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  if (!q || !kv_cache || !pe_cache || !seq_lens || !o_lat || max_seq <= 0 || B <= 0 || Lq <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!attn_aligned(q, kv_cache, pe_cache, o_lat, lse, workspace)) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)Lq * dims->num_heads > (1 << 20) || max_seq > (1 << 30)) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)B * (((int64_t)Lq * dims->num_heads + 3) / 4) > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla::attention_workspace_bytes(B, Lq, dims->num_heads);
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  return launch_status(mla::launch_decode_attn_kvpe(q, kv_cache, pe_cache, max_seq, seq_lens, B, Lq,
+                                                    dims->num_heads, dims->softmax_scale, o_lat, lse, workspace,
+                                                    (hipStream_t)stream));
+}
+
 int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o,
                int32_t N, void* stream) {
   int st = check_dims(dims);

@@ -65,6 +65,7 @@ struct AttnPlan {
 
 AttnPlan plan_attention(int32_t B, int32_t Lq, int32_t H);
 AttnPlan plan_attention_fp8(int32_t B, int32_t Lq, int32_t H);
+AttnPlan plan_attention_kvpe(int32_t B, int32_t Lq, int32_t H);
 
 // Partial-result slots of one call: width + B (one per (workgroup, sequence) pair).
 size_t attention_workspace_bytes(int32_t B, int32_t Lq, int32_t H);
@@ -74,6 +75,16 @@ hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t n
                               const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
                               float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
                               hipStream_t stream);
+
+// Two-buffer latent cache: kv_cache [B][max_seq][512] and pe_cache [B][max_seq][64] bf16.
+hipError_t launch_cache_append_kvpe(const uint16_t* c_kv, const uint16_t* k_pe, const int32_t* pos,
+                                    const int32_t* seq_idx, uint16_t* kv_cache, uint16_t* pe_cache, int32_t B,
+                                    int32_t max_seq, int32_t T, double rope_base, hipStream_t stream);
+
+hipError_t launch_decode_attn_kvpe(const uint16_t* q, const uint16_t* kv_cache, const uint16_t* pe_cache,
+                                   int32_t max_seq, const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
+                                   float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
+                                   hipStream_t stream);
 
 // FP8 latent cache: codes [num_blocks][64][576] E4M3, scales [num_blocks][64] fp32.
 hipError_t launch_cache_append_fp8(const uint16_t* c_kv, const uint16_t* k_pe, const int32_t* pos,

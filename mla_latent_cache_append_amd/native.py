@@ -63,6 +63,10 @@ _SIG = {
     "mla_cache_append_fp8": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _P, _I64, _I32, _P]),
     "mla_decode_attn_fp8": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I64, _P, _I32, _P, _I32,
                                            _I32, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_cache_append_kvpe": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                             _P]),
+    "mla_decode_attn_kvpe": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I32, _P, _I32, _I32, _P, _P,
+                                            _P, ctypes.c_size_t, _P]),
     "mla_out_up": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I32, _P]),
     "mla_linear_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "mla_linear": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _P, ctypes.c_size_t, _P]),
@@ -245,6 +249,49 @@ def mla_decode_attn_fp8(dims: MlaDims, q, pool8, pool_scale, block_table, seq_le
         ctypes.byref(dims), _ptr(q), _ptr(pool8), _ptr(pool_scale), pool8.shape[0], _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), B, Lq, _ptr(o_lat), _ptr(lse), _ptr(workspace),
         workspace.numel(), _stream(stream)))
+
+
+def _check_kvpe(kv_cache, pe_cache):
+    _check("kv_cache", kv_cache, torch.bfloat16)
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != D_C:
+        raise ValueError("kv_cache must be [B, max_seq, 512]")
+    _check("pe_cache", pe_cache, torch.bfloat16, (kv_cache.shape[0], kv_cache.shape[1], D_ROPE))
+
+
+def mla_cache_append_kvpe(dims: MlaDims, c_kv, k_pe, pos, seq_idx, kv_cache, pe_cache, stream=None):
+    """Write c_kv into ``kv_cache[seq_idx, pos]`` and RoPE(k_pe, pos) into
+    ``pe_cache[seq_idx, pos]`` (the two-buffer cache)."""
+    T = c_kv.shape[0]
+    _check("c_kv", c_kv, torch.bfloat16, (T, D_C))
+    _check("k_pe", k_pe, torch.bfloat16, (T, D_ROPE))
+    _check("pos", pos, torch.int32, (T,))
+    _check("seq_idx", seq_idx, torch.int32, (T,))
+    _check_kvpe(kv_cache, pe_cache)
+    _ok("mla_cache_append_kvpe", lib().mla_cache_append_kvpe(
+        ctypes.byref(dims), _ptr(c_kv), _ptr(k_pe), _ptr(pos), _ptr(seq_idx), _ptr(kv_cache), _ptr(pe_cache),
+        kv_cache.shape[0], kv_cache.shape[1], T, _stream(stream)))
+
+
+def mla_decode_attn_kvpe(dims: MlaDims, q, kv_cache, pe_cache, seq_lens, Lq: int, o_lat, lse=None,
+                         workspace=None, stream=None):
+    """Latent attention of ``q`` [B*Lq, H, 576] over the two-buffer cache
+    (kv_cache [B, max_seq, 512], pe_cache [B, max_seq, 64])."""
+    H = dims.num_heads
+    B = seq_lens.shape[0]
+    _check("q", q, torch.bfloat16, (B * Lq, H, D_K))
+    _check_kvpe(kv_cache, pe_cache)
+    if kv_cache.shape[0] != B:
+        raise ValueError("kv_cache must hold B sequences")
+    _check("seq_lens", seq_lens, torch.int32, (B,))
+    _check("o_lat", o_lat, torch.bfloat16, (B * Lq, H, D_C))
+    if lse is not None:
+        _check("lse", lse, torch.float32, (B * Lq, H))
+    if workspace is None:
+        raise ValueError("workspace is required (mla_decode_workspace_size bytes, uint8)")
+    _check("workspace", workspace, torch.uint8)
+    _ok("mla_decode_attn_kvpe", lib().mla_decode_attn_kvpe(
+        ctypes.byref(dims), _ptr(q), _ptr(kv_cache), _ptr(pe_cache), kv_cache.shape[1], _ptr(seq_lens), B, Lq,
+        _ptr(o_lat), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def mla_out_up(dims: MlaDims, o_lat, w_uv, o, stream=None):

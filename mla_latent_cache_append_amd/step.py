@@ -22,14 +22,19 @@ class DecodeStep:
     caller; the step writes the new tokens' cache rows before attending.
     With ``pool_scale`` ([num_blocks, 64] fp32) the pool is the FP8 cache
     ([num_blocks, 64, 576] uint8 E4M3 codes) and the step uses the FP8 calls.
+    With ``pe_cache`` ([B, max_seq, 64] bf16) the cache is the two-buffer
+    layout: ``pool`` is kv_cache [B, max_seq, 512], there is no block table,
+    and the ``slots`` argument of ``append`` / ``__call__`` is each new
+    token's sequence index (int32) instead of its pool slot.
     """
 
     def __init__(self, H: int, B: int, Lq: int, pool, block_table, seq_lens, w_uk, w_uv,
-                 device="cuda", pool_scale=None):
+                 device="cuda", pool_scale=None, pe_cache=None):
         self.dims = nat.mla_dims_default(H)
         self.H, self.B, self.Lq, self.N = H, B, Lq, B * Lq
         self.pool, self.block_table, self.seq_lens = pool, block_table, seq_lens
         self.pool_scale = pool_scale
+        self.pe_cache = pe_cache
         self.w_uk, self.w_uv = w_uk, w_uv
         N = self.N
         self.q = torch.empty(N, H, nat.D_K, dtype=torch.bfloat16, device=device)
@@ -40,14 +45,19 @@ class DecodeStep:
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
 
     def append(self, c_kv, k_pe, pos, slots):
-        if self.pool_scale is None:
+        if self.pe_cache is not None:
+            nat.mla_cache_append_kvpe(self.dims, c_kv, k_pe, pos, slots, self.pool, self.pe_cache)
+        elif self.pool_scale is None:
             nat.mla_cache_append(self.dims, c_kv, k_pe, pos, slots, self.pool)
         else:
             nat.mla_cache_append_fp8(self.dims, c_kv, k_pe, pos, slots, self.pool, self.pool_scale)
 
     def decode_attn(self):
         """The attention call alone, over the absorbed queries in ``self.q``."""
-        if self.pool_scale is None:
+        if self.pe_cache is not None:
+            nat.mla_decode_attn_kvpe(self.dims, self.q, self.pool, self.pe_cache, self.seq_lens, self.Lq,
+                                     self.o_lat, self.lse, self.workspace)
+        elif self.pool_scale is None:
             nat.mla_decode_attn(self.dims, self.q, self.pool, self.block_table, self.seq_lens, self.Lq,
                                 self.o_lat, self.lse, self.workspace)
         else:
@@ -61,7 +71,12 @@ class DecodeStep:
 
     def __call__(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots):
         """Append the N new tokens (row n = b*Lq + i at position q_pos[n]), then
-        attend: append and absorb share one launch, then attention and out_up."""
+        attend: append and absorb share one launch (two launches for the
+        two-buffer cache), then attention and out_up."""
+        if self.pe_cache is not None:
+            self.append(c_kv, k_pe, q_pos, slots)
+            self.attend(q_nope, q_pe, q_pos)
+            return self.o
         nat.mla_append_absorb(self.dims, c_kv, k_pe, slots, self.pool, q_nope, q_pe, q_pos, self.w_uk, self.q,
                               pool_scale=self.pool_scale)
         self.decode_attn()
