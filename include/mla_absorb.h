@@ -153,6 +153,36 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
                     const int32_t* seq_lens, int32_t B, int32_t Lq, uint16_t* o_lat, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the fixed per-GPU array in which mla_decode_attn_noalloc keeps its
+ * partial results (64 MiB; held by each GPU the library runs on until the
+ * process ends). */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * mla_decode_attn_noalloc — mla_decode_attn without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * allocation. The partials of the key-range splits go to a fixed array of
+ * MLA_NOALLOC_SCRATCH_BYTES bytes per GPU instead; the call allocates
+ * nothing (no hipMalloc, no allocating library routine), and the first call
+ * on a GPU looks up that GPU's copy of the array.
+ * Arguments, layouts, results, device-value handling and determinism are
+ * those of mla_decode_attn (same kernels; outputs bit-identical to it).
+ * Limits and errors: MLA_ERR_WORKSPACE when the shape needs more than
+ * MLA_NOALLOC_SCRATCH_BYTES (mla_decode_workspace_size(dims, B, Lq) above it),
+ * checked on the host before anything is enqueued; MLA_ERR_INVALID_ARG when
+ * `stream` belongs to another GPU than the current one; otherwise as
+ * mla_decode_attn.
+ * Concurrency: every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents. Calls that overlap in time on one GPU (other streams,
+ * other host threads) race and give wrong results; calls in one stream are
+ * ordered and safe.
+ */
+int mla_decode_attn_noalloc(const mla_dims* dims, const uint16_t* q, const uint16_t* pool,
+                            int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t B, int32_t Lq, uint16_t* o_lat, float* lse,
+                            void* stream);
+
 /*
  * mla_append_absorb — mla_cache_append and mla_absorb_q of one decode step in
  * a single launch, for the usual case where the step's N new tokens are its N

@@ -33,6 +33,7 @@
 //    balanced exactly. A range that covers a whole sequence writes the final
 //    o_lat; otherwise it writes (m, l, acc) partials that the combine kernel
 //    merges in a fixed order (deterministic, no atomics).
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1517,6 +1518,60 @@ hipError_t launch_decode_attn_fp8(const uint16_t* q, const uint8_t* pool8, const
                                   hipStream_t stream) {
   return launch_attention(q, pool8, nullptr, pool_scale, num_blocks, block_table, max_blocks, max_blocks * BLOCK,
                           seq_lens, B, Lq, H, softmax_scale, o_lat, lse, workspace, stream);
+}
+
+// ----------------------------------------------- without allocation
+//
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc): the partials go to a fixed device
+// array instead of a caller workspace. Each GPU the library runs on holds its
+// own copy of the array until the process ends; every call on that GPU uses
+// it, so calls that overlap in time on one GPU (other streams, other host
+// threads) race. Nothing in it needs to start at a given value: each call
+// writes every partial before its merge reads it.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+static std::mutex scratch_mu;
+static void* scratch_dev[MAX_DEVICES];   // device address of `scratch` on each GPU
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// with that device current. (In host code the array's name is only a
+// stand-in: its address is not the device's.)
+static hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_decode_attn_noalloc(const uint16_t* q, const uint16_t* pool, int64_t num_blocks,
+                                      const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                      int32_t B, int32_t Lq, int32_t H, float softmax_scale, uint16_t* o_lat,
+                                      float* lse, hipStream_t stream) {
+  if (attention_workspace_bytes(B, Lq, H) > NOALLOC_SCRATCH_BYTES) return hipErrorInvalidValue;
+  if (stream) {
+    int cur = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return e;
+    if (sdev != cur) return hipErrorInvalidDevice;
+  }
+  void* ws = nullptr;
+  const hipError_t e = scratch_on_current_device(&ws);
+  if (e != hipSuccess) return e;
+  return launch_attention(q, pool, nullptr, nullptr, num_blocks, block_table, max_blocks, max_blocks * BLOCK,
+                          seq_lens, B, Lq, H, softmax_scale, o_lat, lse, ws, stream);
 }
 
 }  // namespace mla

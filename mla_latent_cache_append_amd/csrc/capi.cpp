@@ -108,6 +108,28 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
                                                (hipStream_t)stream));
 }
 
+int mla_decode_attn_noalloc(const mla_dims* dims, const uint16_t* q, const uint16_t* pool,
+                            int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t B, int32_t Lq, uint16_t* o_lat, float* lse,
+                            void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (dims->num_heads % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  if (!q || !pool || !block_table || !seq_lens || !o_lat || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || B <= 0 || Lq <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!attn_aligned(q, pool, nullptr, o_lat, lse, nullptr)) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)Lq * dims->num_heads > (1 << 20) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
+    return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)B * (((int64_t)Lq * dims->num_heads + 3) / 4) > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
+  if (mla::attention_workspace_bytes(B, Lq, dims->num_heads) > mla::NOALLOC_SCRATCH_BYTES)
+    return MLA_ERR_WORKSPACE;
+  const hipError_t e = mla::launch_decode_attn_noalloc(q, pool, num_blocks, block_table, max_blocks_per_seq,
+                                                       seq_lens, B, Lq, dims->num_heads, dims->softmax_scale,
+                                                       o_lat, lse, (hipStream_t)stream);
+  return e == hipErrorInvalidDevice ? MLA_ERR_INVALID_ARG : launch_status(e);
+}
+
 int mla_append_absorb(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
                       const int64_t* slot_mapping, uint16_t* pool, int64_t num_blocks,
                       const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,

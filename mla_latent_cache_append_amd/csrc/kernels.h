@@ -76,6 +76,16 @@ hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t n
                               float softmax_scale, uint16_t* o_lat, float* lse, void* workspace,
                               hipStream_t stream);
 
+// mla_decode_attn with its partials in a fixed per-device array of this many
+// bytes instead of a caller workspace (see attn.hip); a shape whose workspace
+// exceeds it returns hipErrorInvalidValue before anything is enqueued, and a
+// stream of another device than the current one hipErrorInvalidDevice.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+hipError_t launch_decode_attn_noalloc(const uint16_t* q, const uint16_t* pool, int64_t num_blocks,
+                                      const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                      int32_t B, int32_t Lq, int32_t H, float softmax_scale, uint16_t* o_lat,
+                                      float* lse, hipStream_t stream);
+
 // Two-buffer latent cache: kv_cache [B][max_seq][512] and pe_cache [B][max_seq][64] bf16.
 hipError_t launch_cache_append_kvpe(const uint16_t* c_kv, const uint16_t* k_pe, const int32_t* pos,
                                     const int32_t* seq_idx, uint16_t* kv_cache, uint16_t* pe_cache, int32_t B,

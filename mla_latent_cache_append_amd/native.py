@@ -56,6 +56,8 @@ _SIG = {
     "mla_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaDims), _I32, _I32]),
     "mla_decode_attn": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _I64, _P, _I32, _P, _I32, _I32,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
+    "mla_decode_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _I64, _P, _I32, _P, _I32, _I32,
+                                               _P, _P, _P]),
     "mla_append_absorb": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
                                          _I32, _P]),
     "mla_append_absorb_fp8": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
@@ -178,6 +180,25 @@ def mla_decode_attn(dims: MlaDims, q, pool, block_table, seq_lens, Lq: int, o_la
         ctypes.byref(dims), _ptr(q), _ptr(pool), pool.shape[0], _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), B, Lq, _ptr(o_lat), _ptr(lse), _ptr(workspace),
         workspace.numel(), _stream(stream)))
+
+
+def mla_decode_attn_noalloc(dims: MlaDims, q, pool, block_table, seq_lens, Lq: int, o_lat, lse=None, stream=None):
+    """mla_decode_attn with its partials in the library's fixed per-GPU array
+    (no workspace; calls overlapping in time on one GPU race)."""
+    H = dims.num_heads
+    B = seq_lens.shape[0]
+    _check("q", q, torch.bfloat16, (B * Lq, H, D_K))
+    _check("pool", pool, torch.bfloat16)
+    _check("block_table", block_table, torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _check("seq_lens", seq_lens, torch.int32, (B,))
+    _check("o_lat", o_lat, torch.bfloat16, (B * Lq, H, D_C))
+    if lse is not None:
+        _check("lse", lse, torch.float32, (B * Lq, H))
+    _ok("mla_decode_attn_noalloc", lib().mla_decode_attn_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(pool), pool.shape[0], _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), B, Lq, _ptr(o_lat), _ptr(lse), _stream(stream)))
 
 
 def mla_append_absorb(dims: MlaDims, c_kv, k_pe, slot_mapping, pool, q_nope, q_pe, pos, w_uk, q_out,

@@ -239,3 +239,18 @@ def test_attention_calls_reject_misaligned_buffers(nat):
         assert attn(**kw) == nat.MLA_ERR_INVALID_ARG, kw
         assert attn8(**kw) == nat.MLA_ERR_INVALID_ARG, kw
     assert attn8(sc=odd) == nat.MLA_ERR_INVALID_ARG
+
+
+def test_no_alloc_attention_rejects_shapes_beyond_its_array(nat):
+    """The workspace of a 512-token prefill chunk of 4 sequences at 128 heads
+    (~338 MB) exceeds the fixed 64 MiB array: refused on the host (no device
+    is touched)."""
+    lib = nat.lib()
+    d = nat.mla_dims_default(128)
+    P = ctypes.c_void_p
+    ok, null = P(0x1000), P(0)
+    assert nat.mla_decode_workspace_size(d, 4, 512) > 64 << 20
+    assert lib.mla_decode_attn_noalloc(ctypes.byref(d), ok, ok, 4, ok, 2, ok, 4, 512, ok, null,
+                                       null) == nat.MLA_ERR_WORKSPACE
+    assert lib.mla_decode_attn_noalloc(ctypes.byref(d), null, ok, 4, ok, 2, ok, 1, 1, ok, null,
+                                       null) == nat.MLA_ERR_INVALID_ARG
