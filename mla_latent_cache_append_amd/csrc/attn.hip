@@ -1202,6 +1202,8 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     v_addr(e0);
     // one iteration; the first half tile of the segment (FIRST) starts the
     // PV accumulators from zero and is peeled off the loop
+    // half tiles below e_open hold only keys every row may see (no key mask)
+    const int e_open = max(0, L - a.Lq + 1) / HT_TOK;
     auto step = [&](const int e, auto first) {
       constexpr bool FIRST = decltype(first)::value;
       const bool more = e + 1 < e1;
@@ -1217,8 +1219,9 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
                : OPS_O, OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "+v"(alpha),       \
                  [mref] "+v"(mref)                                                                    \
                : OWN_OPS_Q, OWN_OPS_KA, OWN_OPS_VA, [lr] "v"(lr), [scale] "s"(a.scale_log2),          \
-                 [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO                               \
+                 [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), [open] "s"(open), OWN_OPS_SO             \
                : OWN_CLOB, "vcc", "m0", "scc", "memory")
+      const int open = uni(e + 1 < e_open ? 1 : 0);   // half tile e+1 needs no key mask
       if constexpr (FIRST)
         OWN_ITER(OWN_ASM_IT_FIRST, OWN_OPS_O_OUT);
       else
@@ -1227,6 +1230,8 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
       if (more) {
         // alpha belongs to half tile e+1, whose PV runs in the next iteration
         if (__any(alpha != 1.f)) {
+          // the sequence's last PV MFMAs may still be writing the accumulators
+          asm volatile(OWN_ASM_GUARD ::: "memory");
 #pragma unroll
           for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
         }
@@ -1237,6 +1242,7 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     };
     step(e0, std::true_type{});
     for (int e = e0 + 1; e < e1; ++e) step(e, std::false_type{});
+    asm volatile(OWN_ASM_GUARD ::: "memory");   // PV results settle before the epilogue reads them
 
     // ---- finish the segment. Both outputs hold o / l in bf16 (the final
     // o_lat, or a partial for the merge): each wave writes its 32 rows into

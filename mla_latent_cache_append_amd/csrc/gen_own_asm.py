@@ -28,9 +28,14 @@ Templates (iteration e scores half tile e+1 and accumulates half tile e):
         phase P: the 32 PV MFMAs of half tile e,
                  O^T[col][row] += V^T[col][token] P^T[token][row], V^T
                  fragments read transposed, carrying the first half of the
-                 softmax of half tile e+1 (with the key mask);
+                 softmax of half tile e+1 (with the key mask; IT skips
+                 the mask when operand `open` is non-zero: a half tile
+                 whose keys every row may see);
         nine buffer -> LDS copies of this wave's share of half tile e+3 are
         spread over phase S; FIRST starts the PV accumulators from zero.
+        These end with PV MFMAs still in flight.
+  OWN_ASM_GUARD
+        wait states after them, before code that reads the accumulators.
 
 The MFMA is v_mfma_f32_32x32x16_bf16 throughout. Run: python gen_own_asm.py
 (the build runs it before compiling).
@@ -58,7 +63,11 @@ SN = "v[%d:%d]" % (SN0, SN0 + 15)
 T0 = SN0 - 4                               # temporaries
 TMP = ["v%d" % (T0 + i) for i in range(4)]
 CLOB_LO = T0
-GUARD = ["s_nop 7", "s_nop 7", "s_nop 7"]   # MFMA results settle before the compiler's code reads them
+# MFMA results settle before VALU code reads them (24 wait states: more than an
+# 8-pass XDL result needs). Used only where a VALU instruction follows an MFMA
+# whose result it reads with no other instructions between; measured, each
+# nop wait state costs about four cycles of the wave's issue.
+GUARD = ["s_nop 7", "s_nop 7", "s_nop 7"]
 
 # the nine copies of the next stage, one after every fourth score MFMA (the
 # vector memory unit takes the four waves' copies one at a time; bunched
@@ -127,15 +136,26 @@ def vread(seq, j):
             "V%db" % j)
 
 
-def dma(seq, cg, mb="mb", rs="rs"):
-    """Line cg of this wave's share of a stage: buffer -> LDS copy of 1 KiB
-    (M0 = LDS base of the line; the copy counts in vmcnt, not lgkmcnt). The
-    cache is read once per call, so the copy is marked non-temporal (nt): it
-    streams past the caches instead of displacing the split partials the
-    merge reads right after (measured ~2 % faster per call, same results)."""
+def dma_m0(seq, cg, mb="mb"):
+    """M0 = LDS base of line cg of this wave's share of a stage. The copy that
+    reads it must not be the next instruction (one wait state)."""
     seq.op("s_add_u32 m0, %%[%s], 0x%x" % (mb, cg * 1024))
-    seq.op("s_nop 0")
+
+
+def dma_load(seq, cg, rs="rs"):
+    """Line cg: buffer -> LDS copy of 1 KiB to M0 (the copy counts in vmcnt,
+    not lgkmcnt). The cache is read once per call, so the copy is marked
+    non-temporal (nt): it streams past the caches instead of displacing the
+    split partials the merge reads right after (measured ~2 % faster per
+    call, same results)."""
     seq.op("buffer_load_dwordx4 %%[go], %%[%s], %%[so%d] offen nt lds" % (rs, cg))
+
+
+def dma(seq, cg, mb="mb", rs="rs"):
+    """Both halves of a copy, with the wait state between them as a nop."""
+    dma_m0(seq, cg, mb)
+    seq.op("s_nop 0")
+    dma_load(seq, cg, rs)
 
 
 def sn_reg(i):
@@ -233,6 +253,10 @@ def gen_pro(mask):
 
 
 def gen_iter(mask, first):
+    """mask: the key mask of the half tile whose scores are formed (needed
+    only where some key lies past some row's position). The sequence ends
+    with PV MFMAs in flight: code after it that reads the accumulators waits
+    first (GUARD)."""
     s = Seq()
     s.op("s_nop 1")
     for ks in range(PF_K):
@@ -245,6 +269,8 @@ def gen_iter(mask, first):
         s.op(ins)
     vnext = 0
     for ks in range(KSTEPS):
+        if ks in DMA_S:
+            dma_m0(s, DMA_S.index(ks))     # the score MFMA below is the wait state
         score_mfma(s, ks)
         if ks + PF_K < KSTEPS:
             kread(s, ks + PF_K)
@@ -252,7 +278,7 @@ def gen_iter(mask, first):
             vread(s, vnext)
             vnext += 1
         if ks in DMA_S:
-            dma(s, DMA_S.index(ks))
+            dma_load(s, DMA_S.index(ks))
         for ins in rest[ks * per:(ks + 1) * per]:
             s.op(ins)
     while vnext < PF_V:
@@ -270,26 +296,31 @@ def gen_iter(mask, first):
             vread(s, j + PF_V)
         if j in DMA_P:
             dma(s, len(DMA_S) + DMA_P.index(j))
-        if j == P_VALU_FROM:
-            s.op("s_nop 7")                # the last score MFMA's result settles
-            s.op("s_nop 7")
-            s.op("s_nop 3")
+        # The max half reads the last score MFMA's result only after
+        # P_VALU_FROM + 1 PV MFMAs and their V^T reads and waits: more than
+        # the 11 wait states an 8-pass result needs before a VALU read, and
+        # each of those MFMAs waits for the previous one to leave the XDL
+        # pipe (32 cycles), so no nop is needed there.
         if j >= P_VALU_FROM:
             k = j - P_VALU_FROM
             for ins in max_valu[k * mper:(k + 1) * mper]:
                 s.op(ins)
     s.drain()
-    s.lines += GUARD
     return s.text()
 
 
 def main():
     out = os.path.join(HERE, "own_asm.inc")
     body = ["// Generated by gen_own_asm.py; do not edit.", ""]
-    # the key mask always runs: in phase P its VALU work hides under the PV
-    # MFMAs, and one sequence per call site keeps register allocation simple
-    temps = [("OWN_ASM_QLOAD", gen_qload()), ("OWN_ASM_PRO", gen_pro(True)), ("OWN_ASM_IT", gen_iter(True, False)),
-             ("OWN_ASM_IT_FIRST", gen_iter(True, True))]
+    # IT_NOMASK serves the half tiles every row sees whole (most of them);
+    # IT (key mask) the last ones of a sequence and the causal block
+    # (one asm statement holding both, chosen by a scalar branch, so that the
+    # loop has a single call site and one register assignment)
+    it_sel = ("s_cmp_lg_u32 %[open], 0\\n\\ts_cbranch_scc1 own_open_%=\\n\\t" + gen_iter(True, False)
+              + "s_branch own_done_%=\\n\\town_open_%=:\\n\\t" + gen_iter(False, False) + "own_done_%=:\\n\\t")
+    temps = [("OWN_ASM_QLOAD", gen_qload()), ("OWN_ASM_PRO", gen_pro(True)), ("OWN_ASM_IT", it_sel),
+             ("OWN_ASM_IT_FIRST", gen_iter(True, True)),
+             ("OWN_ASM_GUARD", "".join(l + "\\n\\t" for l in GUARD))]
     for name, text in temps:
         body.append('#define %s "%s"' % (name, text))
         body.append("")
