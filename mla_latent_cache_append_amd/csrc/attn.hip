@@ -1083,9 +1083,11 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     vbase = ht_off(tl, e) + 8 * (i16 & 1);
   }
   const uint32_t goff = (uint32_t)((lane >> 3) * ROW_BYTES + ((lane & 7) ^ swz2(8 * wave + (lane >> 3))) * 16);
-  uint32_t so[9];   // buffer offset of line cg of this wave's 8 tokens
-#pragma unroll
-  for (int cg = 0; cg < 9; ++cg) so[cg] = (uint32_t)(wave * 8 * ROW_BYTES + cg * 128);
+  const uint32_t so = (uint32_t)uni(wave * 8 * ROW_BYTES);   // buffer offset of this wave's 8 tokens
+  // the pool base as descriptor words, and its size as a 32-bit bound
+  const uint32_t pool_lo = (uint32_t)uni((int)(uint32_t)(uintptr_t)a.pool);
+  const uint32_t pool_hi = (uint32_t)uni((int)((uint32_t)((uintptr_t)a.pool >> 32) & 0xffffu));
+  const uint32_t nblk = (uint32_t)uni((int)min(a.num_blocks, (int64_t)0x7fffffff));
 
   int64_t x = x_begin;
   while (x < x_end && b < a.B) {
@@ -1193,17 +1195,34 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     // Half tile e+3 goes into the stage of e-1; its nine copies are spread
     // over the iteration's instruction sequence, which keeps the vector
     // memory queue from stalling the wave. The descriptor of the next
-    // iteration's copies and its LDS addresses are prepared at the end of
-    // the current one.
+    // iteration's copies is prepared between the sequences with 32-bit
+    // scalar arithmetic (a lone wave issues about one instruction per four
+    // cycles, and the MFMA pipe idles meanwhile); the K / V^T addresses and
+    // the mask limit move on inside the sequences, under the PV MFMAs.
     sgpr_x4 rs;
     uint32_t mb;
     prep(e0 + OSTAGE - 1, blk_of(e0 + OSTAGE - 1), rs, mb);
     k_addr(e0 + 1 < e1 ? e0 + 1 : e0);
     v_addr(e0);
-    // one iteration; the first half tile of the segment (FIRST) starts the
-    // PV accumulators from zero and is peeled off the loop
+    const uint32_t mb0 = (uint32_t)uni((int)lds_addr(stages + wave * 9 * 1024));
+    // copies of half tile ep from block blk: pool + blk * 73,728 + (ep & 1) * 36,864,
+    // min(32, L - 32 ep) rows; none past the segment or for a block id outside the pool
+    auto prep_next = [&](int ep, int blk) {
+      mb = mb0 + (uint32_t)(ep & (OSTAGE - 1)) * HT_BYTES;
+      const bool in_seg = ep < e1;
+      const bool ok = (uint32_t)blk < nblk;
+      if (in_seg && !ok) bad = true;
+      const uint64_t base = ((uint64_t)pool_hi << 32 | pool_lo) + (uint64_t)(uint32_t)blk * TILE_BYTES +
+                            (uint32_t)(ep & 1) * HT_BYTES;
+      const uint32_t bytes = (uint32_t)min(HT_TOK, L - ep * HT_TOK) * ROW_BYTES;
+      rs = in_seg && ok ? sgpr_x4{(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, bytes, 0x00020000u}
+                        : sgpr_x4{pool_lo, pool_hi, 0u, 0x00020000u};
+    };
     // half tiles below e_open hold only keys every row may see (no key mask)
     const int e_open = max(0, L - a.Lq + 1) / HT_TOK;
+    int lr = lim - ((e0 + 1) * HT_TOK + 4 * h);   // mask limit of the scores of e0+1 (the sequence moves it on)
+    // one iteration; the first half tile of the segment (FIRST) starts the
+    // PV accumulators from zero and is peeled off the loop
     auto step = [&](const int e, auto first) {
       constexpr bool FIRST = decltype(first)::value;
       const bool more = e + 1 < e1;
@@ -1213,15 +1232,14 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
       // scalar load issued right after it completes under the MFMAs.
       asm volatile("s_barrier" ::: "memory");
       const int blk_next = blk_of(e + OSTAGE);   // for the copies prepared at the end
-      const int lr = lim - ((e + 1) * HT_TOK + 4 * h);   // mask of the scores of e+1
+      int t0, t1, t2;
 #define OWN_ITER(NAME, OPS_O)                                                                         \
   asm volatile(NAME                                                                                   \
                : OPS_O, OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "+v"(alpha),       \
-                 [mref] "+v"(mref)                                                                    \
-               : OWN_OPS_Q, OWN_OPS_KA, OWN_OPS_VA, [lr] "v"(lr), [scale] "s"(a.scale_log2),          \
-                 [mb] "s"(mb), [rs] "s"(rs), [go] "v"(goff), [open] "s"(open), OWN_OPS_SO             \
+                 [mref] "+v"(mref), [lr] "+v"(lr), OWN_OPS_KA_IO, OWN_OPS_VA_IO, OWN_OPS_BOOK_OUT     \
+               : OWN_OPS_Q, [scale] "s"(a.scale_log2), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO,      \
+                 OWN_OPS_BOOK_IN                                                                      \
                : OWN_CLOB, "vcc", "m0", "scc", "memory")
-      const int open = uni(e + 1 < e_open ? 1 : 0);   // half tile e+1 needs no key mask
       if constexpr (FIRST)
         OWN_ITER(OWN_ASM_IT_FIRST, OWN_OPS_O_OUT);
       else
@@ -1235,9 +1253,7 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
 #pragma unroll
           for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
         }
-        prep(e + OSTAGE, blk_next, rs, mb);
-        k_addr(e + 2 < e1 ? e + 2 : e + 1);
-        v_addr(e + 1);
+        prep_next(e + OSTAGE, blk_next);
       }
     };
     step(e0, std::true_type{});

@@ -44,7 +44,7 @@ The MFMA is v_mfma_f32_32x32x16_bf16 throughout. Run: python gen_own_asm.py
 import os
 
 KSTEPS = 36          # 576 features / 16
-PF_K = int(os.environ.get("OWN_PF_K", "5"))   # K fragments in flight
+PF_K = int(os.environ.get("OWN_PF_K", "4"))   # K fragments in flight
 PF_V = int(os.environ.get("OWN_PF_V", "5"))   # V^T fragments in flight (two reads each)
 NEG_INF = "0xff800000"
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +76,7 @@ DMA_S = [1, 5, 9, 13, 17, 21, 25, 29, 33]
 DMA_P = []
 S_VALU_STEPS = 16    # score MFMAs that carry the probability half of the softmax
 P_VALU_FROM = 3      # PV MFMA after which the max half of the softmax starts
+BOOK_FROM = 4        # PV MFMA after which the scalar bookkeeping starts
 
 
 class Seq:
@@ -137,18 +138,22 @@ def vread(seq, j):
 
 
 def dma_m0(seq, cg, mb="mb"):
-    """M0 = LDS base of line cg of this wave's share of a stage. The copy that
-    reads it must not be the next instruction (one wait state)."""
-    seq.op("s_add_u32 m0, %%[%s], 0x%x" % (mb, cg * 1024))
+    """M0 for line cg of this wave's share of a stage. A buffer -> LDS copy
+    adds its instruction offset (cg * 128, see dma_load) to the LDS address
+    as well as to the memory address, so M0 = line base - cg * 128 and the
+    line lands at mb + cg * 1024. The copy that reads M0 must not be the
+    next instruction (one wait state)."""
+    seq.op("s_add_u32 m0, %%[%s], 0x%x" % (mb, cg * (1024 - 128)))
 
 
 def dma_load(seq, cg, rs="rs"):
     """Line cg: buffer -> LDS copy of 1 KiB to M0 (the copy counts in vmcnt,
-    not lgkmcnt). The cache is read once per call, so the copy is marked
-    non-temporal (nt): it streams past the caches instead of displacing the
-    split partials the merge reads right after (measured ~2 % faster per
-    call, same results)."""
-    seq.op("buffer_load_dwordx4 %%[go], %%[%s], %%[so%d] offen nt lds" % (rs, cg))
+    not lgkmcnt): the wave's 8 tokens (soffset so) at column group cg
+    (instruction offset cg * 128). The cache is read once per call, so the
+    copy is marked non-temporal (nt): it streams past the caches instead of
+    displacing the split partials the merge reads right after (measured ~2 %
+    faster per call, same results)."""
+    seq.op("buffer_load_dwordx4 %%[go], %%[%s], %%[so] offen offset:%d nt lds" % (rs, cg * 128))
 
 
 def dma(seq, cg, mb="mb", rs="rs"):
@@ -220,6 +225,38 @@ def softmax_exp():
     return v
 
 
+NEG_STAGES = "0xfffe5000"    # -3 stages of 36,864 bytes: from stage 3 back to stage 0
+STAGE = "0x9000"
+
+
+def book_keeping():
+    """Address work for the next sequence, spread over the PV MFMAs (a lone
+    wave issues about one instruction per four cycles, so this costs no MFMA
+    time here, unlike code between the sequences): the K addresses of the
+    next scores (stage e + 2, or e + 1 again past e1), then, after the last
+    V^T read, the V^T addresses of the next PV (stage e + 1) and the next
+    mask limit. Stage deltas come from the uniform input ep = e + 4 through
+    scratch SGPRs; SCC chains are contiguous. Returns (main, tail)."""
+    b = [
+        "s_sub_i32 %[t0], %[ep], 2",
+        "s_and_b32 %[t1], %[t0], 3",
+        "s_cmp_eq_u32 %[t1], 0",
+        "s_mov_b32 %[t1], " + STAGE,          # (one literal per scalar instruction)
+        "s_cselect_b32 %[t1], " + NEG_STAGES + ", %[t1]",
+        "s_cmp_lt_i32 %[t0], %[e1]",
+        "s_cselect_b32 %[t1], %[t1], 0",
+    ] + ["v_add_u32 %%[ka%d], %%[t1], %%[ka%d]" % (q, q) for q in range(4)]
+    tail = [
+        "v_subrev_u32 %[lr], 32, %[lr]",
+        "s_sub_i32 %[t2], %[ep], 3",
+        "s_and_b32 %[t2], %[t2], 3",
+        "s_cmp_eq_u32 %[t2], 0",
+        "s_mov_b32 %[t2], " + STAGE,
+        "s_cselect_b32 %[t2], " + NEG_STAGES + ", %[t2]",
+    ] + ["v_add_u32 %%[va%d], %%[t2], %%[va%d]" % (q, q) for q in range(4)]
+    return b, tail
+
+
 def gen_qload():
     """Start of a segment: the copies of the first half tile, the 36 query
     fragments straight into registers (row 32 wave + l % 32 at byte offset
@@ -228,7 +265,7 @@ def gen_qload():
     memory results count down in issue order)."""
     s = Seq()
     for cg in range(9):
-        dma(s, cg, "mb0", "rs0")
+        dma(s, cg, "mb0", "rs0")   # lines of half tile e0
     for ks in range(KSTEPS):
         s.op("buffer_load_dwordx4 %%[q%d], %%[qv], %%[qr], 0 offen offset:%d" % (ks, 32 * ks))
     for st in (1, 2):
@@ -284,9 +321,13 @@ def gen_iter(mask, first):
     while vnext < PF_V:
         vread(s, vnext)
         vnext += 1
+    book, book_tail = book_keeping()
     max_valu = softmax_max(mask)
-    nsteps = 32 - P_VALU_FROM - 2
+    nsteps = 32 - P_VALU_FROM - 6
     mper = (len(max_valu) + nsteps - 1) // nsteps
+    # bookkeeping from PV step BOOK_FROM on, the V^T address update after the
+    # last V^T read (issued at step 31 - PF_V), the rescale test at the end
+    bper = (len(book) + (31 - PF_V - BOOK_FROM) - 1) // (31 - PF_V - BOOK_FROM)   # at least one per step
     for j in range(32):
         s.need("V%db" % j)
         cb, kk = pv_step(j)
@@ -305,6 +346,14 @@ def gen_iter(mask, first):
             k = j - P_VALU_FROM
             for ins in max_valu[k * mper:(k + 1) * mper]:
                 s.op(ins)
+        if BOOK_FROM <= j < 31 - PF_V:
+            k = j - BOOK_FROM
+            for ins in book[k * bper:(k + 1) * bper]:
+                s.op(ins)
+        if j == 32 - PF_V:
+            for ins in book_tail:
+                s.op(ins)
+    assert (32 - P_VALU_FROM - 6) * mper >= len(max_valu) and (31 - PF_V - BOOK_FROM) * bper >= len(book)
     s.drain()
     return s.text()
 
@@ -316,7 +365,8 @@ def main():
     # IT (key mask) the last ones of a sequence and the causal block
     # (one asm statement holding both, chosen by a scalar branch, so that the
     # loop has a single call site and one register assignment)
-    it_sel = ("s_cmp_lg_u32 %[open], 0\\n\\ts_cbranch_scc1 own_open_%=\\n\\t" + gen_iter(True, False)
+    it_sel = ("s_sub_i32 %[t0], %[ep], 3\\n\\ts_cmp_lt_i32 %[t0], %[eo]\\n\\t"
+              "s_cbranch_scc1 own_open_%=\\n\\t" + gen_iter(True, False)
               + "s_branch own_done_%=\\n\\town_open_%=:\\n\\t" + gen_iter(False, False) + "own_done_%=:\\n\\t")
     temps = [("OWN_ASM_QLOAD", gen_qload()), ("OWN_ASM_PRO", gen_pro(True)), ("OWN_ASM_IT", it_sel),
              ("OWN_ASM_IT_FIRST", gen_iter(True, True)),
@@ -329,12 +379,16 @@ def main():
         "OWN_OPS_Q": ", ".join('[q%d] "v"(qf[%d])' % (i, i) for i in range(KSTEPS)),
         "OWN_OPS_Q_OUT": ", ".join('[q%d] "=&v"(qf[%d])' % (i, i) for i in range(KSTEPS)),
         "OWN_OPS_KA": ", ".join('[ka%d] "v"(ka[%d])' % (i, i) for i in range(4)),
-        "OWN_OPS_VA": ", ".join('[va%d] "v"(va[%d])' % (i, i) for i in range(4)),
+        "OWN_OPS_KA_IO": ", ".join('[ka%d] "+v"(ka[%d])' % (i, i) for i in range(4)),
+        "OWN_OPS_VA_IO": ", ".join('[va%d] "+v"(va[%d])' % (i, i) for i in range(4)),
+        # bookkeeping operands: scratch SGPRs (outputs never read), then uniform inputs
+        "OWN_OPS_BOOK_OUT": '[t0] "=&s"(t0), [t1] "=&s"(t1), [t2] "=&s"(t2)',
+        "OWN_OPS_BOOK_IN": '[ep] "s"(e + OSTAGE), [eo] "s"(e_open), [e1] "s"(e1), [mb] "s"(mb)',
         "OWN_OPS_S_OUT": ", ".join('[s%d] "=&v"(s[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_S": ", ".join('[s%d] "+v"(s[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_O": ", ".join('[o%d] "+a"(o[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_O_OUT": ", ".join('[o%d] "=&a"(o[%d])' % (i, i) for i in range(16)),
-        "OWN_OPS_SO": ", ".join('[so%d] "s"(so[%d])' % (i, i) for i in range(9)),
+        "OWN_OPS_SO": '[so] "s"(so)',
         "OWN_CLOB": ", ".join('"v%d"' % r for r in range(CLOB_LO, 256)),
     }
     for name, text in ops.items():
