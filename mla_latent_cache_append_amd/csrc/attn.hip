@@ -1321,8 +1321,14 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rb = (a.rows + 3) >> 2;           // workgroups per sequence, four rows each
-  const int b = (int)(blockIdx.x / (unsigned)rb);
-  const int r = (int)(blockIdx.x - (unsigned)b * (unsigned)rb) * 4 + wave;
+  // Workgroups are dealt to the 8 XCDs round-robin by id. The split kernels
+  // give each XCD a contiguous run of ranges (so the partials of one
+  // sequence sit in that XCD's L2); give each XCD the same contiguous run of
+  // (sequence, rows) items here, so that the merge reads them from there.
+  unsigned item = blockIdx.x;
+  if ((gridDim.x & 7) == 0) item = (item & 7) * (gridDim.x >> 3) + (item >> 3);
+  const int b = (int)(item / (unsigned)rb);
+  const int r = (int)(item - (unsigned)b * (unsigned)rb) * 4 + wave;
   if (r >= a.rows) return;
   // total tiles T, first tile of sequence b, and its tile count
   int64_t T = 0, start = 0;
