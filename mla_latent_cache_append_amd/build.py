@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_absorb.so")
 PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
-SOURCES = ["append.hip", "gemm.hip", "linear.hip", "attn.hip", "capi.cpp"]
+SOURCES = ["append.hip", "gemm.hip", "linear.hip", "attn.hip", "plan.cpp", "capi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -44,8 +44,6 @@ namespace mla {
 
 // ------------------------------------------------------------------ plan
 
-constexpr int TARGET_WGS = 256;   // one workgroup per CU on a 256-CU MI355X
-
 __device__ __forceinline__ int tiles_of(int L, int max_blocks) {
   L = max(L, 0);
   L = min(L, max_blocks * BLOCK);
@@ -1409,64 +1407,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-enum { V_ROWS128 = 0, V_ROWS64 = 1, V_COLS32 = 2, V_COLS16 = 3 };
-
-AttnPlan plan_attention(int32_t B, int32_t Lq, int32_t H) {
-  (void)B;
-  AttnPlan p;
-  const int rows = Lq * H;
-  if (rows >= 96) { p.variant = V_ROWS128; p.rg_rows = 128; }
-  else if (rows >= 48) { p.variant = V_ROWS64; p.rg_rows = 64; }
-  else if (rows >= 32) { p.variant = V_COLS32; p.rg_rows = 32; }
-  else { p.variant = V_COLS16; p.rg_rows = 16; }
-  p.n_rg = (rows + p.rg_rows - 1) / p.rg_rows;
-  p.width = (TARGET_WGS + p.n_rg - 1) / p.n_rg;
-  return p;
-}
-
-// FP8 pool: the column kernel for every shape, 16 or 32 rows per row group.
-AttnPlan plan_attention_fp8(int32_t B, int32_t Lq, int32_t H) {
-  (void)B;
-  AttnPlan p;
-  const int rows = Lq * H;
-  if (rows <= 16) { p.variant = V_COLS16; p.rg_rows = 16; }
-  else { p.variant = V_COLS32; p.rg_rows = 32; }
-  p.n_rg = (rows + p.rg_rows - 1) / p.rg_rows;
-  p.width = (TARGET_WGS + p.n_rg - 1) / p.n_rg;
-  return p;
-}
-
-// Two-buffer layout (kv_cache + pe_cache): the column kernel up to 47 rows
-// per sequence, the 64-row kernel above (the 128-row kernel's copy sequences
-// are written for the paged pool's 1,152-byte rows).
-AttnPlan plan_attention_kvpe(int32_t B, int32_t Lq, int32_t H) {
-  AttnPlan p = plan_attention(B, Lq, H);
-  if (p.variant == V_ROWS128) {
-    p.variant = V_ROWS64;
-    p.rg_rows = 64;
-    p.n_rg = (Lq * H + 63) / 64;
-    p.width = (TARGET_WGS + p.n_rg - 1) / p.n_rg;
-  }
-  return p;
-}
-
-// Workspace: (m, l) of every partial in fp32, then the partials themselves
-// in bf16, normalized by their l, starting on a 256-byte boundary. Sized for
-// the widest of the plans, so one workspace serves every cache format and layout.
-static size_t ws_slots(int32_t B, int32_t Lq, int32_t H) {
-  const int w = max(max(plan_attention(B, Lq, H).width, plan_attention_fp8(B, Lq, H).width),
-                    plan_attention_kvpe(B, Lq, H).width);
-  return (size_t)w + (size_t)B;
-}
-static size_t ws_ml_bytes(int32_t B, int32_t Lq, int32_t H) {
-  const size_t bytes = ws_slots(B, Lq, H) * (size_t)Lq * (size_t)H * 2 * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
-}
-
-size_t attention_workspace_bytes(int32_t B, int32_t Lq, int32_t H) {
-  return ws_ml_bytes(B, Lq, H) + ws_slots(B, Lq, H) * (size_t)Lq * (size_t)H * D_C * sizeof(uint16_t);
-}
-
 // pe != null: the two-buffer layout, pool = kv_cache, max_keys = max_seq
 // (max_blocks = ceil(max_seq / 64), no block table); otherwise the paged pool
 // (max_keys = max_blocks * 64).
@@ -1487,7 +1427,7 @@ static hipError_t launch_attention(const uint16_t* q, const void* pool, const ui
   a.o_lat = o_lat;
   a.lse = lse;
   a.ws_ml = (float*)workspace;
-  a.ws_acc = (uint16_t*)((char*)workspace + ws_ml_bytes(B, Lq, H));
+  a.ws_acc = (uint16_t*)((char*)workspace + attention_ws_ml_bytes(B, Lq, H));
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks;
   a.max_keys = max_keys;

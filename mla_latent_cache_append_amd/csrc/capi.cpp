@@ -23,6 +23,21 @@ int launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUN
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Attention shapes the kernels index with 32-bit arithmetic: the rows of one
+// sequence (Lq * H <= 2^20) and the merge's grid (one workgroup per four
+// query rows of every sequence).
+bool attn_shape_ok(int32_t B, int32_t Lq, int32_t H) {
+  const int64_t rows = (int64_t)Lq * H;
+  return rows <= (1 << 20) && (int64_t)B * ((rows + 3) / 4) <= 0x7fffffff;
+}
+
+// Linear maps: K a multiple of 32, M of 4, both at most 2^30; at most 65,535
+// workgroup rows of 32 tokens.
+int linear_shape(int32_t N, int32_t K, int32_t M) {
+  if (K % 32 != 0 || M % 4 != 0 || N > 65535 * 32 || K > (1 << 30) || M > (1 << 30)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
 // The attention kernels move 16 bytes per lane through q, the cache, o_lat
 // and the workspace, and read token scales four at a time.
 bool attn_aligned(const void* q, const void* pool, const void* pool_scale, const void* o_lat,
@@ -80,7 +95,7 @@ int mla_absorb_q(const mla_dims* dims, const uint16_t* q_nope, const uint16_t* q
 }
 
 size_t mla_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t Lq) {
-  if (check_dims(dims) != MLA_OK || B <= 0 || Lq <= 0) return 0;
+  if (check_dims(dims) != MLA_OK || B <= 0 || Lq <= 0 || !attn_shape_ok(B, Lq, dims->num_heads)) return 0;
   return mla::attention_workspace_bytes(B, Lq, dims->num_heads);
 }
 
@@ -96,10 +111,8 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
     return MLA_ERR_INVALID_ARG;
   if (!attn_aligned(q, pool, nullptr, o_lat, lse, workspace)) return MLA_ERR_INVALID_ARG;
   // rows of one sequence index 32-bit offsets inside the kernels
-  if ((int64_t)Lq * dims->num_heads > (1 << 20) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
+  if (!attn_shape_ok(B, Lq, dims->num_heads) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
     return MLA_ERR_UNSUPPORTED;
-  // the merge launches one workgroup per four query rows of every sequence
-  if ((int64_t)B * (((int64_t)Lq * dims->num_heads + 3) / 4) > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
   const size_t need = mla::attention_workspace_bytes(B, Lq, dims->num_heads);
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   return launch_status(mla::launch_decode_attn(q, pool, num_blocks, block_table, max_blocks_per_seq,
@@ -119,9 +132,8 @@ int mla_decode_attn_noalloc(const mla_dims* dims, const uint16_t* q, const uint1
       max_blocks_per_seq <= 0 || B <= 0 || Lq <= 0)
     return MLA_ERR_INVALID_ARG;
   if (!attn_aligned(q, pool, nullptr, o_lat, lse, nullptr)) return MLA_ERR_INVALID_ARG;
-  if ((int64_t)Lq * dims->num_heads > (1 << 20) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
+  if (!attn_shape_ok(B, Lq, dims->num_heads) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
     return MLA_ERR_UNSUPPORTED;
-  if ((int64_t)B * (((int64_t)Lq * dims->num_heads + 3) / 4) > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
   if (mla::attention_workspace_bytes(B, Lq, dims->num_heads) > mla::NOALLOC_SCRATCH_BYTES)
     return MLA_ERR_WORKSPACE;
   const hipError_t e = mla::launch_decode_attn_noalloc(q, pool, num_blocks, block_table, max_blocks_per_seq,
@@ -183,9 +195,8 @@ int mla_decode_attn_fp8(const mla_dims* dims, const uint16_t* q, const uint8_t* 
       max_blocks_per_seq <= 0 || B <= 0 || Lq <= 0)
     return MLA_ERR_INVALID_ARG;
   if (!attn_aligned(q, pool8, pool_scale, o_lat, lse, workspace)) return MLA_ERR_INVALID_ARG;
-  if ((int64_t)Lq * dims->num_heads > (1 << 20) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
+  if (!attn_shape_ok(B, Lq, dims->num_heads) || (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
     return MLA_ERR_UNSUPPORTED;
-  if ((int64_t)B * (((int64_t)Lq * dims->num_heads + 3) / 4) > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
   const size_t need = mla::attention_workspace_bytes(B, Lq, dims->num_heads);
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   return launch_status(mla::launch_decode_attn_fp8(q, pool8, pool_scale, num_blocks, block_table,
@@ -215,8 +226,7 @@ int mla_decode_attn_kvpe(const mla_dims* dims, const uint16_t* q, const uint16_t
   if (!q || !kv_cache || !pe_cache || !seq_lens || !o_lat || max_seq <= 0 || B <= 0 || Lq <= 0)
     return MLA_ERR_INVALID_ARG;
   if (!attn_aligned(q, kv_cache, pe_cache, o_lat, lse, workspace)) return MLA_ERR_INVALID_ARG;
-  if ((int64_t)Lq * dims->num_heads > (1 << 20) || max_seq > (1 << 30)) return MLA_ERR_UNSUPPORTED;
-  if ((int64_t)B * (((int64_t)Lq * dims->num_heads + 3) / 4) > 0x7fffffff) return MLA_ERR_UNSUPPORTED;
+  if (!attn_shape_ok(B, Lq, dims->num_heads) || max_seq > (1 << 30)) return MLA_ERR_UNSUPPORTED;
   const size_t need = mla::attention_workspace_bytes(B, Lq, dims->num_heads);
   if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
   return launch_status(mla::launch_decode_attn_kvpe(q, kv_cache, pe_cache, max_seq, seq_lens, B, Lq,
@@ -234,7 +244,7 @@ int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv
 }
 
 size_t mla_linear_workspace_size(int32_t N, int32_t K, int32_t M) {
-  if (N <= 0 || K <= 0 || M <= 0 || K % 32 != 0 || M % 4 != 0 || N > 65535 * 32) return 0;
+  if (N <= 0 || K <= 0 || M <= 0 || linear_shape(N, K, M) != MLA_OK) return 0;
   return mla::plan_linear(N, K, M, true).ws_bytes;
 }
 
@@ -242,7 +252,7 @@ int mla_linear(const uint16_t* x, const uint16_t* w, const uint16_t* residual, u
                int32_t N, int32_t K, int32_t M, void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !w || !y || N <= 0 || K <= 0 || M <= 0) return MLA_ERR_INVALID_ARG;
   if (workspace && ((uintptr_t)workspace % 16 != 0)) return MLA_ERR_INVALID_ARG;
-  if (K % 32 != 0 || M % 4 != 0 || N > 65535 * 32) return MLA_ERR_UNSUPPORTED;
+  if (linear_shape(N, K, M) != MLA_OK) return MLA_ERR_UNSUPPORTED;
   return launch_status(mla::launch_linear(x, w, residual, y, workspace, workspace ? workspace_bytes : 0, N, K, M,
                                           (hipStream_t)stream));
 }

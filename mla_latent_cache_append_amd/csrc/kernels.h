@@ -20,6 +20,11 @@ constexpr int ROW_BYTES = D_K * 2;              // 1,152
 constexpr int BLOCK_BYTES = BLOCK * ROW_BYTES;  // 73,728
 constexpr int ROW_CHUNKS = ROW_BYTES / 16;      // 72 sixteen-byte chunks per row
 
+// Launch shapes, shared by the host plans (plan.cpp) and the kernels.
+constexpr int TARGET_WGS = 256;  // attention: one workgroup per CU on a 256-CU MI355X
+constexpr int LIN_N = 32;        // linear: tokens per workgroup (two 16-token MFMA tiles)
+constexpr int LIN_WAVES = 16;    // linear: waves per workgroup, each a slice of the contraction
+
 hipError_t launch_cache_append(const uint16_t* c_kv, const uint16_t* k_pe, const int32_t* pos,
                                const int64_t* slot_mapping, uint16_t* pool, int64_t num_blocks,
                                int32_t T, double rope_base, hipStream_t stream);
@@ -56,6 +61,8 @@ hipError_t launch_linear(const uint16_t* x, const uint16_t* w, const uint16_t* r
                          size_t workspace_bytes, int32_t N, int32_t K, int32_t M, hipStream_t stream);
 
 // Split-KV plan shared by the host (workspace sizing, grid) and the kernels.
+// Kernel shapes: the 128-row and 64-row kernels, the 32- and 16-row column kernels.
+enum { V_ROWS128 = 0, V_ROWS64 = 1, V_COLS32 = 2, V_COLS16 = 3 };
 struct AttnPlan {
   int variant;    // kernel shape, see attn.hip
   int rg_rows;    // query rows per workgroup (row group)
@@ -69,6 +76,8 @@ AttnPlan plan_attention_kvpe(int32_t B, int32_t Lq, int32_t H);
 
 // Partial-result slots of one call: width + B (one per (workgroup, sequence) pair).
 size_t attention_workspace_bytes(int32_t B, int32_t Lq, int32_t H);
+// Bytes of the workspace's (m, l) part; the bf16 partials start there.
+size_t attention_ws_ml_bytes(int32_t B, int32_t Lq, int32_t H);
 
 hipError_t launch_decode_attn(const uint16_t* q, const uint16_t* pool, int64_t num_blocks,
                               const int32_t* block_table, int32_t max_blocks,

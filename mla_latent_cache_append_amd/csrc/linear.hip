@@ -46,9 +46,6 @@
 
 namespace mla {
 
-constexpr int LIN_N = 32;      // tokens per workgroup (two 16-token MFMA tiles)
-constexpr int LIN_WAVES = 16;  // waves per workgroup, each a slice of the contraction
-
 // x [N][K], w [M][K], r and y [N][M], all bf16; ws [KS][N][M] fp32 when
 // SPLIT. LIN_U narrow steps per wave have their loads in flight together.
 // K is a multiple of the step width (32 or 128) and M of 4; split z
@@ -191,42 +188,6 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* ws, con
     s1 += bf16_to_f32((uint16_t)(rv >> 16));
   }
   *(uint32_t*)(y + i) = pack_bf16x2(s0, s1);
-}
-
-LinearPlan plan_linear(int32_t N, int32_t K, int32_t M, bool can_split) {
-  LinearPlan p;
-  const int64_t ny = (N + LIN_N - 1) / LIN_N;
-  auto wgs = [&](int mt) { return (int64_t)((M + 16 * mt - 1) / (16 * mt)) * ny; };
-  p.ks = 1;
-  if (wgs(4) >= 224) {
-    // wide outputs: 64 features per workgroup halve the activation bytes
-    // each workgroup streams per weight byte; all of a wave's steps in one
-    // batch of loads when they fit three
-    p.wide = false;
-    p.mt = 4;
-    p.u = K / 32 <= 3 * LIN_WAVES ? 3 : 2;
-  } else if (K % 128 != 0 || K > 8192) {
-    p.wide = false;
-    if (can_split && K >= 8192 && 2 * wgs(4) >= 224) {
-      p.mt = 4;     // long contraction: 64 features, halves of it on their own workgroups
-      p.ks = 2;
-      p.u = 2;
-    } else {
-      p.mt = wgs(2) >= 128 ? 2 : 1;
-      p.u = 4;
-    }
-  } else {
-    p.wide = true;
-    p.mt = M >= 1024 ? 2 : 1;
-    p.u = 1;
-    if (can_split && wgs(p.mt) < 128) {
-      // about 192 workgroups, each slice keeping at least three steps
-      const int64_t want = (192 + wgs(p.mt) - 1) / wgs(p.mt), most = (K / 128) / 3;
-      p.ks = (int)std::max<int64_t>(1, std::min(want, most));
-    }
-  }
-  p.ws_bytes = p.ks > 1 ? (size_t)p.ks * (size_t)N * (size_t)M * sizeof(float) : 0;
-  return p;
 }
 
 template <int MT, bool WIDE, int U>
