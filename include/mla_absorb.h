@@ -113,7 +113,9 @@ int mla_absorb_q(const mla_dims* dims, const uint16_t* q_nope, const uint16_t* q
 /*
  * mla_decode_workspace_size — bytes of device workspace mla_decode_attn needs
  * for B sequences of Lq queries each (partial results of the key-range splits).
- * Pure host arithmetic; depends only on its arguments.
+ * Pure host arithmetic; depends only on its arguments. 0 for arguments the
+ * attention calls reject (invalid dims, B or Lq <= 0, Lq*H above 2^20, or
+ * B*ceil(Lq*H/4) above 2^31-1).
  */
 size_t mla_decode_workspace_size(const mla_dims* dims, int32_t B, int32_t Lq);
 
@@ -324,8 +326,8 @@ size_t mla_linear_workspace_size(int32_t N, int32_t K, int32_t M);
  *              in a fixed order by a second kernel; otherwise the call runs
  *              unsplit and leaves the workspace untouched
  * fp32 accumulation (bf16 MFMA), the residual added in fp32, one rounding to
- * bf16. K must be a multiple of 32 and M of 4, N at most 2,097,120
- * (MLA_ERR_UNSUPPORTED otherwise); null pointers, sizes <= 0 or a misaligned
+ * bf16. K must be a multiple of 32 and M of 4, K and M at most 2^30, N at
+ * most 2,097,120 (MLA_ERR_UNSUPPORTED otherwise); null pointers, sizes <= 0 or a misaligned
  * workspace give MLA_ERR_INVALID_ARG. Deterministic: calls with the same
  * sizes and the same choice (split or not) give the same bits; split and
  * unsplit results differ only in fp32 summation order.
