@@ -104,7 +104,8 @@ int mla_cache_append(const mla_dims* dims, const uint16_t* c_kv, const uint16_t*
  *                               (the head's rows of nn.Linear(d_c, H*d_nope).weight)
  *   q_out   device [N][H][576] bf16
  * The 128-long contraction accumulates in fp32 (bf16 MFMA) and is rounded once
- * to bf16.
+ * to bf16. N above 2^22 gives MLA_ERR_UNSUPPORTED (as for mla_append_absorb
+ * and mla_out_up).
  */
 int mla_absorb_q(const mla_dims* dims, const uint16_t* q_nope, const uint16_t* q_pe,
                  const int32_t* pos, const uint16_t* w_uk, uint16_t* q_out, int32_t N,
@@ -295,7 +296,7 @@ int mla_decode_attn_kvpe(const mla_dims* dims, const uint16_t* q, const uint16_t
  *   o_lat  device [N][H][512] bf16
  *   w_uv   device [H][128][512] bf16  (the head's rows of nn.Linear(d_c, H*d_v).weight)
  *   o      device [N][H][128] bf16
- * fp32 accumulation (bf16 MFMA), one rounding to bf16.
+ * fp32 accumulation (bf16 MFMA), one rounding to bf16. N at most 2^22.
  */
 int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o,
                int32_t N, void* stream);

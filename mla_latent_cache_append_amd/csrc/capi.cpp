@@ -21,6 +21,11 @@ int check_dims(const mla_dims* d) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
 
+// Tokens of one absorb / out_up call: their grids (a workgroup per 256-token
+// run, head and column slice, plus one per four appended tokens) stay within
+// the 2^32 work-items a launch dimension holds.
+constexpr int32_t MAX_TOKENS = 1 << 22;
+
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // Attention shapes the kernels index with 32-bit arithmetic: the rows of one
@@ -90,6 +95,7 @@ int mla_absorb_q(const mla_dims* dims, const uint16_t* q_nope, const uint16_t* q
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (!q_nope || !q_pe || !pos || !w_uk || !q_out || N <= 0) return MLA_ERR_INVALID_ARG;
+  if (N > MAX_TOKENS) return MLA_ERR_UNSUPPORTED;
   return launch_status(mla::launch_absorb_q(q_nope, q_pe, pos, w_uk, q_out, N, dims->num_heads,
                                             (double)dims->rope_base, (hipStream_t)stream));
 }
@@ -151,6 +157,7 @@ int mla_append_absorb(const mla_dims* dims, const uint16_t* c_kv, const uint16_t
   if (!c_kv || !k_pe || !slot_mapping || !pool || num_blocks <= 0 || !q_nope || !q_pe || !pos || !w_uk ||
       !q_out || N <= 0)
     return MLA_ERR_INVALID_ARG;
+  if (N > MAX_TOKENS) return MLA_ERR_UNSUPPORTED;
   return launch_status(mla::launch_append_absorb(c_kv, k_pe, slot_mapping, pool, nullptr, num_blocks, q_nope,
                                                  q_pe, pos, w_uk, q_out, N, dims->num_heads,
                                                  (double)dims->rope_base, (hipStream_t)stream));
@@ -166,6 +173,7 @@ int mla_append_absorb_fp8(const mla_dims* dims, const uint16_t* c_kv, const uint
   if (!c_kv || !k_pe || !slot_mapping || !pool8 || !pool_scale || num_blocks <= 0 || !q_nope || !q_pe ||
       !pos || !w_uk || !q_out || N <= 0)
     return MLA_ERR_INVALID_ARG;
+  if (N > MAX_TOKENS) return MLA_ERR_UNSUPPORTED;
   return launch_status(mla::launch_append_absorb(c_kv, k_pe, slot_mapping, pool8, pool_scale, num_blocks,
                                                  q_nope, q_pe, pos, w_uk, q_out, N, dims->num_heads,
                                                  (double)dims->rope_base, (hipStream_t)stream));
@@ -239,6 +247,7 @@ int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (!o_lat || !w_uv || !o || N <= 0) return MLA_ERR_INVALID_ARG;
+  if (N > MAX_TOKENS) return MLA_ERR_UNSUPPORTED;
   return launch_status(
       mla::launch_out_up(o_lat, w_uv, o, N, dims->num_heads, (hipStream_t)stream));
 }

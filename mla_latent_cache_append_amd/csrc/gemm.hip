@@ -35,13 +35,38 @@ __device__ __forceinline__ int aq_swz(int j) { return 2 * (j & 3) + 8 * ((j >> 3
 // (8 consecutive j of one column c) comes from two transposing LDS reads
 // (ds_read_b64_tr_b16) of the row-major slice.
 constexpr int AQ_LDS = D_NOPE * AQ_COLS * 2;   // 32 KiB weight slice
+// A pass's outputs (32 tokens x 128 columns) go through LDS on their way out,
+// so that 16 consecutive lanes store one token's 256 contiguous bytes (whole
+// 128-byte lines) rather than 32-byte pieces of 16 tokens. Rows are padded
+// to 272 bytes: the 16 tokens of one fragment write land on distinct banks.
+// The staging reuses the weight slice's LDS once its fragments are in registers.
+constexpr int AQ_OSTRIDE = AQ_COLS * 2 + 16;
+static_assert(32 * AQ_OSTRIDE <= AQ_LDS, "output staging fits in the weight slice's LDS");
+
+// Tokens per absorb workgroup: one workgroup per (head, column slice) sweeps
+// a decode batch whole; a prefill-sized batch is split into runs of this many
+// tokens, each on its own workgroups (grid H * 4 * ceil(N / AQ_TPW)).
+constexpr int AQ_TPW = 256;
+__host__ __device__ constexpr int aq_runs(int N) { return (N + AQ_TPW - 1) / AQ_TPW; }
 
 __device__ __forceinline__ void absorb_q_block(
     int blk, char* wl, const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const int32_t* __restrict__ pos, const uint16_t* __restrict__ w_uk,
     uint16_t* __restrict__ q_out, int N, int H, const RopeFreqs& fr) {
-  const int h = blk / AQ_CHUNKS;
-  const int chunk = blk % AQ_CHUNKS;
+  // Workgroups are dealt to the 8 XCDs round-robin by id. The four column
+  // slices of one (token run, head) read the same query rows: give them ids
+  // 8 apart, so they share an XCD and its L2 (when the count allows).
+  int chunk, item;
+  if (((H * aq_runs(N)) & 7) == 0) {
+    chunk = (blk >> 3) & 3;
+    item = ((blk >> 5) << 3) | (blk & 7);
+  } else {
+    chunk = blk % AQ_CHUNKS;
+    item = blk / AQ_CHUNKS;
+  }
+  const int run = item / H;
+  const int h = item - run * H;
+  const int n_begin = run * AQ_TPW, n_end = min(N, n_begin + AQ_TPW);
   const int c0 = chunk * AQ_COLS;
   const uint16_t* w = w_uk + (int64_t)h * D_NOPE * D_C + c0;
   __attribute__((address_space(3))) char* wls = (__attribute__((address_space(3))) char*)wl;
@@ -50,24 +75,40 @@ __device__ __forceinline__ void absorb_q_block(
   // B = q_nope^T[K = j][N = token] of two 16-token blocks: lane (g, c) holds
   // token n0 + 16 tb + c, rows 32 ks + 8 g .. +7. Lanes past the last token
   // load a valid row; their columns are not stored.
-  bf16x8 bq[2][D_NOPE / 32];
-  auto load_q = [&](int n0) {
+  bf16x8 bq[2][D_NOPE / 32], bn[2][D_NOPE / 32];
+  auto load_q = [&](bf16x8 (&dst)[2][D_NOPE / 32], int n0) {
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int n = min(n0 + 16 * tb + c, N - 1);
+      const int n = min(n0 + 16 * tb + c, n_end - 1);
       const uint16_t* src = q_nope + ((int64_t)n * H + h) * D_NOPE + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < D_NOPE / 32; ++ks) bq[tb][ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
+      for (int ks = 0; ks < D_NOPE / 32; ++ks) dst[tb][ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
     }
   };
-  load_q(0);   // in flight together with the weight slice
+  load_q(bq, n_begin);   // in flight together with the weight slice
   {
-    // rope pairs p = (token p / 32, pair p % 32) of head h: q_out[n][h][512 + 2i .. +1]
-    const int npairs = N * (D_ROPE / 2);
-    for (int p = chunk * 256 + (int)threadIdx.x; p < npairs; p += AQ_CHUNKS * 256) {
+    // rope pairs p = (token p / 32, pair p % 32) of head h: q_out[n][h][512 + 2i .. +1];
+    // this slice takes every fourth group of 256, at most AQ_TPW / 32 per
+    // thread, with all the loads issued before the rotations
+    constexpr int RP = AQ_TPW * (D_ROPE / 2) / (AQ_CHUNKS * 256);
+    const int npairs = n_end * (D_ROPE / 2);
+    const int p0 = n_begin * (D_ROPE / 2) + chunk * 256 + (int)threadIdx.x;
+    uint32_t x[RP];
+    int ps[RP];
+#pragma unroll
+    for (int u = 0; u < RP; ++u) {
+      const int p = min(p0 + u * AQ_CHUNKS * 256, npairs - 1);
       const int n = p / (D_ROPE / 2), i = p % (D_ROPE / 2);
-      const uint32_t x = *(const uint32_t*)(q_pe + ((int64_t)n * H + h) * D_ROPE + 2 * i);
-      *(uint32_t*)(q_out + ((int64_t)n * H + h) * D_K + D_C + 2 * i) = rope_pair_bf16(x, pos[n], fr.f[i]);
+      x[u] = *(const uint32_t*)(q_pe + ((int64_t)n * H + h) * D_ROPE + 2 * i);
+      ps[u] = pos[n];
+    }
+#pragma unroll
+    for (int u = 0; u < RP; ++u) {
+      const int p = p0 + u * AQ_CHUNKS * 256;
+      if (p < npairs) {
+        const int n = p / (D_ROPE / 2), i = p % (D_ROPE / 2);
+        *(uint32_t*)(q_out + ((int64_t)n * H + h) * D_K + D_C + 2 * i) = rope_pair_bf16(x[u], ps[u], fr.f[i]);
+      }
     }
   }
   {
@@ -103,24 +144,43 @@ __device__ __forceinline__ void absorb_q_block(
       af[cb][ks] = join_tr(v0, v1);
     }
   }
-  // two 16-token blocks per pass, all their loads in flight before the products
-  for (int n0 = 0; n0 < N; n0 += 32) {
-    if (n0 > 0) load_q(n0);
+  __syncthreads();   // every wave holds its fragments: the slice's LDS becomes the output staging
+  // two 16-token blocks per pass; the next pass's query loads are issued
+  // before this pass's products
+  __attribute__((address_space(3))) char* ols = wls;
+  for (int n0 = n_begin; n0 < n_end; n0 += 32) {
+    const bool more = n0 + 32 < n_end;
+    if (more) load_q(bn, n0 + 32);
     __builtin_amdgcn_sched_barrier(0);
+    if (n0 > n_begin) __syncthreads();   // the previous pass's rows have been stored
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int n = n0 + 16 * tb + c;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D_NOPE / 32; ++ks) acc = mfma16x16x32(af[cb][ks], bq[tb][ks], acc);
-        if (n < N) {
-          // lane holds columns c0 + 32 wave + 16 cb + 4 g + i (i = 0..3) of token n
-          const u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-          *(u32x2*)(q_out + ((int64_t)n * H + h) * D_K + c0 + 32 * wave + 16 * cb + 4 * g) = out;
-        }
+        // lane holds columns 32 wave + 16 cb + 4 g + i (i = 0..3) of token 16 tb + c of the pass
+        const u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        *(__attribute__((address_space(3))) u32x2*)(ols + (16 * tb + c) * AQ_OSTRIDE +
+                                                     (32 * wave + 16 * cb + 4 * g) * 2) = out;
       }
+    }
+    __syncthreads();
+    // 32 tokens x 16 chunks of 16 bytes: chunk k = 16 t + piece, two per thread
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = u * 256 + (int)threadIdx.x, t = k >> 4, piece = k & 15;
+      const int n = n0 + t;
+      if (n < n_end)
+        *(u32x4*)(q_out + ((int64_t)n * H + h) * D_K + c0 + 8 * piece) =
+            *(const __attribute__((address_space(3))) u32x4*)(ols + t * AQ_OSTRIDE + 16 * piece);
+    }
+    if (more) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < D_NOPE / 32; ++ks) bq[tb][ks] = bn[tb][ks];
     }
   }
 }
@@ -146,7 +206,7 @@ __global__ __launch_bounds__(256) void append_absorb_kernel(
     const int32_t* __restrict__ pos, const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_out,
     int N, int H, RopeFreqs fr) {
   __shared__ __attribute__((aligned(16))) char wl[AQ_LDS];
-  const int n_absorb = H * AQ_CHUNKS;
+  const int n_absorb = H * AQ_CHUNKS * aq_runs(N);
   if ((int)blockIdx.x < n_absorb) {
     absorb_q_block(blockIdx.x, wl, q_nope, q_pe, pos, w_uk, q_out, N, H, fr);
   } else {
@@ -162,7 +222,7 @@ hipError_t launch_append_absorb(const uint16_t* c_kv, const uint16_t* k_pe, cons
                                 void* pool, float* pool_scale, int64_t num_blocks, const uint16_t* q_nope,
                                 const uint16_t* q_pe, const int32_t* pos, const uint16_t* w_uk,
                                 uint16_t* q_out, int32_t N, int32_t H, double rope_base, hipStream_t stream) {
-  const dim3 grid(H * AQ_CHUNKS + (N + 3) / 4);
+  const dim3 grid(H * AQ_CHUNKS * aq_runs(N) + (N + 3) / 4);
   if (pool_scale)
     hipLaunchKernelGGL(append_absorb_kernel<true>, grid, dim3(256), 0, stream, c_kv, k_pe, slot_mapping, pool,
                        pool_scale, num_blocks * BLOCK, q_nope, q_pe, pos, w_uk, q_out, N, H, rope_freqs(rope_base));
@@ -176,6 +236,8 @@ hipError_t launch_append_absorb(const uint16_t* c_kv, const uint16_t* k_pe, cons
 constexpr int OU_ROWS = 64;                 // W_UV rows (output features) per workgroup
 constexpr int OU_CHUNKS = D_V / OU_ROWS;    // 2 workgroups per head
 constexpr int OU_TOK = 32;                  // tokens per pass (two 16-token MFMA blocks)
+constexpr int OU_TPW = 256;                 // tokens per workgroup (runs of a prefill-sized batch)
+__host__ __device__ constexpr int ou_runs(int N) { return (N + OU_TPW - 1) / OU_TPW; }
 
 // W_UV[h] is stored [128 j][512 c] and the contraction runs over c, the
 // contiguous axis of both W_UV and o_lat. Each wave keeps its 16 rows of
@@ -186,37 +248,58 @@ constexpr int OU_TOK = 32;                  // tokens per pass (two 16-token MFM
 __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict__ o_lat,
                                                      const uint16_t* __restrict__ w_uv,
                                                      uint16_t* __restrict__ o, int N, int H) {
-  __shared__ __attribute__((aligned(16))) char ol[OU_TOK * D_C * 2];
+  // o_lat rows of a pass, then its outputs (32 tokens x 64 features, rows
+  // padded to 144 bytes) on their way to whole-line stores
+  constexpr int OSTRIDE = OU_ROWS * 2 + 16;
+  __shared__ __attribute__((aligned(16))) char ol[OU_TOK * D_C * 2 + OU_TOK * OSTRIDE];
   typedef __attribute__((address_space(3))) char lchar;
   lchar* ols = (lchar*)ol;
-  const int h = blockIdx.x / OU_CHUNKS;
+  lchar* ost = ols + OU_TOK * D_C * 2;
+  // workgroup = (token run, head, half of the head's 128 output rows); the
+  // two halves read the same o_lat rows: ids 8 apart put them on one XCD
+  // (workgroups are dealt to the 8 XCDs round-robin) when the count allows
+  const int x = blockIdx.x;
+  int half, item;
+  if (((H * ou_runs(N)) & 7) == 0) {
+    half = (x >> 3) & 1;
+    item = ((x >> 4) << 3) | (x & 7);
+  } else {
+    half = x % OU_CHUNKS;
+    item = x / OU_CHUNKS;
+  }
+  const int run = item / H;
+  const int h = item - run * H;
+  const int hc = h * OU_CHUNKS + half;
+  const int n_begin = run * OU_TPW, n_end = min(N, n_begin + OU_TPW);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
-  const int j0 = (blockIdx.x % OU_CHUNKS) * OU_ROWS + 16 * wave;
+  const int j0 = (hc % OU_CHUNKS) * OU_ROWS + 16 * wave;
   const uint16_t* w = w_uv + ((int64_t)h * D_V + j0 + c) * D_C;
+  // 2048 chunks of 16 bytes per pass, eight per thread; rows past the last
+  // token repeat a valid row (their outputs are not stored)
+  constexpr int PER = OU_TOK * (D_C / 8) / 256;
+  u32x4 v[PER];
+  auto load_rows = [&](int n0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int k = u * 256 + threadIdx.x, t = k >> 6, q = k & 63;
+      const int n = min(n0 + t, n_end - 1);
+      v[u] = *(const u32x4*)(o_lat + ((int64_t)n * H + h) * D_C + 8 * q);
+    }
+  };
+  load_rows(n_begin);
   bf16x8 af[D_C / 32];
 #pragma unroll
   for (int ks = 0; ks < D_C / 32; ++ks) af[ks] = as_bf16x8(*(const u32x4*)(w + 32 * ks + 8 * g));
-  for (int n0 = 0; n0 < N; n0 += OU_TOK) {
-    if (n0 > 0) __syncthreads();          // the previous pass has read its rows
-    {
-      // 2048 chunks of 16 bytes, eight per thread, all loads before the LDS writes;
-      // rows past the last token repeat a valid row (their outputs are not stored)
-      constexpr int PER = OU_TOK * (D_C / 8) / 256;
-      u32x4 v[PER];
+  for (int n0 = n_begin; n0 < n_end; n0 += OU_TOK) {
+    if (n0 > n_begin) __syncthreads();          // the previous pass has read its rows and stored its outputs
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int k = u * 256 + threadIdx.x, t = k >> 6, q = k & 63;
-        const int n = min(n0 + t, N - 1);
-        v[u] = *(const u32x4*)(o_lat + ((int64_t)n * H + h) * D_C + 8 * q);
-      }
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int k = u * 256 + threadIdx.x, t = k >> 6, q = k & 63;
-        *(__attribute__((address_space(3))) u32x4*)(ols + t * 1024 + ((q ^ (t & 15)) << 4)) = v[u];
-      }
+    for (int u = 0; u < PER; ++u) {
+      const int k = u * 256 + threadIdx.x, t = k >> 6, q = k & 63;
+      *(__attribute__((address_space(3))) u32x4*)(ols + t * 1024 + ((q ^ (t & 15)) << 4)) = v[u];
     }
     __syncthreads();
+    if (n0 + OU_TOK < n_end) load_rows(n0 + OU_TOK);   // the next pass's rows, under this pass's products
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       const int t = 16 * tb + c;
@@ -229,11 +312,18 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
 #pragma unroll
       for (int ks = 0; ks < D_C / 32; ++ks) acc4[ks & 3] = mfma16x16x32(af[ks], bv[ks], acc4[ks & 3]);
       const f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+      // lane holds features j0 + 4 g + i (i = 0..3) of token t of the pass
+      *(__attribute__((address_space(3))) u32x2*)(ost + t * OSTRIDE + (16 * wave + 4 * g) * 2) =
+          u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    }
+    __syncthreads();
+    {
+      // 32 tokens x 8 chunks of 16 bytes, one per thread: 8 lanes store a token's 128 bytes
+      const int t = (int)threadIdx.x >> 3, piece = (int)threadIdx.x & 7;
       const int n = n0 + t;
-      if (n < N) {
-        u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-        *(u32x2*)(o + ((int64_t)n * H + h) * D_V + j0 + 4 * g) = out;
-      }
+      if (n < n_end)
+        *(u32x4*)(o + ((int64_t)n * H + h) * D_V + (hc % OU_CHUNKS) * OU_ROWS + 8 * piece) =
+            *(const __attribute__((address_space(3))) u32x4*)(ost + t * OSTRIDE + 16 * piece);
     }
   }
 }
@@ -241,14 +331,14 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
 hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
                            const uint16_t* w_uk, uint16_t* q_out, int32_t N, int32_t H,
                            double rope_base, hipStream_t stream) {
-  hipLaunchKernelGGL(absorb_q_kernel, dim3(H * AQ_CHUNKS), dim3(256), 0, stream, q_nope, q_pe,
+  hipLaunchKernelGGL(absorb_q_kernel, dim3(H * AQ_CHUNKS * aq_runs(N)), dim3(256), 0, stream, q_nope, q_pe,
                      pos, w_uk, q_out, N, H, rope_freqs(rope_base));
   return hipGetLastError();
 }
 
 hipError_t launch_out_up(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int32_t N,
                          int32_t H, hipStream_t stream) {
-  hipLaunchKernelGGL(out_up_kernel, dim3(H * OU_CHUNKS), dim3(256), 0, stream, o_lat, w_uv, o, N,
+  hipLaunchKernelGGL(out_up_kernel, dim3(H * OU_CHUNKS * ou_runs(N)), dim3(256), 0, stream, o_lat, w_uv, o, N,
                      H);
   return hipGetLastError();
 }

@@ -86,6 +86,8 @@ static void test_append_absorb_out_up() {
                                  wuk.p(), qo.p(), T, nullptr) == MLA_OK);
     EXPECT(mla_out_up(&d, ol.p(), wuk.p(), o.p(), T, nullptr) == MLA_OK);
     EXPECT(mla_out_up(&d, ol.p(), wuk.p(), nullptr, T, nullptr) == MLA_ERR_INVALID_ARG);
+    EXPECT(mla_out_up(&d, ol.p(), wuk.p(), o.p(), (1 << 22) + 1, nullptr) == MLA_ERR_UNSUPPORTED);
+    EXPECT(mla_absorb_q(&d, qn.p(), qp.p(), pos.p(), wuk.p(), qo.p(), (1 << 22) + 1, nullptr) == MLA_ERR_UNSUPPORTED);
   }
 }
 
