@@ -1220,16 +1220,46 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     const uint32_t mb0 = (uint32_t)uni((int)lds_addr(stages + wave * 9 * 1024));
     // copies of half tile ep from block blk: pool + blk * 73,728 + (ep & 1) * 36,864,
     // min(32, L - 32 ep) rows; none past the segment or for a block id outside the pool
+    // Straight-line scalar code (no branches; a lone wave pays for every
+    // taken branch with a refetch): base = pool + blk * 73,728 + (ep & 1) *
+    // 36,864 (bits 47..32 in the descriptor's second word), bytes = 1,152 *
+    // min(32, L - 32 ep), or 0 past the segment or for a block id outside the
+    // pool; such an id inside the segment sets badacc.
+    static_assert(TILE_BYTES == 0x12000 && HT_BYTES == 0x9000 && ROW_BYTES == 0x480 && HT_TOK == 32 &&
+                      OSTAGE == 4, "constants of the descriptor sequence");
+    uint32_t badacc = 0;
     auto prep_next = [&](int ep, int blk) {
-      mb = mb0 + (uint32_t)(ep & (OSTAGE - 1)) * HT_BYTES;
-      const bool in_seg = ep < e1;
-      const bool ok = (uint32_t)blk < nblk;
-      if (in_seg && !ok) bad = true;
-      const uint64_t base = ((uint64_t)pool_hi << 32 | pool_lo) + (uint64_t)(uint32_t)blk * TILE_BYTES +
-                            (uint32_t)(ep & 1) * HT_BYTES;
-      const uint32_t bytes = (uint32_t)min(HT_TOK, L - ep * HT_TOK) * ROW_BYTES;
-      rs = in_seg && ok ? sgpr_x4{(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, bytes, 0x00020000u}
-                        : sgpr_x4{pool_lo, pool_hi, 0u, 0x00020000u};
+      uint32_t r0, r1, r2, r3;
+      asm volatile(
+          "s_mul_i32 %[r0], %[blk], 0x12000\n\t"
+          "s_mul_hi_u32 %[r1], %[blk], 0x12000\n\t"
+          "s_bitcmp1_b32 %[ep], 0\n\t"
+          "s_cselect_b32 %[r2], 0x9000, 0\n\t"
+          "s_add_u32 %[r0], %[r0], %[r2]\n\t"
+          "s_addc_u32 %[r1], %[r1], 0\n\t"
+          "s_add_u32 %[r0], %[r0], %[plo]\n\t"
+          "s_addc_u32 %[r1], %[r1], %[phi]\n\t"
+          "s_and_b32 %[r1], %[r1], 0xffff\n\t"
+          "s_lshl_b32 %[r2], %[ep], 5\n\t"
+          "s_sub_i32 %[r2], %[L], %[r2]\n\t"
+          "s_min_i32 %[r2], %[r2], 32\n\t"
+          "s_mul_i32 %[r2], %[r2], 0x480\n\t"
+          "s_cmp_ge_u32 %[blk], %[nblk]\n\t"
+          "s_cselect_b32 %[r3], 1, 0\n\t"
+          "s_cselect_b32 %[r2], 0, %[r2]\n\t"
+          "s_cmp_lt_i32 %[ep], %[e1]\n\t"
+          "s_cselect_b32 %[r3], %[r3], 0\n\t"
+          "s_cselect_b32 %[r2], %[r2], 0\n\t"
+          "s_or_b32 %[bd], %[bd], %[r3]\n\t"
+          "s_mov_b32 %[r3], 0x20000\n\t"
+          "s_and_b32 %[mb], %[ep], 3\n\t"
+          "s_mul_i32 %[mb], %[mb], 0x9000\n\t"
+          "s_add_u32 %[mb], %[mb], %[mb0]"
+          : [r0] "=&s"(r0), [r1] "=&s"(r1), [r2] "=&s"(r2), [r3] "=&s"(r3), [mb] "=&s"(mb), [bd] "+s"(badacc)
+          : [blk] "s"(blk), [ep] "s"(ep), [plo] "s"(pool_lo), [phi] "s"(pool_hi), [L] "s"(L), [nblk] "s"(nblk),
+            [e1] "s"(e1), [mb0] "s"(mb0)
+          : "scc");
+      rs = sgpr_x4{r0, r1, r2, r3};
     };
     // half tiles below e_open hold only keys every row may see (no key mask)
     const int e_open = max(0, L - a.Lq + 1) / HT_TOK;
@@ -1239,12 +1269,14 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     auto step = [&](const int e, auto first) {
       constexpr bool FIRST = decltype(first)::value;
       const bool more = e + 1 < e1;
-      if (more) wait_vmem_n<9>();          // stage e+1 complete; the copies of e+2 may be in flight
+      wait_vmem_n<9>();          // stage e+1 complete; the copies of e+2 may be in flight
       // stage e+1 visible; stage e-1 free. The sequence ends with every LDS
       // read done, so the barrier needs no lgkmcnt wait, and the block-id
       // scalar load issued right after it completes under the MFMAs.
       asm volatile("s_barrier" ::: "memory");
-      const int blk_next = blk_of(e + OSTAGE);   // for the copies prepared at the end
+      // for the copies prepared at the end (past the sequence's last tile any
+      // id of it will do: those copies cover zero bytes)
+      const int blk_next = bt[min((e + OSTAGE) >> 1, ntiles - 1)];
       int t0, t1, t2;
 #define OWN_ITER(NAME, OPS_O)                                                                         \
   asm volatile(NAME                                                                                   \
@@ -1258,20 +1290,19 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
       else
         OWN_ITER(OWN_ASM_IT, OWN_OPS_O);
 #undef OWN_ITER
-      if (more) {
-        // alpha belongs to half tile e+1, whose PV runs in the next iteration
-        if (__any(alpha != 1.f)) {
-          // the sequence's last PV MFMAs may still be writing the accumulators
-          asm volatile(OWN_ASM_GUARD ::: "memory");
+      // alpha belongs to half tile e+1, whose PV runs in the next iteration
+      if (more && __any(alpha != 1.f)) {
+        // the sequence's last PV MFMAs may still be writing the accumulators
+        asm volatile(OWN_ASM_GUARD ::: "memory");
 #pragma unroll
-          for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
-        }
-        prep_next(e + OSTAGE, blk_next);
+        for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
       }
+      prep_next(e + OSTAGE, blk_next);
     };
     step(e0, std::true_type{});
     for (int e = e0 + 1; e < e1; ++e) step(e, std::false_type{});
     asm volatile(OWN_ASM_GUARD ::: "memory");   // PV results settle before the epilogue reads them
+    if (badacc) bad = true;
 
     // ---- finish the segment. Both outputs hold o / l in bf16 (the final
     // o_lat, or a partial for the merge): each wave writes its 32 rows into
