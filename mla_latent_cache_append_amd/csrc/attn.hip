@@ -410,25 +410,13 @@ __device__ __forceinline__ void cols_tile(lds_char* cur, __attribute__((address_
 // scales are applied in fp32 to the scores and probabilities instead.
 constexpr int TILE_BYTES8 = BLOCK * D_K;               // 36,864
 constexpr int FP8_LOADS = TILE_BYTES8 / 16 / 256;      // 9 per thread
+constexpr int ROW_CHUNKS8 = D_K / 16;                  // 36 sixteen-byte chunks per row
 
 struct Fp8Stage {
   u32x4 v[FP8_LOADS];
   f32x4 sc;
   int n_valid;
 };
-
-// The 16-code chunk that thread tid moves in step i: eight lanes take four
-// consecutive chunks (c = 4k .. 4k+3) of two adjacent tokens (t = 2p, 2p+1),
-// so that each of the two bf16 writes of a chunk (bf16 chunks 2c, 2c+1, slot
-// 2c & 7 = 2 (c & 3) within their group) puts the eight lanes on distinct
-// banks: the two tokens sit in different 128-byte halves of the bank space.
-// A wave's loads still read whole 64-byte runs of each token.
-__device__ __forceinline__ void fp8_chunk_of(int tid, int i, int& t, int& c) {
-  const int q = (tid >> 3) + 32 * i, r = tid & 7;   // lane group q of 288
-  const int p = q / 9, k = q - 9 * p;               // token pair, chunk quad
-  t = 2 * p + (r >> 2);
-  c = 4 * k + (r & 3);
-}
 
 // Codes and scales of tile `blk`. The whole block lies inside the pool, so
 // every load is in bounds; tokens at or past n_valid (never written, any
@@ -438,11 +426,8 @@ __device__ __forceinline__ void fp8_tile_load(const uint8_t* pool8, const float*
                                               int n_valid, int tid, Fp8Stage& st) {
   const uint8_t* base = pool8 + (int64_t)blk * TILE_BYTES8;
 #pragma unroll
-  for (int i = 0; i < FP8_LOADS; ++i) {   // read once per call: non-temporal
-    int t, c;
-    fp8_chunk_of(tid, i, t, c);
-    st.v[i] = __builtin_nontemporal_load((const u32x4*)(base + t * D_K + 16 * c));
-  }
+  for (int i = 0; i < FP8_LOADS; ++i)   // read once per call: non-temporal
+    st.v[i] = __builtin_nontemporal_load((const u32x4*)(base + 16 * (tid + 256 * i)));
   st.sc = *(const f32x4*)(scales + (int64_t)blk * BLOCK + 4 * (tid & (BLOCK / 4 - 1)));
   st.n_valid = n_valid;
 }
@@ -460,8 +445,8 @@ __device__ __forceinline__ void fp8_tile_store(const Fp8Stage& st, lds_char* dst
                                                __attribute__((address_space(3))) float* sdst, int tid) {
 #pragma unroll
   for (int i = 0; i < FP8_LOADS; ++i) {
-    int t, c;
-    fp8_chunk_of(tid, i, t, c);
+    const int j = tid + 256 * i;
+    const int t = j / ROW_CHUNKS8, c = j - ROW_CHUNKS8 * t;
     const u32x4 v = t < st.n_valid ? st.v[i] : u32x4{0u, 0u, 0u, 0u};
     const u32x2 a = fp8x4_to_bf16x4(v[0]), b = fp8x4_to_bf16x4(v[1]);
     const u32x2 e = fp8x4_to_bf16x4(v[2]), f = fp8x4_to_bf16x4(v[3]);
