@@ -205,9 +205,12 @@ int mla_append_absorb(const mla_dims* dims, const uint16_t* c_kv, const uint16_t
  * MQA-mode kernels with an FP8 KV cache; the pages name the format only).
  * Reading used here: the same 576-element row per token, stored as OCP FP8
  * E4M3 codes ("e4m3fn": exponent bias 7, 3 mantissa bits, largest finite 448,
- * 0x7f / 0xff NaN) of row / scale, with one fp32 scale per token,
- * scale = max|row| / 448 (1 for an all-zero row). Half the bytes of the bf16
- * pool per token (576 + 4 against 1,152).
+ * 0x7f / 0xff NaN) of row / scale, with one fp32 scale per token, a power
+ * of two: the smallest 2^k with max|row| / 2^k <= 448, k >= -124 (1 for an
+ * all-zero row). E4M3 being floating point, a power-of-two scale loses
+ * nothing against max|row| / 448, and every code times its scale is exactly
+ * a bf16 value. Half the bytes of the bf16 pool per token (576 + 4 against
+ * 1,152).
  *   pool8       device [num_blocks][64][576] uint8  E4M3 codes
  *   pool_scale  device [num_blocks][64]      fp32   scale of each slot's row
  */

@@ -76,6 +76,20 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float u) {
   return sign | code;
 }
 
+// Token scale of the FP8 cache: the smallest power of two 2^k with
+// amax / 2^k <= 448, k >= -124, 1 for amax = 0. With amax = 1.m 2^(eb-127):
+// amax / 2^(eb-135) = 1.m * 256 is at most 448 while 1.m <= 1.75 (mantissa
+// bits <= 0x600000), else one more power of two (one fewer always gives
+// 1.m * 512 > 448). A subnormal amax gets the floor 2^-124. Every code
+// times such a scale is a bf16 value, exactly.
+__device__ __forceinline__ float fp8_token_scale(float amax) {
+  if (!(amax > 0.f)) return 1.f;
+  const uint32_t b = __float_as_uint(amax);
+  const int eb = (int)((b >> 23) & 0xFFu);
+  const int k = max(-124, eb - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0));
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
 // One wave per token, as cache_append_kernel: lane l holds latent elements
 // 8l..8l+7, lanes 0..31 also rope pair l; the row's absmax is a wave max.
 __device__ __forceinline__ void append_token_fp8(int j,
@@ -104,7 +118,7 @@ __device__ __forceinline__ void append_token_fp8(int j,
   if (lane < D_ROPE / 2) amax = fmaxf(amax, fmaxf(fabsf(r0), fabsf(r1)));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const float scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  const float scale = fp8_token_scale(amax);
   if (slot < 0 || slot >= num_slots) return;  // outside the pool: no write
   uint32_t lo = 0, hi = 0;
 #pragma unroll

@@ -24,8 +24,9 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 // FP8 variant of the same row ([AUDIT] §6.1 lists an FP8 KV cache for the
 // 576-wide MQA-mode kernels; the scale scheme is not given there). Each
 // token's row v = [c_kv | RoPE(k_pe)] in fp32 (the latent exactly, the rope
-// part rounded once from fp64) is stored as E4M3 codes of v / scale with
-// scale = max|v| / 448 (1 for an all-zero row), both divisions IEEE fp32.
+// part rounded once from fp64) is stored as E4M3 codes of v / scale, the
+// division IEEE fp32, with scale the smallest power of two that brings
+// max|v| within 448 (see fp8_token_scale).
 
 __global__ __launch_bounds__(256) void cache_append_fp8_kernel(
     const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,

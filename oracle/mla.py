@@ -205,11 +205,16 @@ def absorbed_decode(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, scale=None, base=ROPE_
 # scaling). Reading taken here: the 576-element row of each token is stored
 # as OCP FP8 E4M3 codes ("e4m3fn": 4 exponent bits with bias 7, 3 mantissa
 # bits, no infinities, 0x7f / 0xff are NaN, largest finite 448) with one fp32
-# scale per token, scale = max|row| / 448. The codes are integers, so the
-# quantizer takes its decisions in float32, the precision of the kernel that
-# writes them; everything after decoding is fp64 again.
+# scale per token, a power of two: the smallest 2^k with max|row| / 2^k <= 448,
+# k >= -124 (1 for an all-zero row). E4M3 is a floating-point format, so a
+# power-of-two scale costs no precision against max|row| / 448 (it moves the
+# row's largest element into (224, 448] instead of onto 448), and code x scale
+# is then exactly a bf16 value. The codes are integers, so the quantizer takes
+# its decisions in float32, the precision of the kernel that writes them;
+# everything after decoding is fp64 again.
 
 FP8_MAX = 448.0
+FP8_MIN_SCALE_EXP = -124   # code x 2^k stays on the bf16 grid (2^-9 x 2^-124 = 2^-133)
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -251,13 +256,29 @@ def e4m3_encode(u) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+def fp8_token_scale(amax) -> np.ndarray:
+    """The power of two 2^k with k = max(ceil(log2(amax / 448)), -124) for
+    float32 amax > 0, and 1 for amax = 0. Exactly, with amax = f 2^e and
+    448 = F 2^E (f, F in [0.5, 1); F = 0.875, E = 9): amax / 2^(e-E) =
+    (f / F) 448 is at most 448 when f <= F, and twice it is above 448 (f >=
+    0.5 > F / 2), so k = e - E, or e - E + 1 when f > F."""
+    a = np.asarray(amax, dtype=np.float32).astype(np.float64)
+    f, e = np.frexp(np.where(a > 0, a, 1.0))
+    F, E = np.frexp(FP8_MAX)
+    k = np.where(f <= F, e - E, e - E + 1)
+    k = np.maximum(k, FP8_MIN_SCALE_EXP)
+    return np.where(a > 0, np.ldexp(1.0, k), 1.0).astype(np.float32)
+
+
 def quantize_rows_fp8(rows) -> tuple[np.ndarray, np.ndarray]:
-    """Per-token scaled FP8 of float32 rows [..., 576]: scale = max|row| / 448
-    (float32 division; 1 for an all-zero row), codes = E4M3(row / scale) with
-    the division in float32. Returns (codes uint8 [..., 576], scale float32 [...])."""
+    """Per-token scaled FP8 of float32 rows [..., 576]: scale = the power of
+    two of ``fp8_token_scale`` (1 for an all-zero row), codes = E4M3(row /
+    scale); the division by a power of two is exact in float32 down to its
+    subnormals, whose values all encode to code 0 or 1 alike. Returns
+    (codes uint8 [..., 576], scale float32 [...])."""
     r = np.asarray(rows, dtype=np.float32)
     amax = np.max(np.abs(r), axis=-1)
-    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    scale = fp8_token_scale(amax)
     codes = e4m3_encode((r / scale[..., None]).astype(np.float32))
     return codes, scale
 

@@ -7,13 +7,17 @@ brute force fix.
   rounding midpoint and of its neighbours, against torch's float8_e4m3fn
   conversion on the CPU (a library routine);
 * encoding against a pure-Python nearest-value search over the 256 codes;
-* per-token quantization: the largest element of every row lands on +-448,
-  rows made of codes times a power of two come back unchanged, and the
-  dequantized row stays within half a grid step of the input;
+* per-token quantization: the scale is the smallest power of two that
+  brings the row's largest element within +-448 (so it lands in (224, 448]
+  before rounding),
+  with exponent at least -124, checked at the boundaries and against a
+  search over exponents; rows made of codes times a power of two come back
+  unchanged, and the dequantized row stays within half a grid step of the
+  input;
 * the FP8 decode equals the naive (expanding) path run on the dequantized rows
   with their rope part rotated back (fp64, 1e-10);
 * planted mistakes in the quantizer (round half away from zero, no scale,
-  rope left out) fail these pins.
+  a scale one power of two too large, rope left out) fail these pins.
 
 Tags: [AUDIT] llm-atlas "DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界".
 """
@@ -100,14 +104,39 @@ def check_row_quantization():
     codes, scale = mla.quantize_rows_fp8(rows)
     deq = mla.dequantize_rows_fp8(codes, scale)
     mags = np.abs(mla.e4m3_decode(codes))
-    # the largest element of each nonzero row lands on +-448
     nz = np.any(rows != 0, axis=1)
-    assert np.all(mags[nz].max(axis=1) == 448.0)
+    amax = np.abs(rows).max(axis=1).astype(np.float64)
+    s64 = scale.astype(np.float64)
+    # a power of two, the smallest with amax / scale <= 448
+    assert np.all(np.frexp(s64)[0] == 0.5)
+    assert np.all(amax[nz] / s64[nz] <= 448.0) and np.all(amax[nz] / (s64[nz] / 2) > 448.0)
+    # so the largest element of each nonzero row lands in (224, 448] before
+    # rounding, on a code in [224, 448] after it (the grid step there is 16)
+    top = mags[nz].max(axis=1)
+    assert np.all((top >= 224.0) & (top <= 448.0))
     assert scale[7] == 1.0 and np.all(codes[7] == 0)
     # half a grid step: 2^-4 relative in the normal range, 2^-10 scale below it
     r64 = rows.astype(np.float64)
     bound = np.maximum(np.abs(r64) * 2.0 ** -4, scale[:, None].astype(np.float64) * 2.0 ** -10)
     assert np.all(np.abs(deq - r64) <= bound * (1 + 1e-6))
+
+
+def check_token_scale():
+    """Boundaries of the power-of-two scale, and a search over exponents."""
+    f32 = np.float32
+    cases = {448.0: 1.0, 224.0: 0.5, 0.875: 2.0 ** -9, 896.0: 2.0, 1.0: 2.0 ** -8, 2.0 ** 100 * 448: 2.0 ** 100}
+    for a, want in cases.items():
+        assert mla.fp8_token_scale(f32(a)) == f32(want), a
+    assert mla.fp8_token_scale(np.nextafter(f32(448), f32(1e9))) == f32(2.0)
+    assert mla.fp8_token_scale(np.nextafter(f32(224), f32(1e9))) == f32(1.0)
+    assert mla.fp8_token_scale(f32(0)) == f32(1.0)
+    assert mla.fp8_token_scale(f32(1e-40)) == f32(2.0 ** -124)   # float32 subnormal amax: the floor
+    rng = np.random.default_rng(7)
+    a = (np.abs(rng.standard_normal(5000)) * np.exp2(rng.uniform(-100, 100, 5000))).astype(np.float32)
+    got = mla.fp8_token_scale(a).astype(np.float64)
+    for x, g in zip(a.astype(np.float64).tolist(), got.tolist()):
+        k = next(k for k in range(-124, 129) if x / 2.0 ** k <= 448.0)
+        assert g == 2.0 ** k, (x, g, k)
 
 
 def check_round_trip_exact():
@@ -183,6 +212,10 @@ def test_row_quantization_bounds():
     check_row_quantization()
 
 
+def test_token_scale_power_of_two():
+    check_token_scale()
+
+
 def test_row_quantization_round_trip():
     check_round_trip_exact()
 
@@ -219,6 +252,15 @@ def test_planted_missing_scale(monkeypatch):
     monkeypatch.setattr(mla, "FP8_MAX", 1.0)
     with pytest.raises(AssertionError):
         check_row_quantization()
+
+
+def test_planted_scale_too_large(monkeypatch):
+    real = mla.fp8_token_scale
+    monkeypatch.setattr(mla, "fp8_token_scale", lambda a: (real(a) * 2).astype(np.float32))
+    with pytest.raises(AssertionError):
+        check_row_quantization()
+    with pytest.raises(AssertionError):
+        check_token_scale()
 
 
 def test_planted_rope_left_out(monkeypatch):
