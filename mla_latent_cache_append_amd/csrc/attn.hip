@@ -1436,6 +1436,291 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   if (a.lse && lane == 0) a.lse[orow] = l > 0.f ? (M + __log2f(l)) * LN2 : (l != l ? NAN : -INFINITY);
 }
 
+// ------------------------------------------------------ 128 rows, FP8 pool
+//
+// attn_own_kernel over the FP8 pool (E4M3 codes [num_blocks][64][576] and
+// power-of-two token scales [num_blocks][64]). Each wave copies its 8 tokens'
+// codes (4,608 bytes, as five 1-KiB copies) and their scales into a staging
+// slot of its own and widens them, the scale folded into the conversion,
+// into the bf16 half-tile stages the same products read: code x 2^k is a
+// bf16 value, so the stage holds the row exactly and everything after it is
+// the bf16 kernel's arithmetic. Three stages (V of e, K of e+1, e+2 being
+// widened) and two staging slots per wave (e+2 being widened, e+3 in flight;
+// e+4 is copied into e+2's slot once it has been read). The widening and the
+// copies are part of the iteration sequences (OWN8_ASM_*, own_asm.inc).
+constexpr int FSTAGE = 3;
+constexpr int F8_STG = 5376;                  // staging slot: 5,120 bytes of codes, 256 of scales
+constexpr int F8_SC_OFF = 5120;
+constexpr int HT_BYTES8 = HT_TOK * D_K;       // 18,432 code bytes per half tile
+constexpr int TILE_BYTES8_ = BLOCK * D_K;     // 36,864 code bytes per block
+static_assert(OUT_STRIDE * 128 <= FSTAGE * HT_BYTES + 8 * F8_STG, "output staging fits the FP8 kernel's LDS");
+
+// Widen half tile e's codes from this wave's staging slot src into the bf16
+// stage dst (this wave's 8 tokens, the layout of ht_off); the slot holds the
+// 64 scales of e's block. A token at or past nv (past the sequence, codes
+// zero-filled) takes scale 1.
+__device__ __forceinline__ void widen8(const lds_char* src, lds_char* dst, int e, int wave, int lane, int nv) {
+  const int tl = lane >> 3;
+  float sc = *(const __attribute__((address_space(3))) float*)(src + F8_SC_OFF + 4 * (32 * (e & 1) + 8 * wave + tl));
+  if (8 * wave + tl >= nv) sc = 1.f;
+  const uint32_t rd = (uint32_t)(tl * D_K + 8 * ((lane & 7) ^ swz2(8 * wave + tl)));
+  const uint32_t wr = (uint32_t)(wave * 9 * 1024 + lane * 16);
+#pragma unroll
+  for (int c = 0; c < 9; ++c) {
+    const u32x2 v = *(const __attribute__((address_space(3))) u32x2*)(src + rd + 64 * c);
+    u32x4 w4;
+    w4[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, false));
+    w4[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], sc, true));
+    w4[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, false));
+    w4[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], sc, true));
+    *(__attribute__((address_space(3))) u32x4*)(dst + wr + 1024 * c) = w4;
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void attn_own8_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[FSTAGE * HT_BYTES + 8 * F8_STG];
+  lds_char* stages = (lds_char*)smem;
+
+  const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int c32 = lane & 31, h = lane >> 5;
+  lds_char* stg = stages + FSTAGE * HT_BYTES + wave * 2 * F8_STG;   // this wave's two staging slots
+
+  int unit = blockIdx.x;
+  if ((gridDim.x & 7) == 0) unit = (unit & 7) * (int)(gridDim.x >> 3) + (unit >> 3);
+  const int w = unit / a.n_rg;
+  const int rg = unit - w * a.n_rg;
+  const int64_t T = plan_total_tiles(a.seq_lens, a.B, a.max_blocks);
+  if (T == 0) return;
+  const int64_t x_begin = (int64_t)w * T / a.width;
+  const int64_t x_end = (int64_t)(w + 1) * T / a.width;
+  if (x_begin >= x_end) return;
+  int b;
+  int64_t seq_start;
+  plan_find(a.seq_lens, a.B, a.max_blocks, x_begin, b, seq_start);
+
+  const int r = rg * 128 + 32 * wave + c32;
+  const uint32_t kbase = ht_off(c32, h);       // as in attn_own_kernel
+  uint32_t vbase;
+  {
+    const int i16 = lane & 15, q = lane >> 4;
+    const int tl = 4 * (q >> 1) + (i16 >> 2);
+    const int e = 2 * (q & 1) + ((i16 & 3) >> 1);
+    vbase = ht_off(tl, e) + 8 * (i16 & 1);
+  }
+  // copies: lane l moves bytes 16 l (+ 1,024 c) of the wave's 4,608 and
+  // scale l of the half tile's block (the sequences derive both offsets
+  // from go8 = 16 l)
+  const uint32_t go8 = (uint32_t)(lane * 16);
+  const uint32_t so8 = (uint32_t)uni(wave * 8 * D_K);
+  // widening: the lane's token within the half tile, and the staging offset
+  // of its chunk (codes of chunk group c at staging + rdo + 64 c; the bf16
+  // chunk goes to stage + 9,216 wave + go8 + 1,024 c)
+  const uint32_t tlw = (uint32_t)(8 * wave + (lane >> 3));
+  const uint32_t rdo = (uint32_t)((lane >> 3) * D_K + 8 * ((lane & 7) ^ swz2(8 * wave + (lane >> 3))));
+  const uint8_t* pool8 = (const uint8_t*)a.pool;
+  const uint32_t pool_lo = (uint32_t)uni((int)(uint32_t)(uintptr_t)pool8);
+  const uint32_t pool_hi = (uint32_t)uni((int)((uint32_t)((uintptr_t)pool8 >> 32) & 0xffffu));
+  const uint32_t nblk = (uint32_t)uni((int)min(a.num_blocks, (int64_t)0x7fffffff));
+  const uint32_t stg_lds = (uint32_t)uni((int)lds_addr(stg));
+
+  int64_t x = x_begin;
+  while (x < x_end && b < a.B) {
+    const int L = uni(a.seq_lens[b]);
+    const int ntiles = tiles_of(L, a.max_blocks);
+    const int64_t seg_end = min(x_end, seq_start + ntiles);
+    const int k_first = (int)(x - seq_start);
+    const int k_last = (int)(seg_end - seq_start);
+    const bool whole = (x == seq_start) && (seg_end == seq_start + ntiles);
+    bool bad = L > a.max_keys;
+    const int key_end = min(k_last * BLOCK, L);
+    const int e0 = 2 * k_first, e1 = (key_end + HT_TOK - 1) / HT_TOK;
+
+    const int lim = r < a.rows ? L - a.Lq + r / a.H : -1;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 o[16];
+
+    const __attribute__((address_space(4))) int32_t* bt =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)b * a.max_blocks);
+    // valid tokens of half tile e (0 past the segment)
+    auto nv_of = [&](int e) { return e < e1 ? min(HT_TOK, L - e * HT_TOK) : 0; };
+    // copies of half tile e from block blk: codes at pool8 + blk * 36,864 +
+    // (e & 1) * 18,432 (nv * 576 bytes; none past the segment or for a block
+    // id outside the pool), the block's 64 scales at pool_scale + blk * 64
+    // (the pool's first 64, a safe address, when there are no codes)
+    auto prep8 = [&](int e, int blk, sgpr_x4& rs, uint64_t& sb) {
+      const bool in_seg = e < e1;
+      const bool ok = (uint32_t)blk < nblk;
+      if (in_seg && !ok) bad = true;
+      const bool use = in_seg && ok;
+      const uint64_t base = ((uint64_t)pool_hi << 32 | pool_lo) + (uint64_t)(uint32_t)blk * TILE_BYTES8_ +
+                            (uint32_t)(e & 1) * HT_BYTES8;
+      const uint32_t bytes = use ? (uint32_t)nv_of(e) * D_K : 0u;
+      rs = use ? sgpr_x4{(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, bytes, 0x00020000u}
+               : sgpr_x4{pool_lo, pool_hi, 0u, 0x00020000u};
+      const uint64_t sc0 = (uint64_t)(uintptr_t)a.pool_scale;
+      sb = use ? sc0 + (uint64_t)(uint32_t)blk * BLOCK * 4 : sc0;
+    };
+    auto blk_of = [&](int e) { return bt[min(e >> 1, ntiles - 1)]; };
+    uint32_t ka[4], va[4];
+    auto k_addr = [&](int e) {
+      const uint32_t sbk = lds_addr(stages + (e % FSTAGE) * HT_BYTES) + kbase;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ka[q] = sbk ^ (uint32_t)(q << 5);
+    };
+    auto v_addr = [&](int e) {
+      const uint32_t sbv = lds_addr(stages + (e % FSTAGE) * HT_BYTES) + vbase;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int c1 = 0; c1 < 2; ++c1) va[c1 + 2 * rr] = sbv ^ (uint32_t)((c1 << 6) | (rr << 5));
+    };
+
+    // ---- segment start: half tiles e0 and e0+1 copied (with the query
+    // fragments between them) and widened, then e0+2 and e0+3 copied
+    u32x4 qf[KSTEPS16];
+    {
+      const int nv = max(0, min(128, a.rows - rg * 128));
+      sgpr_x4 qr = buffer_rsrc(a.q + ((int64_t)b * a.rows + rg * 128) * D_K, nv * ROW_BYTES);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qr[k] = (uint32_t)uni((int)qr[k]);
+      const uint32_t qv = (uint32_t)((32 * wave + c32) * ROW_BYTES + 16 * h);
+      sgpr_x4 rs0, rs1;
+      uint64_t sb0, sb1;
+      prep8(e0, blk_of(e0), rs0, sb0);
+      prep8(e0 + 1, blk_of(e0 + 1), rs1, sb1);
+      const uint32_t mb0 = stg_lds + (uint32_t)(e0 & 1) * F8_STG, mb1 = stg_lds + (uint32_t)((e0 + 1) & 1) * F8_STG;
+      const uint32_t go8b = go8 + 4096, soff = go8 >> 2;
+      asm volatile(OWN8_ASM_QLOAD
+                   : OWN_OPS_Q_OUT
+                   : [qv] "v"(qv), [qr] "s"(qr), [mb0] "s"(mb0), [rs0] "s"(rs0), [sb0] "s"(sb0), [mb1] "s"(mb1),
+                     [rs1] "s"(rs1), [sb1] "s"(sb1), [go8] "v"(go8), [go8b] "v"(go8b), [so8] "s"(so8),
+                     [soff] "v"(soff)
+                   : "m0", "scc", "memory");
+      widen8(stg + (e0 & 1) * F8_STG, stages + (e0 % FSTAGE) * HT_BYTES, e0, wave, lane, nv_of(e0));
+      widen8(stg + ((e0 + 1) & 1) * F8_STG, stages + ((e0 + 1) % FSTAGE) * HT_BYTES, e0 + 1, wave, lane,
+             nv_of(e0 + 1));
+      prep8(e0 + 2, blk_of(e0 + 2), rs0, sb0);
+      prep8(e0 + 3, blk_of(e0 + 3), rs1, sb1);
+      asm volatile(OWN8_ASM_COPY
+                   :
+                   : [mb0] "s"(mb0), [rs0] "s"(rs0), [sb0] "s"(sb0), [mb1] "s"(mb1), [rs1] "s"(rs1), [sb1] "s"(sb1),
+                     [go8] "v"(go8), [go8b] "v"(go8b), [so8] "s"(so8), [soff] "v"(soff)
+                   : "m0", "scc", "memory");
+    }
+    lds_barrier();                         // every wave's e0 and e0+1 are widened
+    k_addr(e0);
+    float s[16];
+    float alpha, mref;
+    {
+      const int lr = lim - (e0 * HT_TOK + 4 * h);
+      asm volatile(OWN8_ASM_PRO
+                   : OWN_OPS_S_OUT, [mrun] "+v"(m_run), [alpha] "=&v"(alpha), [mref] "=&v"(mref)
+                   : OWN_OPS_Q, OWN_OPS_KA, [lr] "v"(lr), [scale] "s"(a.scale_log2)
+                   : OWN8_CLOB, "vcc", "scc", "memory");
+    }
+    // iteration e widens e+2 and copies e+4 (prepared at the end of e-1)
+    sgpr_x4 rs;
+    uint64_t sb;
+    prep8(e0 + 4, blk_of(e0 + 4), rs, sb);
+    uint32_t mb8 = stg_lds + (uint32_t)(e0 & 1) * F8_STG;           // staging slot of e+2 and e+4
+    int nv2 = nv_of(e0 + 2);
+    int r3 = e0 % FSTAGE;
+    // stage of e+2 plus this wave's 9 lines: where the widening writes
+    const uint32_t stage0 = (uint32_t)uni((int)lds_addr(stages)) + (uint32_t)(wave * 9 * 1024);
+    auto cwb_of = [&](int r) { return stage0 + (uint32_t)((r + 2) % FSTAGE) * HT_BYTES; };
+    uint32_t cwb = cwb_of(r3);
+    k_addr(e0 + 1 < e1 ? e0 + 1 : e0);
+    v_addr(e0);
+    const int e_open = max(0, L - a.Lq + 1) / HT_TOK;
+    int lr = lim - ((e0 + 1) * HT_TOK + 4 * h);
+    auto step = [&](const int e, auto first) {
+      constexpr bool FIRST = decltype(first)::value;
+      const bool more = e + 1 < e1;
+      wait_vmem_n<6>();        // e+2's codes and scales are in this wave's staging; e+3 may be in flight
+      asm volatile("s_barrier" ::: "memory");   // stage e+1 widened by every wave; stage of e-1 free
+      const int blk_next = blk_of(e + 5);
+      int t0, t1, t2;
+#define OWN8_ITER(NAME, OPS_O)                                                                         \
+  asm volatile(NAME                                                                                    \
+               : OPS_O, OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "+v"(alpha),        \
+                 [mref] "+v"(mref), [lr] "+v"(lr), OWN_OPS_KA_IO, OWN_OPS_VA_IO, OWN_OPS_BOOK_OUT      \
+               : OWN_OPS_Q, [scale] "s"(a.scale_log2), [rs] "s"(rs), [sb] "s"(sb), [so8] "s"(so8),     \
+                 [go8] "v"(go8), [rdo] "v"(rdo), [tlw] "v"(tlw), [mb8] "s"(mb8), [cwb] "s"(cwb),       \
+                 [nv2] "s"(nv2), [ep] "s"(e + 4), [eo] "s"(e_open), [e1] "s"(e1), [r3] "s"(r3)         \
+               : OWN8_CLOB, "vcc", "m0", "scc", "memory")
+      if constexpr (FIRST)
+        OWN8_ITER(OWN8_ASM_IT_FIRST, OWN_OPS_O_OUT);
+      else
+        OWN8_ITER(OWN8_ASM_IT, OWN_OPS_O);
+#undef OWN8_ITER
+      if (more && __any(alpha != 1.f)) {
+        asm volatile(OWN_ASM_GUARD ::: "memory");
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
+        // The rescale borrows registers and may reload spilled values from
+        // scratch; wait for them here (the compiler sees this wait), so
+        // that the loop head needs none: a wait there would also drain the
+        // copies in flight every iteration. Rescales are rare.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      }
+      prep8(e + 5, blk_next, rs, sb);
+      mb8 = stg_lds + (uint32_t)((e + 1) & 1) * F8_STG;
+      nv2 = nv_of(e + 3);
+      r3 = r3 == FSTAGE - 1 ? 0 : r3 + 1;
+      cwb = cwb_of(r3);
+    };
+    step(e0, std::true_type{});
+    for (int e = e0 + 1; e < e1; ++e) step(e, std::false_type{});
+    asm volatile(OWN_ASM_GUARD ::: "memory");
+
+    l_run += __shfl_xor(l_run, 32);
+    {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      wait_vmem_n<0>();                    // copies past the segment's end still write their slots
+      lds_barrier();
+      lds_char* orow_l = stages + (32 * wave + c32) * OUT_STRIDE + 8 * h;
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v0 = o[cb][4 * j] * inv, v1 = o[cb][4 * j + 1] * inv;
+          float v2 = o[cb][4 * j + 2] * inv, v3 = o[cb][4 * j + 3] * inv;
+          if (bad) v0 = v1 = v2 = v3 = NAN;
+          *(__attribute__((address_space(3))) u32x2*)(orow_l + (32 * cb + 8 * j) * 2) =
+              u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        }
+      lds_barrier();
+      uint16_t* dst = whole ? a.o_lat + (int64_t)b * a.rows * D_C
+                            : a.ws_acc + (int64_t)(w + b) * a.rows * D_C;
+#pragma unroll 4
+      for (int i = 0; i < 32; ++i) {
+        const int rl = 32 * wave + i;
+        const int rr = rg * 128 + rl;
+        if (rr >= a.rows) break;
+        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(stages + rl * OUT_STRIDE + 16 * lane);
+        *(u32x4*)(dst + (int64_t)rr * D_C + 8 * lane) = v;
+      }
+      if (r < a.rows && h == 0) {
+        if (whole) {
+          if (a.lse) {
+            const float lv = l_run > 0.f ? (m_run + __log2f(l_run)) * LN2 : -INFINITY;
+            a.lse[(int64_t)b * a.rows + r] = bad ? NAN : lv;
+          }
+        } else {
+          const int64_t prow = (int64_t)(w + b) * a.rows + r;
+          a.ws_ml[prow * 2 + 0] = bad ? NAN : m_run;
+          a.ws_ml[prow * 2 + 1] = bad ? NAN : l_run;
+        }
+      }
+    }
+    x = seg_end;
+    seq_start += ntiles;
+    ++b;
+    while (b < a.B && tiles_of(uni(a.seq_lens[b]), a.max_blocks) == 0) ++b;
+    lds_barrier();
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 // pe != null: the two-buffer layout, pool = kv_cache, max_keys = max_seq
@@ -1471,7 +1756,8 @@ static hipError_t launch_attention(const uint16_t* q, const void* pool, const ui
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
   const dim3 grid(p.width * p.n_rg);
   if (fp8) {
-    if (p.variant == V_COLS16) hipLaunchKernelGGL((attn_cols_kernel<1, true>), grid, dim3(256), 0, stream, a);
+    if (p.variant == V_ROWS128) hipLaunchKernelGGL(attn_own8_kernel, grid, dim3(256), 0, stream, a);
+    else if (p.variant == V_COLS16) hipLaunchKernelGGL((attn_cols_kernel<1, true>), grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((attn_cols_kernel<2, true>), grid, dim3(256), 0, stream, a);
   } else switch (p.variant) {
     case V_ROWS128:

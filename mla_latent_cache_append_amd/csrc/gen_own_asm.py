@@ -358,6 +358,248 @@ def gen_iter(mask, first):
     return s.text()
 
 
+# --------------------------------------------------------------- FP8 pool
+#
+# The FP8 kernel streams E4M3 codes (576 bytes per token) and power-of-two
+# token scales into a per-wave staging area and widens them, scale folded in,
+# into the same bf16 half-tile stages the products read: code x 2^k is a
+# bf16 value, so v_cvt_scalef32_pk_bf16_fp8 gives the row exactly. Stages:
+# three bf16 half tiles (slot e % 3: V of e, K of e+1, and e+2 being written)
+# and two staging slots per wave (half tiles e+2, being widened, and e+3 in
+# flight; e+4 is copied into e+2's slot once it is widened).
+#
+# Staging slot of a wave: 5,120 bytes of codes (its 8 tokens, 4,608 bytes,
+# as five 1 KiB copies; the fifth reads past them) and 256 bytes of scales
+# (word i = scale of token min(i, 7)).
+F8_STG = 5376
+F8_SC_OFF = 5120
+
+
+def use_layout(pf_k, pf_v, conv):
+    """Fixed-register layout (from v255 down) for ring depths pf_k, pf_v and,
+    with conv, the FP8 widening registers (two 4-register chunk buffers and
+    the lane's token scale)."""
+    global PF_K, PF_V, VR0, VRING, KR0, KRING, P0, P_OP, SN0, SN, T0, TMP, CLOB_LO, CB0, CSC
+    PF_K, PF_V = pf_k, pf_v
+    VR0 = _top - 4 * PF_V
+    VRING = [("v[%d:%d]" % (VR0 + 4 * i, VR0 + 4 * i + 1), "v[%d:%d]" % (VR0 + 4 * i + 2, VR0 + 4 * i + 3),
+              "v[%d:%d]" % (VR0 + 4 * i, VR0 + 4 * i + 3)) for i in range(PF_V)]
+    KR0 = VR0 - 4 * PF_K
+    KRING = ["v[%d:%d]" % (KR0 + 4 * i, KR0 + 4 * i + 3) for i in range(PF_K)]
+    P0 = KR0 - 8
+    P_OP = ["v[%d:%d]" % (P0, P0 + 3), "v[%d:%d]" % (P0 + 4, P0 + 7)]
+    SN0 = P0 - 16
+    SN = "v[%d:%d]" % (SN0, SN0 + 15)
+    T0 = SN0 - 4
+    TMP = ["v%d" % (T0 + i) for i in range(4)]
+    CLOB_LO = T0
+    CB0 = CSC = None
+    if conv:
+        CB0 = T0 - 10         # chunk buffers v[CB0 .. CB0+7] (even: 64-bit tuples), scale v[CB0+8]
+        CSC = "v%d" % (CB0 + 8)
+        CLOB_LO = CB0
+
+
+F8_HT_NEG2 = "0xfffee000"    # -2 stages of 36,864 bytes: from stage 2 back to stage 0
+
+
+def conv_read(seq, c):
+    """Codes of chunk group c of the lane's token (8 bytes at the read base
+    + 64 c) into the upper half of chunk buffer c % 2."""
+    b = CB0 + 4 * (c % 2)
+    seq.lds("ds_read_b64 v[%d:%d], %s offset:%d" % (b + 2, b + 3, TMP[1], 64 * c), "C%d" % c)
+
+
+def conv_widen(seq, c):
+    """Four conversions (two codes each, scale folded in) into the whole
+    buffer, in an order that overwrites each code register only after its
+    last use, then the 16-byte write into the bf16 stage (cw + 1,024 c)."""
+    b = CB0 + 4 * (c % 2)
+    seq.need("C%d" % c)
+    seq.op("v_cvt_scalef32_pk_bf16_fp8 v%d, v%d, %s" % (b, b + 2, CSC))
+    seq.op("v_cvt_scalef32_pk_bf16_fp8 v%d, v%d, %s op_sel:[1,0,0]" % (b + 1, b + 2, CSC))
+    seq.op("v_cvt_scalef32_pk_bf16_fp8 v%d, v%d, %s" % (b + 2, b + 3, CSC))
+    seq.op("v_cvt_scalef32_pk_bf16_fp8 v%d, v%d, %s op_sel:[1,0,0]" % (b + 3, b + 3, CSC))
+    seq.lds("ds_write_b128 %s, v[%d:%d] offset:%d" % (TMP[2], b, b + 3, 1024 * c), "W%d" % c)
+
+
+def dma8_ops(prologue=False):
+    """Copies of half tile e+4 into the staging slot just widened (M0 = mb8):
+    five 1 KiB code copies (the lane's 16 bytes at so8 + 1,024 c + go8,
+    go8 = 16 l; the fifth through go8 + 4,096, since an instruction offset
+    stops at 4,095) and the 64 scales of the half tile's block (lane l reads
+    scale l at sb + 4 l). The offsets of the last two sit in the chunk
+    buffers, free once the widening is done. Each M0 write has one other
+    instruction between it and its copy."""
+    if prologue:   # outside the loop the two offsets come in as operands
+        return [
+            ("m0", "s_mov_b32 m0, %[mb8]"),
+            ("ld", "buffer_load_dwordx4 %[go8], %[rs], %[so8] offen offset:0 nt lds"),
+            ("ld", "buffer_load_dwordx4 %[go8], %[rs], %[so8] offen offset:1024 nt lds"),
+            ("ld", "buffer_load_dwordx4 %[go8], %[rs], %[so8] offen offset:2048 nt lds"),
+            ("ld", "buffer_load_dwordx4 %[go8], %[rs], %[so8] offen offset:3072 nt lds"),
+            ("m0", "s_add_u32 m0, %%[mb8], 0x%x" % 4096),
+            ("ld", "buffer_load_dwordx4 %[go8b], %[rs], %[so8] offen offset:0 nt lds"),
+            ("m0", "s_add_u32 m0, %%[mb8], 0x%x" % F8_SC_OFF),
+            ("ld", "global_load_lds_dword %[soff], %[sb] offset:0"),
+        ]
+    gb, so = "v%d" % CB0, "v%d" % (CB0 + 1)
+    return [
+        ("m0", "s_mov_b32 m0, %[mb8]"),
+        ("ld", "buffer_load_dwordx4 %[go8], %[rs], %[so8] offen offset:0 nt lds"),
+        ("ld", "buffer_load_dwordx4 %[go8], %[rs], %[so8] offen offset:1024 nt lds"),
+        ("ld", "buffer_load_dwordx4 %[go8], %[rs], %[so8] offen offset:2048 nt lds"),
+        ("ld", "buffer_load_dwordx4 %[go8], %[rs], %[so8] offen offset:3072 nt lds"),
+        ("m0", "s_add_u32 m0, %%[mb8], 0x%x" % 4096),
+        ("va", "v_add_u32 %s, 0x1000, %%[go8]" % gb),
+        ("ld", "buffer_load_dwordx4 %s, %%[rs], %%[so8] offen offset:0 nt lds" % gb),
+        ("m0", "s_add_u32 m0, %%[mb8], 0x%x" % F8_SC_OFF),
+        ("va", "v_lshrrev_b32 %s, 2, %%[go8]" % so),
+        ("ld", "global_load_lds_dword %s, %%[sb] offset:0" % so),
+    ]
+
+
+def book_keeping8():
+    """Address work for the next sequence: K addresses to the stage of e+2
+    (or e+1 again past e1), V^T addresses to the stage of e+1, and the mask
+    limit. Stages advance one slot (+36,864) or wrap from slot 2 to 0;
+    r3 = e % 3 says which address wraps. Returns (groups, tail):
+    each group is emitted in one piece, so that no SCC-writing instruction
+    (the copies' M0 sums) falls between a compare and its select."""
+    groups = [
+        ["s_sub_i32 %[t0], %[ep], 2",
+         "s_cmp_eq_u32 %[r3], 1",
+         "s_mov_b32 %[t1], " + STAGE,
+         "s_cselect_b32 %[t1], " + F8_HT_NEG2 + ", %[t1]",
+         "s_cmp_lt_i32 %[t0], %[e1]",
+         "s_cselect_b32 %[t1], %[t1], 0"],
+    ] + [["v_add_u32 %%[ka%d], %%[t1], %%[ka%d]" % (q, q)] for q in range(4)]
+    tail = [
+        "v_subrev_u32 %[lr], 32, %[lr]",
+        "s_cmp_eq_u32 %[r3], 2",
+        "s_mov_b32 %[t2], " + STAGE,
+        "s_cselect_b32 %[t2], " + F8_HT_NEG2 + ", %[t2]",
+    ] + ["v_add_u32 %%[va%d], %%[t2], %%[va%d]" % (q, q) for q in range(4)]
+    return groups, tail
+
+
+CONV_AT = [1 + 3 * c for c in range(9)]     # score step after which chunk c is read
+DMA8_P = [8, 10, 12, 14, 16, 18, 20, 22, 24, 26, 27]   # PV steps after which the copies go
+
+
+def gen_iter8(mask, first):
+    """FP8 iteration e: as gen_iter (phase S: scores of e+1 under the
+    probabilities of e; phase P: PV of e under the max half of e+1), plus the
+    widening of half tile e+2 (this wave's 8 tokens) spread over phase S and
+    the copies of e+4 in phase P, after the widening has read its slot."""
+    s = Seq()
+    s.op("s_nop 1")
+    for ks in range(PF_K):
+        kread(s, ks)
+    # widening bases: codes at mb8 + rdo (the lane's swizzled chunk of its
+    # token), bf16 stage at cwb + go8; the lane's token scale is word
+    # 32 (e & 1) + tlw of the block's 64 in the staging slot, 1 for a token
+    # past the half tile's valid ones (its codes are zeros; a scale slot
+    # never written might hold anything)
+    s.op("v_add_u32 %s, %%[mb8], %%[rdo]" % TMP[1])
+    s.op("v_add_u32 %s, %%[cwb], %%[go8]" % TMP[2])
+    s.op("s_bitcmp1_b32 %[ep], 0")
+    s.op("s_cselect_b32 %[t0], 0x80, 0")
+    s.op("s_add_u32 %[t0], %[t0], %[mb8]")
+    s.op("v_lshl_add_u32 %s, %%[tlw], 2, %%[t0]" % CSC)
+    s.lds("ds_read_b32 %s, %s offset:%d" % (CSC, CSC, F8_SC_OFF), "SC")
+    exp_valu = softmax_exp()
+    lead, rest = exp_valu[:8], exp_valu[8:]
+    per = (len(rest) + S_VALU_STEPS - 1) // S_VALU_STEPS
+    for ins in lead:
+        s.op(ins)
+    vnext = 0
+    widened = 0
+    for ks in range(KSTEPS):
+        score_mfma(s, ks)
+        if ks + PF_K < KSTEPS:
+            kread(s, ks + PF_K)
+        elif vnext < PF_V:
+            vread(s, vnext)
+            vnext += 1
+        if ks == 2:
+            s.need("SC")
+            s.op("v_cmp_gt_i32 vcc, %[nv2], %[tlw]")
+            s.op("v_cndmask_b32 %s, 1.0, %s, vcc" % (CSC, CSC))
+        if ks in CONV_AT:
+            c = CONV_AT.index(ks)
+            conv_read(s, c)
+            if c >= 1:
+                conv_widen(s, c - 1)
+                widened = c
+        for ins in rest[ks * per:(ks + 1) * per]:
+            s.op(ins)
+    conv_widen(s, 8)
+    while vnext < PF_V:
+        vread(s, vnext)
+        vnext += 1
+    book, book_tail = book_keeping8()
+    max_valu = softmax_max(mask)
+    nsteps = 32 - P_VALU_FROM - 6
+    mper = (len(max_valu) + nsteps - 1) // nsteps
+    assert len(book) <= 31 - PF_V - BOOK_FROM
+    dma = dma8_ops()
+    assert len(dma) == len(DMA8_P)
+    for j in range(32):
+        s.need("V%db" % j)
+        cb, kk = pv_step(j)
+        acc = "0" if first and kk == 0 else "%%[o%d]" % cb
+        s.op("v_mfma_f32_32x32x16_bf16 %%[o%d], %s, %s, %s" % (cb, VRING[j % PF_V][2], P_OP[kk], acc))
+        if j + PF_V < 32:
+            vread(s, j + PF_V)
+        if j in DMA8_P:
+            k = DMA8_P.index(j)
+            s.op(dma[k][1])
+        if j >= P_VALU_FROM:
+            k = j - P_VALU_FROM
+            for ins in max_valu[k * mper:(k + 1) * mper]:
+                s.op(ins)
+        if BOOK_FROM <= j < BOOK_FROM + len(book):
+            for ins in book[j - BOOK_FROM]:
+                s.op(ins)
+        if j == 32 - PF_V:
+            for ins in book_tail:
+                s.op(ins)
+    assert (32 - P_VALU_FROM - 6) * mper >= len(max_valu)
+    s.drain()
+    return s.text()
+
+
+def gen_qload8():
+    """Start of an FP8 segment: copies of half tiles e0 and e0+1 (codes and
+    scales) into the wave's two staging slots, with the 36 query fragments
+    loaded between them; waits for all of it (the caller then widens both)."""
+    s = Seq()
+    for st in (0, 1):
+        for kind, text in dma8_ops(prologue=True):
+            s.op(text.replace("%[mb8]", "%%[mb%d]" % st).replace("%[rs]", "%%[rs%d]" % st)
+                 .replace("%[sb]", "%%[sb%d]" % st))
+            if kind == "m0":
+                s.op("s_nop 0")
+        if st == 0:
+            for ks in range(KSTEPS):
+                s.op("buffer_load_dwordx4 %%[q%d], %%[qv], %%[qr], 0 offen offset:%d" % (ks, 32 * ks))
+    s.op("s_waitcnt vmcnt(0)")
+    return s.text()
+
+
+def gen_copy8():
+    """Copies of two half tiles (codes and scales) into the two staging slots."""
+    s = Seq()
+    for st in (0, 1):
+        for kind, text in dma8_ops(prologue=True):
+            s.op(text.replace("%[mb8]", "%%[mb%d]" % st).replace("%[rs]", "%%[rs%d]" % st)
+                 .replace("%[sb]", "%%[sb%d]" % st))
+            if kind == "m0":
+                s.op("s_nop 0")
+    return s.text()
+
+
 def main():
     out = os.path.join(HERE, "own_asm.inc")
     body = ["// Generated by gen_own_asm.py; do not edit.", ""]
@@ -394,6 +636,21 @@ def main():
     for name, text in ops.items():
         body.append("#define %s %s" % (name, text))
     body.append("")
+    # FP8 pool: the same sequences with shallower operand rings (their
+    # registers go to the widening) plus the widening and the code copies
+    bf16_layout = (PF_K, PF_V)
+    use_layout(3, 3, True)
+    it8 = ("s_sub_i32 %[t0], %[ep], 3\\n\\ts_cmp_lt_i32 %[t0], %[eo]\\n\\t"
+           "s_cbranch_scc1 own8_open_%=\\n\\t" + gen_iter8(True, False)
+           + "s_branch own8_done_%=\\n\\town8_open_%=:\\n\\t" + gen_iter8(False, False) + "own8_done_%=:\\n\\t")
+    temps8 = [("OWN8_ASM_QLOAD", gen_qload8()), ("OWN8_ASM_COPY", gen_copy8()), ("OWN8_ASM_PRO", gen_pro(True)),
+              ("OWN8_ASM_IT", it8), ("OWN8_ASM_IT_FIRST", gen_iter8(True, True))]
+    for name, text in temps8:
+        body.append('#define %s "%s"' % (name, text))
+        body.append("")
+    body.append("#define OWN8_CLOB %s" % ", ".join('"v%d"' % r for r in range(CLOB_LO, 256)))
+    body.append("")
+    use_layout(*bf16_layout, False)
     new = "\n".join(body)
     if not os.path.exists(out) or open(out).read() != new:
         with open(out, "w") as f:

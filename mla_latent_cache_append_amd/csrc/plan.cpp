@@ -21,12 +21,14 @@ AttnPlan plan_attention(int32_t B, int32_t Lq, int32_t H) {
   return p;
 }
 
-// FP8 pool: the column kernel for every shape, 16 or 32 rows per row group.
+// FP8 pool: the 128-row kernel from 96 rows per sequence (codes widened in
+// the LDS), the column kernel below, 16 or 32 rows per row group.
 AttnPlan plan_attention_fp8(int32_t B, int32_t Lq, int32_t H) {
   (void)B;
   AttnPlan p;
   const int rows = Lq * H;
-  if (rows <= 16) { p.variant = V_COLS16; p.rg_rows = 16; }
+  if (rows >= 96) { p.variant = V_ROWS128; p.rg_rows = 128; }
+  else if (rows <= 16) { p.variant = V_COLS16; p.rg_rows = 16; }
   else { p.variant = V_COLS32; p.rg_rows = 32; }
   p.n_rg = (rows + p.rg_rows - 1) / p.rg_rows;
   p.width = (TARGET_WGS + p.n_rg - 1) / p.n_rg;

@@ -128,9 +128,10 @@ def test_fp8_decode_small(H, Lq, lens):
         check_outputs(w.name, w, out, b, ref)
 
 
-def test_fp8_zero_lengths_and_determinism():
-    w = workloads.Workload("fp8_short", 4, 16, 4, [0, 3, 5, 64], "contiguous", seed=19)
-    _say("fp8 lens [0, 3, 5, 64] with Lq=4, run twice")
+@pytest.mark.parametrize("H", [16, 128])
+def test_fp8_zero_lengths_and_determinism(H):
+    w = workloads.Workload("fp8_short", 4, H, 4, [0, 3, 5, 64], "contiguous", seed=19)
+    _say(f"fp8 H={H} lens [0, 3, 5, 64] with Lq=4, run twice")
     run = hz.GpuRun(w, fp8=True)
     out = run.run()
     again = run.run()
@@ -142,9 +143,10 @@ def test_fp8_zero_lengths_and_determinism():
         check_outputs(w.name, w, out, b, hz.oracle_seq_fp8(w, b))
 
 
-def test_fp8_bad_block_id_poisons_only_its_sequence():
-    w = workloads.Workload("fp8_poison", 3, 16, 1, [100, 100, 100], "contiguous", seed=14)
-    _say("fp8: block id out of range in seq 1 and seq_len beyond the table in seq 2")
+@pytest.mark.parametrize("H", [16, 128])   # the column kernel, the 128-row kernel
+def test_fp8_bad_block_id_poisons_only_its_sequence(H):
+    w = workloads.Workload("fp8_poison", 3, H, 1, [100, 100, 100], "contiguous", seed=14)
+    _say(f"fp8 H={H}: block id out of range in seq 1 and seq_len beyond the table in seq 2")
     run = hz.GpuRun(w, fp8=True)
     run.block_table[1, 1] = w.num_blocks
     run.seq_lens[2] = w.max_blocks * 64 + 1
