@@ -240,19 +240,23 @@ int mla_append_absorb_fp8(const mla_dims* dims, const uint16_t* c_kv, const uint
 
 /*
  * mla_decode_attn_fp8 — mla_decode_attn over the FP8 pool: C_t is the row the
- * codes stand for, code value x pool_scale of its slot. Scores are formed
- * from the exact code values in bf16 MFMAs and multiplied by the token scale
- * in fp32; probabilities are multiplied by the token scale before their bf16
- * rounding for the weighted sum (the row sum takes them unscaled). pool8 and
- * pool_scale must be 16-byte aligned. Every other argument, the workspace
- * (the same mla_decode_workspace_size), the alignment rules, the error codes,
- * the device-value handling and determinism are as for mla_decode_attn.
- * Where it pays: few query rows per sequence (up to 47: e.g. 16 heads), where
+ * codes stand for, code value x pool_scale of its slot. The scale being a
+ * power of two, code x scale is exactly a bf16 value, and the kernels use
+ * that row in the bf16 products: the 128-row kernel (96 or more query rows
+ * per sequence) widens code x scale to bf16 in the LDS; the column kernels
+ * (fewer rows) form scores from the codes and multiply them by the scale in
+ * fp32, and multiply probabilities by it before their bf16 rounding for the
+ * weighted sum. Both give the same scores and terms, exactly, up to
+ * summation order (scaling by a power of two commutes with rounding). pool8
+ * and pool_scale must be 16-byte aligned. Every other argument, the
+ * workspace (the same mla_decode_workspace_size), the alignment rules, the
+ * error codes, the device-value handling and determinism are as for
+ * mla_decode_attn.
+ * Cost against the bf16 pool: with few query rows per sequence (16 heads)
  * the call is bound by memory and half the bytes make it faster (16 heads,
- * 4,096 keys: ~50 against ~60 us in bf16). Above that the call runs on the
- * same 32-row kernel, with every group of 32 rows streaming the whole key
- * range: at 128 heads it takes 2.3-2.9 times as long as the bf16 call, so
- * keep a bf16 pool there.
+ * 4,096 keys: ~48 against ~60 us); at 128 heads both run on the 128-row
+ * kernel, bound by its products, and take about the same time (16,384 keys:
+ * ~152 against ~153-160 us), so FP8 there saves memory, not time.
  */
 int mla_decode_attn_fp8(const mla_dims* dims, const uint16_t* q, const uint8_t* pool8,
                         const float* pool_scale, int64_t num_blocks, const int32_t* block_table,
