@@ -1192,60 +1192,29 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     }
     // Half tile e+3 goes into the stage of e-1; its nine copies are spread
     // over the iteration's instruction sequence, which keeps the vector
-    // memory queue from stalling the wave. The descriptor of the next
-    // iteration's copies is prepared between the sequences with 32-bit
-    // scalar arithmetic (a lone wave issues about one instruction per four
-    // cycles, and the MFMA pipe idles meanwhile); the K / V^T addresses and
-    // the mask limit move on inside the sequences, under the PV MFMAs.
+    // memory queue from stalling the wave. The same sequence loads the block
+    // id of half tile e+4 (a scalar load issued before its first LDS read)
+    // and forms the descriptor of the next iteration's copies from it under
+    // its last PV MFMAs, so that nothing but the loop test, the copy wait
+    // and the barrier runs between the sequences (a lone wave issues about
+    // one instruction per four cycles, and the MFMA pipe idles meanwhile);
+    // the K / V^T addresses and the mask limit move on inside the sequences
+    // too. Descriptor: base = pool + blk * 73,728 + (ep & 1) * 36,864 (bits
+    // 47..32 in its second word), bytes = 1,152 * min(32, L - 32 ep), or 0
+    // past the segment or for a block id outside the pool; such an id inside
+    // the segment sets badacc.
+    static_assert(TILE_BYTES == 0x12000 && HT_BYTES == 0x9000 && ROW_BYTES == 0x480 && HT_TOK == 32 &&
+                      OSTAGE == 4, "constants of the descriptor sequence");
     sgpr_x4 rs;
     uint32_t mb;
     prep(e0 + OSTAGE - 1, blk_of(e0 + OSTAGE - 1), rs, mb);
     k_addr(e0 + 1 < e1 ? e0 + 1 : e0);
     v_addr(e0);
     const uint32_t mb0 = (uint32_t)uni((int)lds_addr(stages + wave * 9 * 1024));
-    // copies of half tile ep from block blk: pool + blk * 73,728 + (ep & 1) * 36,864,
-    // min(32, L - 32 ep) rows; none past the segment or for a block id outside the pool
-    // Straight-line scalar code (no branches; a lone wave pays for every
-    // taken branch with a refetch): base = pool + blk * 73,728 + (ep & 1) *
-    // 36,864 (bits 47..32 in the descriptor's second word), bytes = 1,152 *
-    // min(32, L - 32 ep), or 0 past the segment or for a block id outside the
-    // pool; such an id inside the segment sets badacc.
-    static_assert(TILE_BYTES == 0x12000 && HT_BYTES == 0x9000 && ROW_BYTES == 0x480 && HT_TOK == 32 &&
-                      OSTAGE == 4, "constants of the descriptor sequence");
+    const int64_t bt_u = uni64((int64_t)(uintptr_t)bt);   // the sequence's block-table row, in SGPRs
+    const int nt1 = uni(ntiles - 1);
+    mb = (uint32_t)uni((int)mb);
     uint32_t badacc = 0;
-    auto prep_next = [&](int ep, int blk) {
-      uint32_t r0, r1, r2, r3;
-      asm volatile(
-          "s_mul_i32 %[r0], %[blk], 0x12000\n\t"
-          "s_mul_hi_u32 %[r1], %[blk], 0x12000\n\t"
-          "s_bitcmp1_b32 %[ep], 0\n\t"
-          "s_cselect_b32 %[r2], 0x9000, 0\n\t"
-          "s_add_u32 %[r0], %[r0], %[r2]\n\t"
-          "s_addc_u32 %[r1], %[r1], 0\n\t"
-          "s_add_u32 %[r0], %[r0], %[plo]\n\t"
-          "s_addc_u32 %[r1], %[r1], %[phi]\n\t"
-          "s_and_b32 %[r1], %[r1], 0xffff\n\t"
-          "s_lshl_b32 %[r2], %[ep], 5\n\t"
-          "s_sub_i32 %[r2], %[L], %[r2]\n\t"
-          "s_min_i32 %[r2], %[r2], 32\n\t"
-          "s_mul_i32 %[r2], %[r2], 0x480\n\t"
-          "s_cmp_ge_u32 %[blk], %[nblk]\n\t"
-          "s_cselect_b32 %[r3], 1, 0\n\t"
-          "s_cselect_b32 %[r2], 0, %[r2]\n\t"
-          "s_cmp_lt_i32 %[ep], %[e1]\n\t"
-          "s_cselect_b32 %[r3], %[r3], 0\n\t"
-          "s_cselect_b32 %[r2], %[r2], 0\n\t"
-          "s_or_b32 %[bd], %[bd], %[r3]\n\t"
-          "s_mov_b32 %[r3], 0x20000\n\t"
-          "s_and_b32 %[mb], %[ep], 3\n\t"
-          "s_mul_i32 %[mb], %[mb], 0x9000\n\t"
-          "s_add_u32 %[mb], %[mb], %[mb0]"
-          : [r0] "=&s"(r0), [r1] "=&s"(r1), [r2] "=&s"(r2), [r3] "=&s"(r3), [mb] "=&s"(mb), [bd] "+s"(badacc)
-          : [blk] "s"(blk), [ep] "s"(ep), [plo] "s"(pool_lo), [phi] "s"(pool_hi), [L] "s"(L), [nblk] "s"(nblk),
-            [e1] "s"(e1), [mb0] "s"(mb0)
-          : "scc");
-      rs = sgpr_x4{r0, r1, r2, r3};
-    };
     // half tiles below e_open hold only keys every row may see (no key mask)
     const int e_open = max(0, L - a.Lq + 1) / HT_TOK;
     int lr = lim - ((e0 + 1) * HT_TOK + 4 * h);   // mask limit of the scores of e0+1 (the sequence moves it on)
@@ -1256,25 +1225,30 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
       const bool more = e + 1 < e1;
       wait_vmem_n<9>();          // stage e+1 complete; the copies of e+2 may be in flight
       // stage e+1 visible; stage e-1 free. The sequence ends with every LDS
-      // read done, so the barrier needs no lgkmcnt wait, and the block-id
-      // scalar load issued right after it completes under the MFMAs.
+      // read done, so the barrier needs no lgkmcnt wait.
       asm volatile("s_barrier" ::: "memory");
-      // for the copies prepared at the end (past the sequence's last tile any
-      // id of it will do: those copies cover zero bytes)
-      const int blk_next = bt[min((e + OSTAGE) >> 1, ntiles - 1)];
       int t0, t1, t2;
+      uint32_t r0, r1, r2, r3, blkv;
 #define OWN_ITER(NAME, OPS_O)                                                                         \
   asm volatile(NAME                                                                                   \
                : OPS_O, OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "+v"(alpha),       \
-                 [mref] "+v"(mref), [lr] "+v"(lr), OWN_OPS_KA_IO, OWN_OPS_VA_IO, OWN_OPS_BOOK_OUT     \
+                 [mref] "+v"(mref), [lr] "+v"(lr), OWN_OPS_KA_IO, OWN_OPS_VA_IO, OWN_OPS_BOOK_OUT,    \
+                 OWN_OPS_PREP_OUT                                                                     \
                : OWN_OPS_Q, [scale] "s"(a.scale_log2), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO,      \
-                 OWN_OPS_BOOK_IN                                                                      \
+                 OWN_OPS_BOOK_IN, OWN_OPS_PREP_IN                                                     \
                : OWN_CLOB, "vcc", "m0", "scc", "memory")
       if constexpr (FIRST)
         OWN_ITER(OWN_ASM_IT_FIRST, OWN_OPS_O_OUT);
       else
         OWN_ITER(OWN_ASM_IT, OWN_OPS_O);
 #undef OWN_ITER
+      // the copies of half tile e+4, issued by the next sequence. The values
+      // are in SGPRs, but an asm statement with vector outputs counts as
+      // divergent to the compiler: readfirstlane marks them uniform, so that
+      // the loop carries them in SGPRs.
+      rs = sgpr_x4{(uint32_t)uni((int)r0), (uint32_t)uni((int)r1), (uint32_t)uni((int)r2), (uint32_t)uni((int)r3)};
+      mb = (uint32_t)uni((int)mb);
+      badacc = (uint32_t)uni((int)badacc);
       // alpha belongs to half tile e+1, whose PV runs in the next iteration
       if (more && __any(alpha != 1.f)) {
         // the sequence's last PV MFMAs may still be writing the accumulators
@@ -1282,7 +1256,6 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
 #pragma unroll
         for (int cb = 0; cb < 16; ++cb) scale_acc(o[cb], alpha);
       }
-      prep_next(e + OSTAGE, blk_next);
     };
     step(e0, std::true_type{});
     for (int e = e0 + 1; e < e1; ++e) step(e, std::false_type{});

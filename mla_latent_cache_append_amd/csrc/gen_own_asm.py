@@ -74,9 +74,11 @@ GUARD = ["s_nop 7", "s_nop 7", "s_nop 7"]
 # together they stall the issuing waves; issued in phase P they arrive later)
 DMA_S = [1, 5, 9, 13, 17, 21, 25, 29, 33]
 DMA_P = []
-S_VALU_STEPS = 16    # score MFMAs that carry the probability half of the softmax
+S_VALU_STEPS = int(os.environ.get("OWN_S_VALU", "16"))   # score MFMAs that carry the probability half
+EXP_SKEW = int(os.environ.get("OWN_EXP_SKEW", "0"))      # probability i's exp placed after fma i + skew
 P_VALU_FROM = 3      # PV MFMA after which the max half of the softmax starts
 BOOK_FROM = 4        # PV MFMA after which the scalar bookkeeping starts
+PREP_AT = int(os.environ.get("OWN_PREP_AT", "29"))       # PV MFMA before which every LDS read (and the block id) is waited for
 
 
 class Seq:
@@ -213,9 +215,13 @@ def softmax_exp():
     running l (after alpha), and the bf16 packing into P for the PV MFMAs."""
     tb = TMP[0]
     v = []
-    for i in range(16):
-        v.append("v_fma_f32 %%[s%d], %%[s%d], %%[scale], -%%[mref]" % (i, i))
-        v.append("v_exp_f32 %%[s%d], %%[s%d]" % (i, i))
+    # exp i follows fma i + EXP_SKEW, so that it does not wait on the result
+    # of the instruction just before it
+    for k in range(16 + EXP_SKEW):
+        if k < 16:
+            v.append("v_fma_f32 %%[s%d], %%[s%d], %%[scale], -%%[mref]" % (k, k))
+        if k >= EXP_SKEW:
+            v.append("v_exp_f32 %%[s%d], %%[s%d]" % (k - EXP_SKEW, k - EXP_SKEW))
     v.append("v_add_f32 %s, %%[s0], %%[s1]" % tb)
     for i in range(2, 16):
         v.append("v_add_f32 %s, %s, %%[s%d]" % (tb, tb, i))
@@ -257,6 +263,41 @@ def book_keeping():
     return b, tail
 
 
+def blk_load():
+    """Block id of half tile ep = e + 4 (the copies the next sequence
+    issues): bt[min(ep / 2, ntiles - 1)], a scalar load issued before any
+    LDS read of the sequence. While it is outstanding the lgkmcnt waits
+    below, counted for the LDS reads alone, wait for one read more than
+    needed; the full drain at PV step PREP_AT waits for it."""
+    return ["s_lshr_b32 %[t0], %[ep], 1",
+            "s_min_i32 %[t0], %[t0], %[nt1]",
+            "s_lshl_b32 %[t0], %[t0], 2",
+            "s_load_dword %[blk], %[bt], %[t0]"]
+
+
+def prep_groups():
+    """Descriptor (r0..r3) and LDS base (mb) of the copies of half tile
+    ep = e + 4 from its block id: base = pool + blk * 73,728 + (ep & 1) *
+    36,864 (bits 47..32 in r1), bytes = 1,152 * min(32, L - 32 ep), or 0 past
+    the segment (ep >= e1) or for a block id outside the pool, which inside
+    the segment sets bd. Groups are emitted whole, so that no other SCC
+    writer falls inside a compare / select or carry chain; mb is read by
+    the sequence's copies, all issued before these."""
+    return [
+        ["s_mul_i32 %[r0], %[blk], 0x12000", "s_mul_hi_u32 %[r1], %[blk], 0x12000"],
+        ["s_bitcmp1_b32 %[ep], 0", "s_cselect_b32 %[r2], 0x9000, 0"],
+        ["s_add_u32 %[r0], %[r0], %[r2]", "s_addc_u32 %[r1], %[r1], 0"],
+        ["s_add_u32 %[r0], %[r0], %[plo]", "s_addc_u32 %[r1], %[r1], %[phi]"],
+        ["s_and_b32 %[r1], %[r1], 0xffff"],
+        ["s_lshl_b32 %[r2], %[ep], 5", "s_sub_i32 %[r2], %[L], %[r2]"],
+        ["s_min_i32 %[r2], %[r2], 32", "s_mul_i32 %[r2], %[r2], 0x480"],
+        ["s_cmp_ge_u32 %[blk], %[nblk]", "s_cselect_b32 %[r3], 1, 0", "s_cselect_b32 %[r2], 0, %[r2]"],
+        ["s_cmp_lt_i32 %[ep], %[e1]", "s_cselect_b32 %[r3], %[r3], 0", "s_cselect_b32 %[r2], %[r2], 0"],
+        ["s_or_b32 %[bd], %[bd], %[r3]", "s_mov_b32 %[r3], 0x20000"],
+        ["s_and_b32 %[mb], %[ep], 3", "s_mul_i32 %[mb], %[mb], 0x9000", "s_add_u32 %[mb], %[mb], %[mb0]"],
+    ]
+
+
 def gen_qload():
     """Start of a segment: the copies of the first half tile, the 36 query
     fragments straight into registers (row 32 wave + l % 32 at byte offset
@@ -295,6 +336,8 @@ def gen_iter(mask, first):
     with PV MFMAs in flight: code after it that reads the accumulators waits
     first (GUARD)."""
     s = Seq()
+    for ins in blk_load():
+        s.op(ins)
     s.op("s_nop 1")
     for ks in range(PF_K):
         kread(s, ks)
@@ -328,7 +371,11 @@ def gen_iter(mask, first):
     # bookkeeping from PV step BOOK_FROM on, the V^T address update after the
     # last V^T read (issued at step 31 - PF_V), the rescale test at the end
     bper = (len(book) + (31 - PF_V - BOOK_FROM) - 1) // (31 - PF_V - BOOK_FROM)   # at least one per step
+    prep = prep_groups()
+    pper = (len(prep) + (32 - PREP_AT) - 1) // (32 - PREP_AT)
     for j in range(32):
+        if j == PREP_AT:
+            s.drain()          # the last V^T reads and the block id
         s.need("V%db" % j)
         cb, kk = pv_step(j)
         acc = "0" if first and kk == 0 else "%%[o%d]" % cb   # first half tile: start from 0
@@ -353,7 +400,12 @@ def gen_iter(mask, first):
         if j == 32 - PF_V:
             for ins in book_tail:
                 s.op(ins)
+        if j >= PREP_AT:       # the next copies' descriptor, under the last PV MFMAs
+            for g in prep[(j - PREP_AT) * pper:(j - PREP_AT + 1) * pper]:
+                for ins in g:
+                    s.op(ins)
     assert (32 - P_VALU_FROM - 6) * mper >= len(max_valu) and (31 - PF_V - BOOK_FROM) * bper >= len(book)
+    assert 32 - PF_V < PREP_AT and 31 - PF_V <= PREP_AT and P_VALU_FROM + 32 - P_VALU_FROM - 6 <= PREP_AT
     s.drain()
     return s.text()
 
@@ -625,7 +677,12 @@ def main():
         "OWN_OPS_VA_IO": ", ".join('[va%d] "+v"(va[%d])' % (i, i) for i in range(4)),
         # bookkeeping operands: scratch SGPRs (outputs never read), then uniform inputs
         "OWN_OPS_BOOK_OUT": '[t0] "=&s"(t0), [t1] "=&s"(t1), [t2] "=&s"(t2)',
-        "OWN_OPS_BOOK_IN": '[ep] "s"(e + OSTAGE), [eo] "s"(e_open), [e1] "s"(e1), [mb] "s"(mb)',
+        "OWN_OPS_BOOK_IN": '[ep] "s"(e + OSTAGE), [eo] "s"(e_open), [e1] "s"(e1)',
+        # the next copies' descriptor: outputs (r0..r3 form rs; blk is scratch) and inputs
+        "OWN_OPS_PREP_OUT": ('[r0] "=&s"(r0), [r1] "=&s"(r1), [r2] "=&s"(r2), [r3] "=&s"(r3), '
+                             '[blk] "=&s"(blkv), [bd] "+s"(badacc), [mb] "+s"(mb)'),
+        "OWN_OPS_PREP_IN": ('[bt] "s"(bt_u), [nt1] "s"(nt1), [plo] "s"(pool_lo), [phi] "s"(pool_hi), '
+                            '[L] "s"(L), [nblk] "s"(nblk), [mb0] "s"(mb0)'),
         "OWN_OPS_S_OUT": ", ".join('[s%d] "=&v"(s[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_S": ", ".join('[s%d] "+v"(s[%d])' % (i, i) for i in range(16)),
         "OWN_OPS_O": ", ".join('[o%d] "+a"(o[%d])' % (i, i) for i in range(16)),
