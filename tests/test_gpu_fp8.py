@@ -112,6 +112,7 @@ def test_fp8_append_skips_out_of_range_slots_and_zero_row():
     (128, 1, [1, 64, 65, 700]),
     (128, 8, [8, 9, 71, 200]),
     (16, 3, [3, 4, 64, 66, 190]),
+    (32, 3, [3, 33, 96, 300]),       # 96 rows: the 128-row kernel's threshold, its fourth wave all padding
     # prefill chunks over the FP8 cache: many query tokens, causal among themselves
     (128, 64, [64, 100, 1000]),
     (16, 203, [203, 777]),

@@ -76,6 +76,7 @@ def test_append_skips_out_of_range_slots():
     (128, 1, [1, 64, 65, 700]),
     (128, 8, [8, 9, 71, 200]),
     (16, 3, [3, 4, 64, 66, 190]),
+    (32, 3, [3, 33, 96, 300]),       # 96 rows: the 128-row kernel's threshold, its fourth wave all padding
     # prefill chunks: many query tokens per sequence, causal among themselves
     (128, 64, [64, 100, 1000]),
     (16, 203, [203, 777]),
