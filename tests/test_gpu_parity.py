@@ -101,14 +101,24 @@ def test_many_short_sequences_multi_segment():
         hz.check_seq(w.name, w, out, b)
 
 
-def test_zero_and_short_lengths():
-    w = workloads.Workload("short", 4, 16, 4, [0, 3, 5, 64], "contiguous", seed=9)
-    _say("lens [0, 3, 5, 64] with Lq=4: empty sequence and negative positions")
+@pytest.mark.parametrize("H,Lq,lens", [
+    (16, 4, [0, 3, 5, 64]),       # 64 rows: the 64-row kernel, merged by the merge launch
+    (16, 1, [0, 3, 5, 64]),       # 16 rows: the column kernel, which merges its own partials
+    (16, 2, [0, 70, 0, 3000]),    # 32 rows, empty sequences between split ones
+    (16, 1, [0, 0, 0]),           # no keys at all
+], ids=lambda v: str(v))
+def test_zero_and_short_lengths(H, Lq, lens):
+    w = workloads.Workload("short", len(lens), H, Lq, lens, "contiguous", seed=9)
+    _say(f"lens {lens} with Lq={Lq}, H={H}: empty sequences (and positions below 0)")
     out = hz.GpuRun(w).run()
-    o_lat = orc.bf16_bits_to_f64(out["o_lat"][0:4])
-    assert np.all(o_lat == 0) and np.all(out["lse"][0:4] == -np.inf)
-    for b in (1, 2, 3):
-        hz.check_seq(w.name, w, out, b)
+    rows = Lq * H
+    for b, L in enumerate(lens):
+        if L == 0:
+            o_lat = orc.bf16_bits_to_f64(out["o_lat"][b * Lq:(b + 1) * Lq])
+            assert np.all(o_lat == 0) and np.all(out["lse"][b * Lq:(b + 1) * Lq] == -np.inf), b
+        else:
+            hz.check_seq(w.name, w, out, b)
+    assert out["o_lat"].shape[0] * out["o_lat"].shape[1] == len(lens) * rows
 
 
 # ------------------------------------------------------------------ tiny V2-Lite layer
