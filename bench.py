@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device read (a sum) and a 1 GiB device write (a fill), "
                          "the calibration of the traffic counters")
+    ap.add_argument("--crossover", action="store_true",
+                    help="instead of the decode step: time a causal prefill chunk of Lq tokens per sequence "
+                         "(B=4, 128 heads, 16,384 cached tokens) in the absorbed form (absorb_q + attention + "
+                         "out_up) and in the expanded form (mla_prefill_expanded) for several Lq, one JSON line")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="parse two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench "
                          "with --copy-calib into profiles/traffic_<cache>_<workload>.json, then exit")
@@ -277,8 +281,128 @@ def cpu_baseline(w, budget_s: float) -> dict:
                       f"L={int(w.lens[0])}, H={w.H}; fp64 NumPy absorbed path, BLAS {blas}), {spent:.1f} s"}
 
 
+def crossover(args) -> None:
+    """Absorbed against expanded form on one cache: B sequences of HIST
+    cached tokens plus a chunk of Lq new ones (already in the cache), every
+    query token attending causally. Each form runs as a HIP graph of
+    CROSS_CALLS calls when it captures (else eager calls), median of
+    CROSS_REPS timed replays; flops are the algorithm's for each form."""
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import workloads
+    from mla_latent_cache_append_amd import native as nat
+    from mla_latent_cache_append_amd.step import DecodeStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    B, H, HIST = 4, 128, 16384
+    lqs = (32, 64, 128, 256, 512, 1024, 2048)
+    lmax = HIST + max(lqs)
+    dev = torch.device("cuda")
+    w = workloads.Workload("crossover_b4_h128", B, H, max(lqs), [lmax] * B, "permuted", args.seed)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wuk, wuv = (to_dev(x) for x in w.weights())
+    pool = torch.empty((w.num_blocks, 64, 576), dtype=torch.bfloat16, device=dev)
+    block_table = torch.from_numpy(w.block_table).to(dev)
+    dims = nat.mla_dims_default(H)
+    for b in range(B):   # every token of the longest chunk in the cache
+        ckv, kpe = w.seq_cache(b)
+        for s0 in range(0, lmax, 65536):
+            p = np.arange(s0, min(lmax, s0 + 65536))
+            nat.mla_cache_append(dims, to_dev(ckv[p]), to_dev(kpe[p]), torch.from_numpy(p.astype(np.int32)).to(dev),
+                                 torch.from_numpy(w.slots(b, p)).to(dev), pool)
+        print(f"[bench] filled sequence {b}/{B}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        mode = "graph"
+        try:
+            g = _capture_graph(torch, lambda: [fn() for _ in range(CROSS_CALLS)])
+            run = g.replay
+        except Exception:   # a library call that does not capture: eager calls
+            mode = "eager"
+            torch.cuda.synchronize()
+
+            def run():
+                for _ in range(CROSS_CALLS):
+                    fn()
+        run()
+        us = []
+        for _ in range(CROSS_REPS):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            e1.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3 / CROSS_CALLS)
+        return float(np.median(us)), mode
+
+    series = []
+    for lq in lqs:
+        L = HIST + lq
+        N = B * lq
+        seq_lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        qn = to_dev(workloads.normal_bf16((args.seed, workloads.TAG_QNOPE, lq), (N, H, 128)))
+        qp = to_dev(workloads.normal_bf16((args.seed, workloads.TAG_QPE, lq), (N, H, 64)))
+        pos = torch.from_numpy(np.tile(np.arange(HIST, L, dtype=np.int32), B)).to(dev)
+        q = torch.empty((N, H, 576), dtype=torch.bfloat16, device=dev)
+        o_lat = torch.empty((N, H, 512), dtype=torch.bfloat16, device=dev)
+        o_a = torch.empty((N, H, 128), dtype=torch.bfloat16, device=dev)
+        o_x = torch.empty((N, H, 128), dtype=torch.bfloat16, device=dev)
+        ws_a = torch.empty(nat.mla_decode_workspace_size(dims, B, lq), dtype=torch.uint8, device=dev)
+        ws_x = torch.empty(nat.mla_prefill_expanded_workspace_size(dims, B, L), dtype=torch.uint8, device=dev)
+
+        def absorbed():
+            nat.mla_absorb_q(dims, qn, qp, pos, wuk, q)
+            nat.mla_decode_attn(dims, q, pool, block_table, seq_lens, lq, o_lat, workspace=ws_a)
+            nat.mla_out_up(dims, o_lat, wuv, o_a)
+
+        def expanded():
+            nat.mla_prefill_expanded(dims, qn, qp, pos, pool, block_table, seq_lens, lq, L, wuk, wuv, o_x,
+                                     workspace=ws_x)
+
+        a_us, a_mode = timed(absorbed)
+        x_us, x_mode = timed(expanded)
+        torch.cuda.synchronize()
+        # the two forms' outputs on the same inputs agree to bf16 rounding
+        diff = (o_a.float() - o_x.float()).abs().mean().item() / max(o_a.float().abs().mean().item(), 1e-30)
+        pairs = B * (lq * HIST + lq * (lq + 1) // 2)          # (query, visible key) pairs
+        f_a = 2 * H * pairs * (576 + 512) + 2 * 2 * N * H * 128 * 512
+        f_x = 2 * B * L * H * 256 * 512 + 2 * H * pairs * (192 + 128)
+        series.append(dict(Lq=lq, keys=L, absorbed_us=a_us, expanded_us=x_us, speedup=a_us / x_us,
+                           absorbed_tflops=f_a / a_us / 1e6, expanded_tflops=f_x / x_us / 1e6,
+                           absorbed_gflop=f_a / 1e9, expanded_gflop=f_x / 1e9, timing=[a_mode, x_mode],
+                           mean_rel_diff=diff))
+        print(f"[bench] Lq={lq}: absorbed {a_us:.1f} us, expanded {x_us:.1f} us", file=sys.stderr, flush=True)
+        del ws_x, ws_a
+        torch.cuda.empty_cache()
+    cross = None
+    for s0, s1 in zip(series, series[1:]):
+        if s0["speedup"] < 1.0 <= s1["speedup"]:   # interpolate in log Lq
+            t = (1.0 - s0["speedup"]) / (s1["speedup"] - s0["speedup"])
+            cross = float(np.exp(np.log(s0["Lq"]) + t * (np.log(s1["Lq"]) - np.log(s0["Lq"]))))
+    print(json.dumps({"metric": "prefill chunk time, absorbed vs expanded form", "unit": "us",
+                      "config": {"workload": "crossover_b4_h128", "B": B, "H": H, "cached_tokens": HIST,
+                                 "Lq": list(lqs)},
+                      "series": series, "crossover_Lq": cross, "data": "synthetic"}), flush=True)
+
+
+CROSS_CALLS = 5
+CROSS_REPS = 5
+
+
 def main():
     args = parse()
+    if args.crossover:
+        crossover(args)
+        return
     if args.traffic_from:
         t = traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
         t["cache"] = args.cache

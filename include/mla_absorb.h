@@ -265,6 +265,51 @@ int mla_decode_attn_fp8(const mla_dims* dims, const uint16_t* q, const uint8_t* 
                         void* stream);
 
 /*
+ * Expanded-form attention for long query chunks ([MLA80] §2: the model's
+ * forward expands per-head keys and values from the latent, k_c[t,h] =
+ * W_UK[h] c_kv[t] and v[t,h] = W_UV[h] c_kv[t], concatenates the shared RoPE
+ * key and runs multi-head attention; [MLA80] §3 times prefill in that form).
+ * It computes what mla_absorb_q + mla_decode_attn + mla_out_up compute
+ * together, o[n,h] = sum_t softmax_t(q[n,h].k[t,h] scale) v[t,h] with
+ * q = [q_nope | RoPE(q_pe, pos)], k = [k_c | k_r], over the same visible keys
+ * (query token i of a sequence of L keys sits at L - Lq + i), by another
+ * route: 2 L H 256 512 flops for the expansion plus 2 H Lq L (192 + 128) for
+ * the attention, against 2 H Lq L (576 + 512) for the absorbed form, so it
+ * pays once a chunk holds a few hundred query tokens per sequence.
+ *   Steps, on `stream`: the sequence's cache rows are gathered into the
+ *   workspace, W_UK and W_UV expand them in two bf16 GEMMs per sequence
+ *   (hipBLASLt; fp32 accumulation, one rounding of k_c and v to bf16), and a
+ *   causal attention kernel forms the scores in bf16 MFMAs, the softmax in
+ *   fp32 and o in one rounding to bf16. The expansion runs over max_len rows
+ *   for every sequence.
+ *   q_nope [B*Lq][H][128] bf16, q_pe [B*Lq][H][64] bf16 (not rotated),
+ *   pos [B*Lq] int32: the queries, as for mla_absorb_q (token n = b*Lq + i).
+ *   pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, B, Lq: as
+ *   for mla_decode_attn (seq_lens include the chunk's own tokens).
+ *   max_len: host bound on every seq_lens[b]; a sequence longer than max_len
+ *   gets NaN outputs, one with a block id outside the pool NaN outputs.
+ *   w_uk, w_uv [H][128][512] bf16 (nn.Linear rows, as for mla_absorb_q and
+ *   mla_out_up).
+ *   o [B*Lq][H][128] bf16 out; lse [B*Lq][H] fp32 out or NULL (natural log of
+ *   the sum of exp of the scaled scores; -inf and o = 0 for a row that sees
+ *   no key).
+ *   workspace: device memory of mla_prefill_expanded_workspace_size bytes,
+ *   256-byte aligned, contents ignored (the expanded K and V^T: 2 B max_len
+ *   H 256 bytes plus the gathered rows).
+ * Pointers 16-byte aligned (lse 4-byte). Errors: MLA_ERR_INVALID_ARG (null,
+ * non-positive size, misalignment), MLA_ERR_UNSUPPORTED (B > 65,535, Lq or
+ * max_len > 2^20, B*Lq > 2^30), MLA_ERR_WORKSPACE, MLA_ERR_LAUNCH (a launch
+ * or a GEMM failed to enqueue), all before anything is enqueued except the
+ * last.
+ */
+size_t mla_prefill_expanded_workspace_size(const mla_dims* dims, int32_t B, int32_t max_len);
+int mla_prefill_expanded(const mla_dims* dims, const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                         const uint16_t* pool, int64_t num_blocks, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B, int32_t Lq,
+                         int32_t max_len, const uint16_t* w_uk, const uint16_t* w_uv, uint16_t* o, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Two-buffer latent cache ([AUDIT] §0: the V3 reference's absorbed decode
  * keeps kv_cache [1,32,512] and pe_cache [1,32,64]; §4.2: a 32-slot buffer,
  * 32,768 + 4,096 = 36,864 bytes allocated for 26 active tokens). The same

@@ -10,7 +10,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_absorb.so")
 PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
-SOURCES = ["append.hip", "gemm.hip", "linear.hip", "attn.hip", "plan.cpp", "capi.cpp"]
+SOURCES = ["append.hip", "gemm.hip", "linear.hip", "attn.hip", "expand.hip", "plan.cpp", "capi.cpp"]
+# the expanded-form prefill's two expansion GEMMs are plain matrix products (hipBLASLt)
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -30,7 +32,7 @@ def build(verbose: bool = False) -> str:
     gen_own_asm.main()
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES] + LIBS
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -127,6 +127,36 @@ int mla_decode_attn(const mla_dims* dims, const uint16_t* q, const uint16_t* poo
                                                (hipStream_t)stream));
 }
 
+size_t mla_prefill_expanded_workspace_size(const mla_dims* dims, int32_t B, int32_t max_len) {
+  if (check_dims(dims) != MLA_OK || B <= 0 || B > 65535 || max_len <= 0 || max_len > (1 << 20)) return 0;
+  return mla::expanded_layout(B, dims->num_heads, max_len).bytes;
+}
+
+int mla_prefill_expanded(const mla_dims* dims, const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                         const uint16_t* pool, int64_t num_blocks, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B, int32_t Lq,
+                         int32_t max_len, const uint16_t* w_uk, const uint16_t* w_uv, uint16_t* o, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !q_pe || !pos || !pool || !block_table || !seq_lens || !w_uk || !w_uv || !o ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || B <= 0 || Lq <= 0 || max_len <= 0)
+    return MLA_ERR_INVALID_ARG;
+  // 16-byte loads of q, the cache and the weights; 8-byte stores of o
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(pool, 16) || !aligned(w_uk, 16) ||
+      !aligned(w_uv, 16) || !aligned(o, 16) || !aligned(lse, 4) || !aligned(workspace, 256))
+    return MLA_ERR_INVALID_ARG;
+  // one launch dimension per sequence (65,535 at most); 2^20 keys and query tokens
+  if (B > 65535 || max_len > (1 << 20) || Lq > (1 << 20) || (int64_t)B * Lq > (1 << 30) ||
+      (int64_t)max_blocks_per_seq * mla::BLOCK > (1 << 30))
+    return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla::expanded_layout(B, dims->num_heads, max_len).bytes;
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  return launch_status(mla::launch_prefill_expanded(
+      q_nope, q_pe, pos, pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, B, Lq, dims->num_heads,
+      max_len, w_uk, w_uv, dims->softmax_scale, (double)dims->rope_base, o, lse, workspace, (hipStream_t)stream));
+}
+
 int mla_decode_attn_noalloc(const mla_dims* dims, const uint16_t* q, const uint16_t* pool,
                             int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
                             const int32_t* seq_lens, int32_t B, int32_t Lq, uint16_t* o_lat, float* lse,

@@ -74,6 +74,25 @@ AttnPlan plan_attention(int32_t B, int32_t Lq, int32_t H);
 AttnPlan plan_attention_fp8(int32_t B, int32_t Lq, int32_t H);
 AttnPlan plan_attention_kvpe(int32_t B, int32_t Lq, int32_t H);
 
+// Workspace of the expanded-form attention (expand.hip): the gathered latent
+// rows c [B][Lpad][512] and rope keys [B][Lpad][64], the expanded content keys
+// K [B][Lpad][H 128] and the transposed values V^T [B][H 128][Lpad], each
+// region on a 256-byte boundary; Lpad = max_len rounded up to 32.
+struct ExpandedLayout {
+  int32_t Lpad;
+  size_t c_off, kr_off, k_off, vt_off, bytes;
+};
+ExpandedLayout expanded_layout(int32_t B, int32_t H, int32_t max_len);
+
+// Expanded-form attention of Lq query tokens per sequence: gather, the two
+// expansion GEMMs per sequence, the attention kernel (expand.hip).
+hipError_t launch_prefill_expanded(const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                                   const uint16_t* pool, int64_t num_blocks, const int32_t* block_table,
+                                   int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
+                                   int32_t max_len, const uint16_t* w_uk, const uint16_t* w_uv,
+                                   float softmax_scale, double rope_base, uint16_t* o, float* lse,
+                                   void* workspace, hipStream_t stream);
+
 // Partial-result slots of one call: width + B (one per (workgroup, sequence) pair).
 size_t attention_workspace_bytes(int32_t B, int32_t Lq, int32_t H);
 // Bytes of the workspace's (m, l) part; the bf16 partials start there.

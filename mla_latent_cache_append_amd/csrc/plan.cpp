@@ -66,6 +66,20 @@ size_t attention_workspace_bytes(int32_t B, int32_t Lq, int32_t H) {
   return attention_ws_ml_bytes(B, Lq, H) + ws_slots(B, Lq, H) * (size_t)Lq * (size_t)H * D_C * sizeof(uint16_t);
 }
 
+ExpandedLayout expanded_layout(int32_t B, int32_t H, int32_t max_len) {
+  auto r256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  ExpandedLayout w;
+  w.Lpad = (max_len + 31) / 32 * 32;
+  const size_t rows = (size_t)B * (size_t)w.Lpad;
+  const size_t hd = (size_t)H * D_NOPE;
+  w.c_off = 0;
+  w.kr_off = w.c_off + r256(rows * D_C * sizeof(uint16_t));
+  w.k_off = w.kr_off + r256(rows * D_ROPE * sizeof(uint16_t));
+  w.vt_off = w.k_off + r256(rows * hd * sizeof(uint16_t));
+  w.bytes = w.vt_off + r256(rows * hd * sizeof(uint16_t));
+  return w;
+}
+
 LinearPlan plan_linear(int32_t N, int32_t K, int32_t M, bool can_split) {
   LinearPlan p;
   const int64_t ny = (N + LIN_N - 1) / LIN_N;

@@ -70,6 +70,9 @@ _SIG = {
     "mla_decode_attn_kvpe": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I32, _P, _I32, _I32, _P, _P,
                                             _P, ctypes.c_size_t, _P]),
     "mla_out_up": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I32, _P]),
+    "mla_prefill_expanded_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaDims), _I32, _I32]),
+    "mla_prefill_expanded": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
+                                            _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "mla_linear_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "mla_linear": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _P, ctypes.c_size_t, _P]),
 }
@@ -180,6 +183,40 @@ def mla_decode_attn(dims: MlaDims, q, pool, block_table, seq_lens, Lq: int, o_la
         ctypes.byref(dims), _ptr(q), _ptr(pool), pool.shape[0], _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), B, Lq, _ptr(o_lat), _ptr(lse), _ptr(workspace),
         workspace.numel(), _stream(stream)))
+
+
+def mla_prefill_expanded_workspace_size(dims: MlaDims, B: int, max_len: int) -> int:
+    return int(lib().mla_prefill_expanded_workspace_size(ctypes.byref(dims), int(B), int(max_len)))
+
+
+def mla_prefill_expanded(dims: MlaDims, q_nope, q_pe, pos, pool, block_table, seq_lens, Lq: int, max_len: int,
+                         w_uk, w_uv, o, lse=None, workspace=None, stream=None):
+    """Expanded-form attention of ``Lq`` query tokens per sequence: o [B*Lq, H, 128]
+    straight from q_nope, q_pe (not rotated) and pos, through per-head keys and
+    values expanded from the cache (``max_len`` bounds every length)."""
+    H = dims.num_heads
+    B = seq_lens.shape[0]
+    N = B * Lq
+    _check("q_nope", q_nope, torch.bfloat16, (N, H, D_NOPE))
+    _check("q_pe", q_pe, torch.bfloat16, (N, H, D_ROPE))
+    _check("pos", pos, torch.int32, (N,))
+    _check("pool", pool, torch.bfloat16)
+    _check("block_table", block_table, torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _check("seq_lens", seq_lens, torch.int32, (B,))
+    _check("w_uk", w_uk, torch.bfloat16, (H, D_NOPE, D_C))
+    _check("w_uv", w_uv, torch.bfloat16, (H, D_V, D_C))
+    _check("o", o, torch.bfloat16, (N, H, D_V))
+    if lse is not None:
+        _check("lse", lse, torch.float32, (N, H))
+    if workspace is None:
+        raise ValueError("workspace is required (mla_prefill_expanded_workspace_size bytes, uint8)")
+    _check("workspace", workspace, torch.uint8)
+    _ok("mla_prefill_expanded", lib().mla_prefill_expanded(
+        ctypes.byref(dims), _ptr(q_nope), _ptr(q_pe), _ptr(pos), _ptr(pool), pool.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), B, Lq, int(max_len), _ptr(w_uk), _ptr(w_uv), _ptr(o), _ptr(lse),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def mla_decode_attn_noalloc(dims: MlaDims, q, pool, block_table, seq_lens, Lq: int, o_lat, lse=None, stream=None):

@@ -187,6 +187,40 @@ hipError_t launch_cache_append_fp8(const uint16_t* c_kv, const uint16_t* k_pe, c
   return hipSuccess;
 }
 
+hipError_t launch_prefill_expanded(const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                                   const uint16_t* pool, int64_t num_blocks, const int32_t* block_table,
+                                   int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H,
+                                   int32_t max_len, const uint16_t* w_uk, const uint16_t* w_uv, float, double,
+                                   uint16_t* o, float* lse, void* workspace, hipStream_t) {
+  const size_t N = (size_t)B * Lq;
+  touch_read(q_nope, N * H * D_NOPE);
+  touch_read(q_pe, N * H * D_ROPE);
+  touch_read(pos, N);
+  touch_read(seq_lens, (size_t)B);
+  touch_read(w_uk, (size_t)H * D_NOPE * D_C);
+  touch_read(w_uv, (size_t)H * D_V * D_C);
+  const ExpandedLayout w = expanded_layout(B, H, max_len);
+  for (int32_t b = 0; b < B; ++b) {   // the gather reads the rows of keys below min(L, max_len)
+    const int32_t L = seq_lens[b] < max_len ? seq_lens[b] : max_len;
+    const int32_t nt = L > 0 ? (L + BLOCK - 1) / BLOCK : 0;
+    const int32_t nk = nt < max_blocks ? nt : max_blocks;
+    touch_read(block_table + (size_t)b * max_blocks, (size_t)nk);
+    for (int32_t k = 0; k < nk; ++k) {
+      const int32_t blk = block_table[(size_t)b * max_blocks + k];
+      if (blk >= 0 && blk < num_blocks) touch_read(pool + (size_t)blk * BLOCK * D_K, (size_t)BLOCK * D_K);
+    }
+  }
+  char* ws = (char*)workspace;
+  const size_t rows = (size_t)B * w.Lpad;
+  touch_write((uint16_t*)(ws + w.c_off), rows * D_C);
+  touch_write((uint16_t*)(ws + w.kr_off), rows * D_ROPE);
+  touch_write((uint16_t*)(ws + w.k_off), rows * H * D_NOPE);
+  touch_write((uint16_t*)(ws + w.vt_off), rows * H * D_NOPE);
+  touch_write(o, N * H * D_V);
+  if (lse) touch_write(lse, N * H);
+  return hipSuccess;
+}
+
 hipError_t launch_decode_attn_fp8(const uint16_t* q, const uint8_t* pool8, const float* pool_scale,
                                   int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
                                   const int32_t* seq_lens, int32_t B, int32_t Lq, int32_t H, float, uint16_t* o_lat,
