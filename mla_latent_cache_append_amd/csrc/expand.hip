@@ -12,9 +12,10 @@
 //      accumulation, one rounding to bf16): K = c W_UK^T as [t][h 128 + j],
 //      and V^T = W_UV c^T as [h 128 + j][t] (the layout the kernel's PV
 //      product reads as its A operand).
-//   3. mha_prefill_kernel: causal attention per (sequence, head, 128 query
-//      rows): 32-key tiles of K (with k_r) and V^T through the LDS, scores in
-//      32x32x16 bf16 MFMAs, online softmax in fp32, O^T = V^T P^T.
+//   3. mha_prefill_kernel: causal attention per (sequence, head, 256 query
+//      rows, eight waves): 64-key tiles of K (with k_r) and V^T through the
+//      LDS, scores in 32x32x16 bf16 MFMAs, online softmax in fp32,
+//      O^T = V^T P^T.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
@@ -28,15 +29,20 @@ namespace mla {
 
 namespace {
 
-constexpr int XT = 32;                         // keys per tile
-constexpr int XQ = 128;                        // query rows per workgroup, 32 per wave
+constexpr int XW = 8;                          // waves per workgroup
+constexpr int XTHREADS = 64 * XW;              // 512
+constexpr int XT = 64;                         // keys per tile (two 32-key blocks)
+constexpr int XQ = 32 * XW;                    // query rows per workgroup, 32 per wave
 constexpr int XQK = D_NOPE + D_ROPE;           // 192: key / query width
 constexpr int K_STRIDE = 400;                  // LDS bytes per key row: 384, padded to 25 x 16
-constexpr int VT_STRIDE = 72;                  // LDS bytes per value column: 64, padded to 9 x 8
-constexpr int K_TILE = XT * K_STRIDE;          // 12,800
-constexpr int VT_TILE = D_V * VT_STRIDE;       // 9,216
-constexpr int X_STAGE = K_TILE + VT_TILE;      // 22,016
+constexpr int VT_STRIDE = 136;                 // LDS bytes per value column: 128, padded to 17 x 8
+constexpr int K_TILE = XT * K_STRIDE;          // 25,600
+constexpr int VT_TILE = D_V * VT_STRIDE;       // 17,408
+constexpr int X_STAGE = K_TILE + VT_TILE;      // 43,008
 constexpr int K_CHUNKS = XQK / 8;              // 24 sixteen-byte chunks per key row
+constexpr int K_LOADS = XT * K_CHUNKS / XTHREADS;       // 3 per thread
+constexpr int V_LOADS = D_V * (XT / 8) / XTHREADS;      // 2 per thread
+static_assert(K_LOADS * XTHREADS == XT * K_CHUNKS && V_LOADS * XTHREADS == D_V * (XT / 8), "tile loads");
 constexpr float LN2F = 0.69314718055994530942f;
 
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
@@ -91,21 +97,26 @@ struct MhaArgs {
   RopeFreqs fr;
 };
 
-// Workgroup (query block qb, head h, sequence b); wave w holds query rows
-// 128 qb + 32 w + (l % 32); query row i sits at position L - Lq + i and sees
-// keys t <= it. MFMA layouts of v_mfma_f32_32x32x16_bf16 for lane l:
+// Workgroup (query block qb, head h; sequence b = blockIdx.y); wave w holds
+// query rows 256 qb + 32 w + (l % 32); query row i sits at position
+// L - Lq + i and sees keys t <= that position. Workgroup ids are dealt to the
+// 8 XCDs round-robin; x is remapped so that the query blocks of one head,
+// which read the same keys and values, run on one XCD and share its L2. MFMA layouts of
+// v_mfma_f32_32x32x16_bf16 for lane l:
 //   A (32x16): a[j] = A[l % 32][8 (l / 32) + j]
 //   B (16x32): b[j] = B[8 (l / 32) + j][l % 32]
 //   D (32x32): d[i] = D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]
-// Scores S^T = K Q^T: A = 32 keys x 16 features of K, B = Q^T, so score
-// value v of lane l is key 8 (v / 4) + 4 (l / 32) + v % 4 of the tile for
-// row l % 32; values 8 kk .. 8 kk + 7 are the B operand of O^T += V^T P^T
-// for key block kk with k-slot 8 (l / 32) + j <-> key 16 kk + 8 (j / 4) +
-// 4 (l / 32) + j % 4, and V^T is read in that key order (two runs of four
-// keys, 8 bytes each).
-__global__ __launch_bounds__(256, 2) void mha_prefill_kernel(MhaArgs a) {
+// Scores S^T = K Q^T per 32-key block kb: A = 32 keys x 16 features of K,
+// B = Q^T, so score value v of block kb is key 32 kb + 8 (v / 4) + 4 (l / 32)
+// + v % 4 of the tile for row l % 32; values 8 m .. 8 m + 7 of block kb are
+// the B operand of O^T += V^T P^T for key slice kk = 2 kb + m with k-slot
+// 8 (l / 32) + j <-> key 16 kk + 8 (j / 4) + 4 (l / 32) + j % 4, and V^T is
+// read in that key order (two runs of four keys, 8 bytes each).
+__global__ __launch_bounds__(XTHREADS, 1) void mha_prefill_kernel(MhaArgs a, int32_t nqb) {
   __shared__ __attribute__((aligned(16))) char smem[2 * X_STAGE];
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int unit = blockIdx.x;
+  if ((gridDim.x & 7) == 0) unit = (unit & 7) * (int)(gridDim.x >> 3) + (unit >> 3);
+  const int qb = unit % nqb, h = unit / nqb, b = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r32 = lane & 31, hf = lane >> 5;
   const int HD = a.H * D_NOPE;
@@ -142,18 +153,18 @@ __global__ __launch_bounds__(256, 2) void mha_prefill_kernel(MhaArgs a) {
     }
   }
 
-  // tile j's keys 32 j .. +31 in registers: three 16-byte chunks of the key
-  // rows (24 per row: 16 content, 8 rope) and two of the value columns (4 per
-  // column, eight keys each) per thread; keys at or past Lc read as zeros
+  // tile j's keys 64 j .. +63 in registers: 16-byte chunks of the key rows
+  // (24 per row: 16 content, 8 rope) and of the value columns (8 per column,
+  // eight keys each); keys at or past Lc read as zeros
   struct Stage {
-    u32x4 k[3];
-    u32x4 v[2];
+    u32x4 k[K_LOADS];
+    u32x4 v[V_LOADS];
   };
   auto load = [&](int j, Stage& st) {
     const int t0 = j * XT;
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int c = tid + 256 * u, tt = c / K_CHUNKS, ch = c - tt * K_CHUNKS, t = t0 + tt;
+    for (int u = 0; u < K_LOADS; ++u) {
+      const int c = tid + XTHREADS * u, tt = c / K_CHUNKS, ch = c - tt * K_CHUNKS, t = t0 + tt;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (t < Lc)
         v = ch < D_NOPE / 8 ? *(const u32x4*)(a.k + ((int64_t)b * a.Lpad + t) * HD + h * D_NOPE + 8 * ch)
@@ -161,8 +172,8 @@ __global__ __launch_bounds__(256, 2) void mha_prefill_kernel(MhaArgs a) {
       st.k[u] = v;
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + 256 * u, col = c >> 2, t = t0 + 8 * (c & 3);
+    for (int u = 0; u < V_LOADS; ++u) {
+      const int c = tid + XTHREADS * u, col = c / (XT / 8), t = t0 + 8 * (c % (XT / 8));
       u32x4 v = {0u, 0u, 0u, 0u};
       if (t < Lc) {
         v = *(const u32x4*)(a.vt + ((int64_t)b * HD + h * D_NOPE + col) * a.Lpad + t);
@@ -178,13 +189,13 @@ __global__ __launch_bounds__(256, 2) void mha_prefill_kernel(MhaArgs a) {
   auto store = [&](int s, const Stage& st) {
     lds_char* base = (lds_char*)smem + s * X_STAGE;
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int c = tid + 256 * u, tt = c / K_CHUNKS, ch = c - tt * K_CHUNKS;
+    for (int u = 0; u < K_LOADS; ++u) {
+      const int c = tid + XTHREADS * u, tt = c / K_CHUNKS, ch = c - tt * K_CHUNKS;
       *(__attribute__((address_space(3))) u32x4*)(base + tt * K_STRIDE + 16 * ch) = st.k[u];
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + 256 * u, col = c >> 2, qq = c & 3;
+    for (int u = 0; u < V_LOADS; ++u) {
+      const int c = tid + XTHREADS * u, col = c / (XT / 8), qq = c % (XT / 8);
       lds_char* p = base + K_TILE + col * VT_STRIDE + 16 * qq;
       *(__attribute__((address_space(3))) u32x2*)p = u32x2{st.v[u][0], st.v[u][1]};
       *(__attribute__((address_space(3))) u32x2*)(p + 8) = u32x2{st.v[u][2], st.v[u][3]};
@@ -210,38 +221,46 @@ __global__ __launch_bounds__(256, 2) void mha_prefill_kernel(MhaArgs a) {
     if (more) load(j + 1, nx);
     const lds_char* kst = (const lds_char*)smem + (j & 1) * X_STAGE;
     const lds_char* vst = kst + K_TILE;
-    f32x16 S;
+    f32x16 S[2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) S[v] = 0.f;
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int ks = 0; ks < XQK / 16; ++ks) {
-      const u32x4 kf = *(const __attribute__((address_space(3))) u32x4*)(kst + r32 * K_STRIDE + 2 * (16 * ks + 8 * hf));
-      S = mfma32(as_bf16x8(kf), qf[ks], S);
+      for (int v = 0; v < 16; ++v) S[kb][v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < XQK / 16; ++ks) {
+        const u32x4 kf = *(const __attribute__((address_space(3))) u32x4*)(
+            kst + (32 * kb + r32) * K_STRIDE + 2 * (16 * ks + 8 * hf));
+        S[kb] = mfma32(as_bf16x8(kf), qf[ks], S[kb]);
+      }
     }
     // online softmax in log2 units; keys past the row's position or past Lc masked
     const int t0 = j * XT;
     const bool need_mask = __any(t0 + XT - 1 > prow) || t0 + XT > Lc;
     float mt = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float s = S[v] * a.scale_log2;
-      if (need_mask) {
-        const int tok = t0 + 8 * (v >> 2) + 4 * hf + (v & 3);
-        if (tok > prow || tok >= Lc) s = -INFINITY;
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float s = S[kb][v] * a.scale_log2;
+        if (need_mask) {
+          const int tok = t0 + 32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3);
+          if (tok > prow || tok >= Lc) s = -INFINITY;
+        }
+        S[kb][v] = s;
+        mt = fmaxf(mt, s);
       }
-      S[v] = s;
-      mt = fmaxf(mt, s);
-    }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
     const float mref = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = exp2f(m_run - mref);
     float ps = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      S[v] = exp2f(S[v] - mref);
-      ps += S[v];
-    }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        S[kb][v] = exp2f(S[kb][v] - mref);
+        ps += S[kb][v];
+      }
     l_run = l_run * alpha + ps;
     m_run = m_new;
     if (__any(alpha != 1.f)) {
@@ -250,18 +269,19 @@ __global__ __launch_bounds__(256, 2) void mha_prefill_kernel(MhaArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) O[cb][v] *= alpha;
     }
-    bf16x8 P[2];
+    bf16x8 P[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < 4; ++kk) {
       u32x4 w;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(S[8 * kk + 2 * jj], S[8 * kk + 2 * jj + 1]);
+      for (int jj = 0; jj < 4; ++jj)
+        w[jj] = pack_bf16x2(S[kk >> 1][8 * (kk & 1) + 2 * jj], S[kk >> 1][8 * (kk & 1) + 2 * jj + 1]);
       P[kk] = as_bf16x8(w);
     }
 #pragma unroll
     for (int cb = 0; cb < D_V / 32; ++cb)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < 4; ++kk) {
         const lds_char* vp = vst + (32 * cb + r32) * VT_STRIDE + 2 * (16 * kk + 4 * hf);
         const u32x2 lo = *(const __attribute__((address_space(3))) u32x2*)vp;
         const u32x2 hi = *(const __attribute__((address_space(3))) u32x2*)(vp + 16);
@@ -404,8 +424,8 @@ hipError_t launch_prefill_expanded(const uint16_t* q_nope, const uint16_t* q_pe,
   a.max_len = max_len;
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
   a.fr = rope_freqs(rope_base);
-  const dim3 grid((unsigned)((Lq + XQ - 1) / XQ), (unsigned)H, (unsigned)B);
-  hipLaunchKernelGGL(mha_prefill_kernel, grid, dim3(256), 0, stream, a);
+  const int32_t nqb = (Lq + XQ - 1) / XQ;
+  hipLaunchKernelGGL(mha_prefill_kernel, dim3((unsigned)(nqb * H), (unsigned)B), dim3(XTHREADS), 0, stream, a, nqb);
   return hipGetLastError();
 }
 
