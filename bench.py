@@ -58,6 +58,8 @@ def parse():
                     help="instead of the decode step: time a causal prefill chunk of Lq tokens per sequence "
                          "(B=4, 128 heads, 16,384 cached tokens) in the absorbed form (absorb_q + attention + "
                          "out_up) and in the expanded form (mla_prefill_expanded) for several Lq, one JSON line")
+    ap.add_argument("--cross-lq", type=int, nargs="+", default=[32, 64, 128, 256, 512, 1024, 2048],
+                    help="chunk sizes (query tokens per sequence) that --crossover times")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="parse two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this bench "
                          "with --copy-calib into profiles/traffic_<cache>_<workload>.json, then exit")
@@ -297,7 +299,10 @@ def crossover(args) -> None:
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     B, H, HIST = 4, 128, 16384
-    lqs = (32, 64, 128, 256, 512, 1024, 2048)
+    lqs = tuple(sorted(set(args.cross_lq)))
+    if not lqs or lqs[0] < 1 or lqs[-1] > 65536:
+        print("--cross-lq takes chunk sizes from 1 to 65536", file=sys.stderr)
+        sys.exit(2)
     lmax = HIST + max(lqs)
     dev = torch.device("cuda")
     w = workloads.Workload("crossover_b4_h128", B, H, max(lqs), [lmax] * B, "permuted", args.seed)

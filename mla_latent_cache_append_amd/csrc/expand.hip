@@ -39,10 +39,8 @@ constexpr int VT_STRIDE = 136;                 // LDS bytes per value column: 12
 constexpr int K_TILE = XT * K_STRIDE;          // 25,600
 constexpr int VT_TILE = D_V * VT_STRIDE;       // 17,408
 constexpr int X_STAGE = K_TILE + VT_TILE;      // 43,008
-constexpr int K_CHUNKS = XQK / 8;              // 24 sixteen-byte chunks per key row
-constexpr int K_LOADS = XT * K_CHUNKS / XTHREADS;       // 3 per thread
-constexpr int V_LOADS = D_V * (XT / 8) / XTHREADS;      // 2 per thread
-static_assert(K_LOADS * XTHREADS == XT * K_CHUNKS && V_LOADS * XTHREADS == D_V * (XT / 8), "tile loads");
+static_assert(2 * XTHREADS == XT * (D_NOPE / 8) && XTHREADS == XT * (D_ROPE / 8) &&
+              2 * XTHREADS == D_V * (XT / 8), "tile loads: two content, one rope, two value chunks per thread");
 constexpr float LN2F = 0.69314718055994530942f;
 
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
@@ -153,49 +151,68 @@ __global__ __launch_bounds__(XTHREADS, 1) void mha_prefill_kernel(MhaArgs a, int
     }
   }
 
-  // tile j's keys 64 j .. +63 in registers: 16-byte chunks of the key rows
-  // (24 per row: 16 content, 8 rope) and of the value columns (8 per column,
-  // eight keys each); keys at or past Lc read as zeros
+  // tile j's keys 64 j .. +63 in registers, 16-byte chunks: two content
+  // chunks (key c / 16, chunk c % 16 for c = tid, tid + 512), one rope chunk
+  // (key tid / 8, chunk tid % 8) and two value chunks (column c / 8, keys
+  // 8 (c % 8) .. +7); per-thread byte offsets are fixed, the tile moves a
+  // wave-uniform base. Keys at or past Lc (tail tile only) read as zeros.
   struct Stage {
-    u32x4 k[K_LOADS];
-    u32x4 v[V_LOADS];
+    u32x4 kc[2];
+    u32x4 kr;
+    u32x4 v[2];
   };
+  const char* kbase = (const char*)(a.k + (int64_t)b * a.Lpad * HD + h * D_NOPE);
+  const char* rbase = (const char*)(a.kr + (int64_t)b * a.Lpad * D_ROPE);
+  const char* vbase = (const char*)(a.vt + ((int64_t)b * HD + h * D_NOPE) * a.Lpad);
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t c = tid + XTHREADS * u;
+    koff[u] = (c / 16) * (uint32_t)HD * 2u + (c % 16) * 16u;
+    voff[u] = (c / 8) * (uint32_t)a.Lpad * 2u + (c % 8) * 16u;
+  }
+  const uint32_t roff = (tid / 8) * (uint32_t)D_ROPE * 2u + (tid % 8) * 16u;
   auto load = [&](int j, Stage& st) {
     const int t0 = j * XT;
+    const char* kb = kbase + (int64_t)t0 * HD * 2;
+    const char* rb = rbase + (int64_t)t0 * D_ROPE * 2;
+    const char* vb = vbase + (int64_t)t0 * 2;
+    if (t0 + XT <= Lc) {
 #pragma unroll
-    for (int u = 0; u < K_LOADS; ++u) {
-      const int c = tid + XTHREADS * u, tt = c / K_CHUNKS, ch = c - tt * K_CHUNKS, t = t0 + tt;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (t < Lc)
-        v = ch < D_NOPE / 8 ? *(const u32x4*)(a.k + ((int64_t)b * a.Lpad + t) * HD + h * D_NOPE + 8 * ch)
-                            : *(const u32x4*)(a.kr + ((int64_t)b * a.Lpad + t) * D_ROPE + 8 * (ch - D_NOPE / 8));
-      st.k[u] = v;
-    }
+      for (int u = 0; u < 2; ++u) st.kc[u] = *(const u32x4*)(kb + koff[u]);
+      st.kr = *(const u32x4*)(rb + roff);
 #pragma unroll
-    for (int u = 0; u < V_LOADS; ++u) {
-      const int c = tid + XTHREADS * u, col = c / (XT / 8), t = t0 + 8 * (c % (XT / 8));
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (t < Lc) {
-        v = *(const u32x4*)(a.vt + ((int64_t)b * HD + h * D_NOPE + col) * a.Lpad + t);
+      for (int u = 0; u < 2; ++u) st.v[u] = *(const u32x4*)(vb + voff[u]);
+    } else {
+      const int n = Lc - t0;   // keys of this tile present, 0 < n < 64
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) st.kc[u] = (int)((tid + XTHREADS * u) / 16) < n ? *(const u32x4*)(kb + koff[u]) : z;
+      st.kr = (int)(tid / 8) < n ? *(const u32x4*)(rb + roff) : z;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = 8 * (int)((tid + XTHREADS * u) % 8);
+        u32x4 v = t < n ? *(const u32x4*)(vb + voff[u]) : z;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {   // keys t + 2e, t + 2e + 1
-          if (t + 2 * e >= Lc) v[e] = 0u;
-          else if (t + 2 * e + 1 >= Lc) v[e] &= 0xffffu;
+          if (t + 2 * e >= n) v[e] = 0u;
+          else if (t + 2 * e + 1 >= n) v[e] &= 0xffffu;
         }
+        st.v[u] = v;
       }
-      st.v[u] = v;
     }
   };
   auto store = [&](int s, const Stage& st) {
     lds_char* base = (lds_char*)smem + s * X_STAGE;
 #pragma unroll
-    for (int u = 0; u < K_LOADS; ++u) {
-      const int c = tid + XTHREADS * u, tt = c / K_CHUNKS, ch = c - tt * K_CHUNKS;
-      *(__attribute__((address_space(3))) u32x4*)(base + tt * K_STRIDE + 16 * ch) = st.k[u];
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + XTHREADS * u;
+      *(__attribute__((address_space(3))) u32x4*)(base + (c / 16) * K_STRIDE + 16 * (c % 16)) = st.kc[u];
     }
+    *(__attribute__((address_space(3))) u32x4*)(base + (tid / 8) * K_STRIDE + 2 * D_NOPE + 16 * (tid % 8)) = st.kr;
 #pragma unroll
-    for (int u = 0; u < V_LOADS; ++u) {
-      const int c = tid + XTHREADS * u, col = c / (XT / 8), qq = c % (XT / 8);
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + XTHREADS * u, col = c / 8, qq = c % 8;
       lds_char* p = base + K_TILE + col * VT_STRIDE + 16 * qq;
       *(__attribute__((address_space(3))) u32x2*)p = u32x2{st.v[u][0], st.v[u][1]};
       *(__attribute__((address_space(3))) u32x2*)(p + 8) = u32x2{st.v[u][2], st.v[u][3]};
@@ -233,32 +250,34 @@ __global__ __launch_bounds__(XTHREADS, 1) void mha_prefill_kernel(MhaArgs a, int
         S[kb] = mfma32(as_bf16x8(kf), qf[ks], S[kb]);
       }
     }
-    // online softmax in log2 units; keys past the row's position or past Lc masked
+    // online softmax in log2 units: the max is taken over the raw scores
+    // (the scale is positive), exponentials as exp2(s * scale - m); keys past
+    // the row's position or past Lc masked
     const int t0 = j * XT;
-    const bool need_mask = __any(t0 + XT - 1 > prow) || t0 + XT > Lc;
+    if (__any(t0 + XT - 1 > prow) || t0 + XT > Lc) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int tok = t0 + 32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3);
+          if (tok > prow || tok >= Lc) S[kb][v] = -INFINITY;
+        }
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float s = S[kb][v] * a.scale_log2;
-        if (need_mask) {
-          const int tok = t0 + 32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3);
-          if (tok > prow || tok >= Lc) s = -INFINITY;
-        }
-        S[kb][v] = s;
-        mt = fmaxf(mt, s);
-      }
+      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, S[kb][v]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
+    const float m_new = fmaxf(m_run, mt * a.scale_log2);
     const float mref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - mref);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mref);   // 0 while m_run = -inf
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        S[kb][v] = exp2f(S[kb][v] - mref);
+        S[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][v], a.scale_log2, -mref));
         ps += S[kb][v];
       }
     l_run = l_run * alpha + ps;
