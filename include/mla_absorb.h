@@ -281,7 +281,9 @@ int mla_decode_attn_fp8(const mla_dims* dims, const uint16_t* q, const uint8_t* 
  *   (hipBLASLt; fp32 accumulation, one rounding of k_c and v to bf16), and a
  *   causal attention kernel forms the scores in bf16 MFMAs, the softmax in
  *   fp32 and o in one rounding to bf16. The expansion runs over max_len rows
- *   for every sequence.
+ *   (rounded up to 32) for every sequence. The first call on a device creates
+ *   that device's hipBLASLt handle, kept until the process ends; the GEMMs
+ *   are given no hipBLASLt workspace.
  *   q_nope [B*Lq][H][128] bf16, q_pe [B*Lq][H][64] bf16 (not rotated),
  *   pos [B*Lq] int32: the queries, as for mla_absorb_q (token n = b*Lq + i).
  *   pool, num_blocks, block_table, max_blocks_per_seq, seq_lens, B, Lq: as
