@@ -1039,6 +1039,7 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float f) {
   asm volatile("" : "+a"(acc));
 }
 
+template <bool PE>
 __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[OSTAGE * HT_BYTES];
   lds_char* stages = (lds_char*)smem;
@@ -1080,8 +1081,16 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     const int e = 2 * (q & 1) + ((i16 & 3) >> 1);
     vbase = ht_off(tl, e) + 8 * (i16 & 1);
   }
-  const uint32_t goff = (uint32_t)((lane >> 3) * ROW_BYTES + ((lane & 7) ^ swz2(8 * wave + (lane >> 3))) * 16);
-  const uint32_t so = (uint32_t)uni(wave * 8 * ROW_BYTES);   // buffer offset of this wave's 8 tokens
+  // Copy operands of a line: lane l reads token l / 8 of the wave's 8, at the
+  // swizzled 16-byte chunk the LDS slot expects; the pool's rows are 1,152
+  // bytes, the two-buffer cache's latent rows 1,024 (columns 0..1,023 as in
+  // the pool) and its rope rows 128, in their own array (PE)
+  constexpr int KV_ROW = PE ? D_C * 2 : ROW_BYTES;
+  const uint32_t gchunk = (uint32_t)(((lane & 7) ^ swz2(8 * wave + (lane >> 3))) * 16);
+  const uint32_t goff = (uint32_t)((lane >> 3) * KV_ROW) + gchunk;
+  const uint32_t so = (uint32_t)uni(wave * 8 * KV_ROW);   // buffer offset of this wave's 8 tokens
+  const uint32_t gpoff = (uint32_t)((lane >> 3) * (D_ROPE * 2)) + gchunk;   // rope rows (PE)
+  const uint32_t sp = (uint32_t)uni(wave * 8 * (D_ROPE * 2));
   // the pool base as descriptor words, and its size as a 32-bit bound
   const uint32_t pool_lo = (uint32_t)uni((int)(uint32_t)(uintptr_t)a.pool);
   const uint32_t pool_hi = (uint32_t)uni((int)((uint32_t)((uintptr_t)a.pool >> 32) & 0xffffu));
@@ -1098,6 +1107,12 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     bool bad = L > a.max_keys;
     const int key_end = min(k_last * BLOCK, L);
     const int e0 = 2 * k_first, e1 = (key_end + HT_TOK - 1) / HT_TOK;
+    // two-buffer cache: the sequence's rows, and the keys that exist in them
+    const int Lc = uni(min(L, a.max_keys));
+    const uint16_t* kv_seq = PE ? (const uint16_t*)uni64((int64_t)(uintptr_t)(a.pool + (int64_t)b * a.max_keys * D_C))
+                                : nullptr;
+    const uint16_t* pe_seq = PE ? (const uint16_t*)uni64((int64_t)(uintptr_t)(a.pe + (int64_t)b * a.max_keys * D_ROPE))
+                                : nullptr;
 
     const int lim = r < a.rows ? L - a.Lq + r / a.H : -1;   // last key row r sees
     float m_run = -INFINITY, l_run = 0.f;
@@ -1108,16 +1123,30 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     // half tile copied at the end of an iteration is requested right after
     // its barrier, so the load is long complete when it is used.
     const __attribute__((address_space(4))) int32_t* bt =
-        (const __attribute__((address_space(4))) int32_t*)(a.block_table + (int64_t)b * a.max_blocks);
-    auto blk_of = [&](int e) { return (e >> 1) < ntiles ? bt[e >> 1] : -1; };
+        (const __attribute__((address_space(4))) int32_t*)(PE ? nullptr : a.block_table + (int64_t)b * a.max_blocks);
+    auto blk_of = [&](int e) { return PE ? 0 : (e >> 1) < ntiles ? bt[e >> 1] : -1; };
     // Copy of half tile e (cache block blk) into its stage: descriptor rs and
     // this wave's LDS base mb (wave w copies tokens 8 w .. 8 w + 7, nine
     // 1-KiB lines). Past the segment's last half tile the descriptor covers
     // zero bytes, so the copy only writes zeros into a stage that is not read
     // again; every iteration then has exactly nine copies per wave in flight.
-    auto prep = [&](int e, int blk, sgpr_x4& rs, uint32_t& mb) {
+    // Two-buffer cache: the latent lines come through rs, the rope line
+    // through rp, both at half tile e of the sequence's rows.
+    auto prep = [&](int e, int blk, sgpr_x4& rs, sgpr_x4& rp, uint32_t& mb) {
       mb = lds_addr(stages + (e % OSTAGE) * HT_BYTES + wave * 9 * 1024);
+      if constexpr (PE) {
+        const int nv = e < e1 ? max(0, min(HT_TOK, Lc - e * HT_TOK)) : 0;
+        rs = buffer_rsrc(kv_seq + (int64_t)e * HT_TOK * D_C, nv * (D_C * 2));
+        rp = buffer_rsrc(pe_seq + (int64_t)e * HT_TOK * D_ROPE, nv * (D_ROPE * 2));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {   // uniform: keep them in SGPRs
+          rs[k] = (uint32_t)uni((int)rs[k]);
+          rp[k] = (uint32_t)uni((int)rp[k]);
+        }
+        return;
+      }
       rs = buffer_rsrc(a.pool, 0);
+      rp = rs;
       if (e >= e1) return;
       if (blk < 0 || blk >= a.num_blocks) {
         bad = true;
@@ -1168,16 +1197,24 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) qr[k] = (uint32_t)uni((int)qr[k]);   // uniform: keep it in SGPRs
       const uint32_t qv = (uint32_t)((32 * wave + c32) * ROW_BYTES + 16 * h);
-      sgpr_x4 rs0, rs1, rs2;
+      sgpr_x4 rs0, rs1, rs2, rp0, rp1, rp2;
       uint32_t mb0, mb1, mb2;
-      prep(e0, blk_of(e0), rs0, mb0);
-      prep(e0 + 1, blk_of(e0 + 1), rs1, mb1);
-      prep(e0 + 2, blk_of(e0 + 2), rs2, mb2);
-      asm volatile(OWN_ASM_QLOAD
-                   : OWN_OPS_Q_OUT
-                   : [qv] "v"(qv), [qr] "s"(qr), [mb0] "s"(mb0), [rs0] "s"(rs0), [mb1] "s"(mb1), [rs1] "s"(rs1),
-                     [mb2] "s"(mb2), [rs2] "s"(rs2), [go] "v"(goff), OWN_OPS_SO
-                   : "m0", "scc", "memory");
+      prep(e0, blk_of(e0), rs0, rp0, mb0);
+      prep(e0 + 1, blk_of(e0 + 1), rs1, rp1, mb1);
+      prep(e0 + 2, blk_of(e0 + 2), rs2, rp2, mb2);
+      if constexpr (PE)
+        asm volatile(OWNP_ASM_QLOAD
+                     : OWN_OPS_Q_OUT
+                     : [qv] "v"(qv), [qr] "s"(qr), [mb0] "s"(mb0), [rs0] "s"(rs0), [mb1] "s"(mb1), [rs1] "s"(rs1),
+                       [mb2] "s"(mb2), [rs2] "s"(rs2), [rp0] "s"(rp0), [rp1] "s"(rp1), [rp2] "s"(rp2),
+                       [go] "v"(goff), OWN_OPS_SO, OWNP_OPS_SP
+                     : "m0", "scc", "memory");
+      else
+        asm volatile(OWN_ASM_QLOAD
+                     : OWN_OPS_Q_OUT
+                     : [qv] "v"(qv), [qr] "s"(qr), [mb0] "s"(mb0), [rs0] "s"(rs0), [mb1] "s"(mb1), [rs1] "s"(rs1),
+                       [mb2] "s"(mb2), [rs2] "s"(rs2), [go] "v"(goff), OWN_OPS_SO
+                     : "m0", "scc", "memory");
     }
     lds_barrier();                         // every wave's copies of e0 are in the LDS
     k_addr(e0);
@@ -1205,13 +1242,18 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
     // the segment sets badacc.
     static_assert(TILE_BYTES == 0x12000 && HT_BYTES == 0x9000 && ROW_BYTES == 0x480 && HT_TOK == 32 &&
                       OSTAGE == 4, "constants of the descriptor sequence");
-    sgpr_x4 rs;
+    sgpr_x4 rs, rp;
     uint32_t mb;
-    prep(e0 + OSTAGE - 1, blk_of(e0 + OSTAGE - 1), rs, mb);
+    prep(e0 + OSTAGE - 1, blk_of(e0 + OSTAGE - 1), rs, rp, mb);
     k_addr(e0 + 1 < e1 ? e0 + 1 : e0);
     v_addr(e0);
     const uint32_t mb0 = (uint32_t)uni((int)lds_addr(stages + wave * 9 * 1024));
     const int64_t bt_u = uni64((int64_t)(uintptr_t)bt);   // the sequence's block-table row, in SGPRs
+    // two-buffer cache: the sequence's latent and rope rows, as descriptor words
+    const uint32_t kv_lo = (uint32_t)uni((int)(uint32_t)(uintptr_t)kv_seq);
+    const uint32_t kv_hi = (uint32_t)uni((int)((uint32_t)((uintptr_t)kv_seq >> 32) & 0xffffu));
+    const uint32_t pe_lo = (uint32_t)uni((int)(uint32_t)(uintptr_t)pe_seq);
+    const uint32_t pe_hi = (uint32_t)uni((int)((uint32_t)((uintptr_t)pe_seq >> 32) & 0xffffu));
     const int nt1 = uni(ntiles - 1);
     mb = (uint32_t)uni((int)mb);
     uint32_t badacc = 0;
@@ -1228,7 +1270,15 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
       // read done, so the barrier needs no lgkmcnt wait.
       asm volatile("s_barrier" ::: "memory");
       int t0, t1, t2;
-      uint32_t r0, r1, r2, r3, blkv;
+      uint32_t r0, r1, r2, r3, r4, r5, r6, r7, blkv;
+#define OWNP_ITER(NAME, OPS_O)                                                                        \
+  asm volatile(NAME                                                                                   \
+               : OPS_O, OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "+v"(alpha),       \
+                 [mref] "+v"(mref), [lr] "+v"(lr), OWN_OPS_KA_IO, OWN_OPS_VA_IO, OWN_OPS_BOOK_OUT,    \
+                 OWNP_OPS_PREP_OUT                                                                    \
+               : OWN_OPS_Q, [scale] "s"(a.scale_log2), [rs] "s"(rs), [rp] "s"(rp), [go] "v"(goff),    \
+                 OWN_OPS_SO, OWNP_OPS_SP, OWN_OPS_BOOK_IN, OWNP_OPS_PREP_IN                           \
+               : OWN_CLOB, "vcc", "m0", "scc", "memory")
 #define OWN_ITER(NAME, OPS_O)                                                                         \
   asm volatile(NAME                                                                                   \
                : OPS_O, OWN_OPS_S, [mrun] "+v"(m_run), [lrun] "+v"(l_run), [alpha] "+v"(alpha),       \
@@ -1237,11 +1287,20 @@ __global__ __launch_bounds__(256, 1) void attn_own_kernel(AttnArgs a) {
                : OWN_OPS_Q, [scale] "s"(a.scale_log2), [rs] "s"(rs), [go] "v"(goff), OWN_OPS_SO,      \
                  OWN_OPS_BOOK_IN, OWN_OPS_PREP_IN                                                     \
                : OWN_CLOB, "vcc", "m0", "scc", "memory")
-      if constexpr (FIRST)
-        OWN_ITER(OWN_ASM_IT_FIRST, OWN_OPS_O_OUT);
-      else
-        OWN_ITER(OWN_ASM_IT, OWN_OPS_O);
+      if constexpr (PE) {
+        if constexpr (FIRST)
+          OWNP_ITER(OWNP_ASM_IT_FIRST, OWN_OPS_O_OUT);
+        else
+          OWNP_ITER(OWNP_ASM_IT, OWN_OPS_O);
+        rp = sgpr_x4{(uint32_t)uni((int)r4), (uint32_t)uni((int)r5), (uint32_t)uni((int)r6), (uint32_t)uni((int)r7)};
+      } else {
+        if constexpr (FIRST)
+          OWN_ITER(OWN_ASM_IT_FIRST, OWN_OPS_O_OUT);
+        else
+          OWN_ITER(OWN_ASM_IT, OWN_OPS_O);
+      }
 #undef OWN_ITER
+#undef OWNP_ITER
       // the copies of half tile e+4, issued by the next sequence. The values
       // are in SGPRs, but an asm statement with vector outputs counts as
       // divergent to the compiler: readfirstlane marks them uniform, so that
@@ -1734,7 +1793,8 @@ static hipError_t launch_attention(const uint16_t* q, const void* pool, const ui
     else hipLaunchKernelGGL((attn_cols_kernel<2, true>), grid, dim3(256), 0, stream, a);
   } else switch (p.variant) {
     case V_ROWS128:
-      hipLaunchKernelGGL(attn_own_kernel, grid, dim3(256), 0, stream, a);
+      if (pe) hipLaunchKernelGGL(attn_own_kernel<true>, grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL(attn_own_kernel<false>, grid, dim3(256), 0, stream, a);
       break;
     case V_ROWS64:
       hipLaunchKernelGGL(attn_rows_kernel<1>, grid, dim3(256), 0, stream, a);

@@ -139,13 +139,27 @@ def vread(seq, j):
             "V%db" % j)
 
 
+# Two-buffer cache (PE = True below): the latent rows (1,024 bytes per token)
+# and the rope rows (128 bytes per token) sit in two arrays. Lines 0..7 of a
+# half tile read the latent array with the same instructions as the pool
+# (operands go / so / rs carry the 1,024-byte stride); line 8 reads the rope
+# array through its own offsets gp / sp and descriptor rp, at instruction
+# offset 0.
+PE = False
+
+
+def pe_line(cg):
+    return PE and cg == 8
+
+
 def dma_m0(seq, cg, mb="mb"):
     """M0 for line cg of this wave's share of a stage. A buffer -> LDS copy
     adds its instruction offset (cg * 128, see dma_load) to the LDS address
     as well as to the memory address, so M0 = line base - cg * 128 and the
-    line lands at mb + cg * 1024. The copy that reads M0 must not be the
-    next instruction (one wait state)."""
-    seq.op("s_add_u32 m0, %%[%s], 0x%x" % (mb, cg * (1024 - 128)))
+    line lands at mb + cg * 1024 (the rope line of the two-buffer cache has
+    offset 0). The copy that reads M0 must not be the next instruction (one
+    wait state)."""
+    seq.op("s_add_u32 m0, %%[%s], 0x%x" % (mb, cg * 1024 if pe_line(cg) else cg * (1024 - 128)))
 
 
 def dma_load(seq, cg, rs="rs"):
@@ -155,7 +169,10 @@ def dma_load(seq, cg, rs="rs"):
     copy is marked non-temporal (nt): it streams past the caches instead of
     displacing the split partials the merge reads right after (measured ~2 %
     faster per call, same results)."""
-    seq.op("buffer_load_dwordx4 %%[go], %%[%s], %%[so] offen offset:%d nt lds" % (rs, cg * 128))
+    if pe_line(cg):
+        seq.op("buffer_load_dwordx4 %%[gp], %%[%s], %%[sp] offen offset:0 nt lds" % rs.replace("rs", "rp"))
+    else:
+        seq.op("buffer_load_dwordx4 %%[go], %%[%s], %%[so] offen offset:%d nt lds" % (rs, cg * 128))
 
 
 def dma(seq, cg, mb="mb", rs="rs"):
@@ -298,6 +315,29 @@ def prep_groups():
     ]
 
 
+def prep_groups_pe():
+    """Two-buffer cache: descriptors of the copies of half tile ep = e + 4,
+    latent rows (r0..r3) at kv + ep * 32,768 and rope rows (r4..r7) at pe +
+    ep * 4,096 (the sequence's bases klo:khi and plo:phi, bits 47..32 in the
+    second word), bytes = 1,024 (128) * max(0, min(32, Lc - 32 ep)), or 0
+    past the segment (ep >= e1); LDS base mb as for the pool. Groups are
+    emitted whole (SCC chains)."""
+    return [
+        ["s_mul_i32 %[r0], %[ep], 0x8000", "s_mul_hi_u32 %[r1], %[ep], 0x8000"],
+        ["s_add_u32 %[r0], %[r0], %[klo]", "s_addc_u32 %[r1], %[r1], %[khi]"],
+        ["s_and_b32 %[r1], %[r1], 0xffff"],
+        ["s_mul_i32 %[r4], %[ep], 0x1000", "s_mul_hi_u32 %[r5], %[ep], 0x1000"],
+        ["s_add_u32 %[r4], %[r4], %[plo]", "s_addc_u32 %[r5], %[r5], %[phi]"],
+        ["s_and_b32 %[r5], %[r5], 0xffff"],
+        ["s_lshl_b32 %[r2], %[ep], 5", "s_sub_i32 %[r2], %[L], %[r2]"],
+        ["s_min_i32 %[r2], %[r2], 32", "s_max_i32 %[r2], %[r2], 0"],
+        ["s_cmp_lt_i32 %[ep], %[e1]", "s_cselect_b32 %[r2], %[r2], 0"],
+        ["s_lshl_b32 %[r6], %[r2], 7", "s_lshl_b32 %[r2], %[r2], 10"],
+        ["s_mov_b32 %[r3], 0x20000", "s_mov_b32 %[r7], 0x20000"],
+        ["s_and_b32 %[mb], %[ep], 3", "s_mul_i32 %[mb], %[mb], 0x9000", "s_add_u32 %[mb], %[mb], %[mb0]"],
+    ]
+
+
 def gen_qload():
     """Start of a segment: the copies of the first half tile, the 36 query
     fragments straight into registers (row 32 wave + l % 32 at byte offset
@@ -336,8 +376,9 @@ def gen_iter(mask, first):
     with PV MFMAs in flight: code after it that reads the accumulators waits
     first (GUARD)."""
     s = Seq()
-    for ins in blk_load():
-        s.op(ins)
+    if not PE:
+        for ins in blk_load():
+            s.op(ins)
     s.op("s_nop 1")
     for ks in range(PF_K):
         kread(s, ks)
@@ -371,7 +412,7 @@ def gen_iter(mask, first):
     # bookkeeping from PV step BOOK_FROM on, the V^T address update after the
     # last V^T read (issued at step 31 - PF_V), the rescale test at the end
     bper = (len(book) + (31 - PF_V - BOOK_FROM) - 1) // (31 - PF_V - BOOK_FROM)   # at least one per step
-    prep = prep_groups()
+    prep = prep_groups_pe() if PE else prep_groups()
     pper = (len(prep) + (32 - PREP_AT) - 1) // (32 - PREP_AT)
     for j in range(32):
         if j == PREP_AT:
@@ -691,6 +732,28 @@ def main():
         "OWN_CLOB": ", ".join('"v%d"' % r for r in range(CLOB_LO, 256)),
     }
     for name, text in ops.items():
+        body.append("#define %s %s" % (name, text))
+    body.append("")
+    # two-buffer cache: the same sequences with the rope line read from its
+    # own array and the descriptors formed from the half-tile index
+    global PE
+    PE = True
+    it_pe = ("s_sub_i32 %[t0], %[ep], 3\\n\\ts_cmp_lt_i32 %[t0], %[eo]\\n\\t"
+             "s_cbranch_scc1 ownp_open_%=\\n\\t" + gen_iter(True, False)
+             + "s_branch ownp_done_%=\\n\\townp_open_%=:\\n\\t" + gen_iter(False, False) + "ownp_done_%=:\\n\\t")
+    for name, text in [("OWNP_ASM_QLOAD", gen_qload()), ("OWNP_ASM_IT", it_pe),
+                       ("OWNP_ASM_IT_FIRST", gen_iter(True, True))]:
+        body.append('#define %s "%s"' % (name, text))
+        body.append("")
+    PE = False
+    ops_pe = {
+        "OWNP_OPS_PREP_OUT": ('[r0] "=&s"(r0), [r1] "=&s"(r1), [r2] "=&s"(r2), [r3] "=&s"(r3), '
+                              '[r4] "=&s"(r4), [r5] "=&s"(r5), [r6] "=&s"(r6), [r7] "=&s"(r7), [mb] "+s"(mb)'),
+        "OWNP_OPS_PREP_IN": ('[klo] "s"(kv_lo), [khi] "s"(kv_hi), [plo] "s"(pe_lo), [phi] "s"(pe_hi), '
+                             '[L] "s"(Lc), [mb0] "s"(mb0)'),
+        "OWNP_OPS_SP": '[gp] "v"(gpoff), [sp] "s"(sp)',
+    }
+    for name, text in ops_pe.items():
         body.append("#define %s %s" % (name, text))
     body.append("")
     # FP8 pool: the same sequences with shallower operand rings (their

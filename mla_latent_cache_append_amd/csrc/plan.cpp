@@ -35,19 +35,9 @@ AttnPlan plan_attention_fp8(int32_t B, int32_t Lq, int32_t H) {
   return p;
 }
 
-// Two-buffer layout (kv_cache + pe_cache): the column kernel up to 47 rows
-// per sequence, the 64-row kernel above (the 128-row kernel's copy sequences
-// are written for the paged pool's 1,152-byte rows).
-AttnPlan plan_attention_kvpe(int32_t B, int32_t Lq, int32_t H) {
-  AttnPlan p = plan_attention(B, Lq, H);
-  if (p.variant == V_ROWS128) {
-    p.variant = V_ROWS64;
-    p.rg_rows = 64;
-    p.n_rg = (Lq * H + 63) / 64;
-    p.width = (TARGET_WGS + p.n_rg - 1) / p.n_rg;
-  }
-  return p;
-}
+// Two-buffer layout (kv_cache + pe_cache): the same kernels as the paged
+// pool (the 128-row kernel reads the rope rows through a second descriptor).
+AttnPlan plan_attention_kvpe(int32_t B, int32_t Lq, int32_t H) { return plan_attention(B, Lq, H); }
 
 // Workspace: (m, l) of every partial in fp32, then the partials themselves
 // in bf16, normalized by their l, starting on a 256-byte boundary. Sized for

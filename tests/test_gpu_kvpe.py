@@ -144,7 +144,10 @@ def test_v2lite_4k_full_size_matches_oracle_and_paged_pool():
 
 
 @pytest.mark.parametrize("H,Lq,lens,max_seq", [
-    (128, 1, [1000, 3001], 3072),          # 128 heads: the 64-row kernel, two row groups
+    (128, 1, [1000, 3001], 3072),          # 128 heads: the 128-row kernel, rope rows through their own descriptor
+    (128, 2, [37, 100, 1, 64], 100),       # two 128-row groups, max_seq not a multiple of 64
+    (48, 2, [700, 1, 129], 700),           # 96 rows: the 128-row kernel with its last wave all padding
+    (32, 2, [300, 65], 320),               # 64 rows: the 64-row kernel
     (16, 3, [5, 64, 130, 200], 256),       # several new tokens, causal among themselves
     (32, 1, [1, 64, 65, 100], 100),        # max_seq not a multiple of 64, tails of 1..36
     (64, 2, [700, 1, 129], 700),
@@ -168,6 +171,35 @@ def test_length_beyond_max_seq_gives_nan_and_spares_the_others():
         hz.check_seq("kvpe bad-neighbour", w, out, b)
     assert np.all(np.isnan(orc.bf16_bits_to_f64(out["o_lat"][1])))
     assert np.all(np.isnan(out["lse"][1]))
+
+
+def test_length_beyond_max_seq_128_heads():
+    """The same through the 128-row kernel, with the long sequence last: its
+    length lies between max_seq and the next multiple of 64, so only the
+    clamp of the copies to max_seq keeps them inside the buffers."""
+    w = workloads.Workload("kvpe_bad128", 3, 128, 1, [90, 40, 128], "contiguous", seed=6)
+    _say("kvpe H=128 lens [90, 40, 128 (> max_seq 100)]")
+    out = KvpeRun(w, 100).step()
+    for b in (0, 1):
+        hz.check_seq("kvpe bad-last 128", w, out, b)
+    assert np.all(np.isnan(orc.bf16_bits_to_f64(out["o_lat"][2])))
+    assert np.all(np.isnan(out["lse"][2]))
+
+
+def test_v3_16k_full_size_matches_paged_pool():
+    """The 128-head 16k batch (B=32, L=16384) at full size: two sequences
+    against the oracle, every output bit for bit equal to the paged pool's
+    (the 128-row kernel over the same rows, read through two descriptors)."""
+    w = workloads.make("v3_b32_h128_l16384", seed=0)
+    _say("kvpe v3_b32_h128_l16384 full size")
+    out = KvpeRun(w, 16384).step()
+    for b in (0, 31):
+        hz.check_seq("kvpe v3 16k", w, out, b)
+    paged = hz.GpuRun(w).run()
+    for k in ("q", "o_lat", "o"):
+        assert np.array_equal(out[k], paged[k]), k
+    assert np.array_equal(out["lse"], paged["lse"])
+    print("  bitwise equal to the paged pool", flush=True)
 
 
 def test_append_skips_outside_the_buffers():
