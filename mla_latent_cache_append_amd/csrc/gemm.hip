@@ -102,13 +102,15 @@ __device__ __forceinline__ void absorb_q_block(
       x[u] = *(const uint32_t*)(q_pe + ((int64_t)n * H + h) * D_ROPE + 2 * i);
       ps[u] = pos[n];
     }
+    // Every thread stores: one past the last pair rewrites the last pair
+    // with the same value. (A store behind a branch would leave the vector
+    // memory counter unknown to the compiler, whose next wait for a load
+    // would then also wait for these stores to complete.)
 #pragma unroll
     for (int u = 0; u < RP; ++u) {
-      const int p = p0 + u * AQ_CHUNKS * 256;
-      if (p < npairs) {
-        const int n = p / (D_ROPE / 2), i = p % (D_ROPE / 2);
-        *(uint32_t*)(q_out + ((int64_t)n * H + h) * D_K + D_C + 2 * i) = rope_pair_bf16(x[u], ps[u], fr.f[i]);
-      }
+      const int p = min(p0 + u * AQ_CHUNKS * 256, npairs - 1);
+      const int n = p / (D_ROPE / 2), i = p % (D_ROPE / 2);
+      *(uint32_t*)(q_out + ((int64_t)n * H + h) * D_K + D_C + 2 * i) = rope_pair_bf16(x[u], ps[u], fr.f[i]);
     }
   }
   {
@@ -167,14 +169,16 @@ __device__ __forceinline__ void absorb_q_block(
       }
     }
     __syncthreads();
-    // 32 tokens x 16 chunks of 16 bytes: chunk k = 16 t + piece, two per thread
+    // 32 tokens x 16 chunks of 16 bytes: chunk k = 16 t + piece, two per
+    // thread. Rows past the last token hold that token's outputs (its query
+    // row was loaded for them) and are stored over it, unconditionally, with
+    // the same values.
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int k = u * 256 + (int)threadIdx.x, t = k >> 4, piece = k & 15;
-      const int n = n0 + t;
-      if (n < n_end)
-        *(u32x4*)(q_out + ((int64_t)n * H + h) * D_K + c0 + 8 * piece) =
-            *(const __attribute__((address_space(3))) u32x4*)(ols + t * AQ_OSTRIDE + 16 * piece);
+      const int n = min(n0 + t, n_end - 1);
+      *(u32x4*)(q_out + ((int64_t)n * H + h) * D_K + c0 + 8 * piece) =
+          *(const __attribute__((address_space(3))) u32x4*)(ols + t * AQ_OSTRIDE + 16 * piece);
     }
     if (more) {
 #pragma unroll
@@ -319,11 +323,12 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
     __syncthreads();
     {
       // 32 tokens x 8 chunks of 16 bytes, one per thread: 8 lanes store a token's 128 bytes
+      // (rows past the last token hold that token's outputs and are stored
+      // over it with the same values, so the store is unconditional)
       const int t = (int)threadIdx.x >> 3, piece = (int)threadIdx.x & 7;
-      const int n = n0 + t;
-      if (n < n_end)
-        *(u32x4*)(o + ((int64_t)n * H + h) * D_V + (hc % OU_CHUNKS) * OU_ROWS + 8 * piece) =
-            *(const __attribute__((address_space(3))) u32x4*)(ost + t * OSTRIDE + 16 * piece);
+      const int n = min(n0 + t, n_end - 1);
+      *(u32x4*)(o + ((int64_t)n * H + h) * D_V + (hc % OU_CHUNKS) * OU_ROWS + 8 * piece) =
+          *(const __attribute__((address_space(3))) u32x4*)(ost + t * OSTRIDE + 16 * piece);
     }
   }
 }
