@@ -133,6 +133,12 @@ def make(name: str, seed: int = 0, B: int | None = None, L: int | None = None,
         B = 32 if B is None else B
         L = 16384 if L is None else L
         return Workload(name, B, 128, 1, [L] * B if lens is None else lens, "permuted", seed)
+    if name == "v3share8_b32_h128_l2048":
+        # one GPU's share of the 128-head 16k batch when each sequence's keys
+        # are split over 8 GPUs: 2,048 keys per sequence
+        B = 32 if B is None else B
+        L = 2048 if L is None else L
+        return Workload(name, B, 128, 1, [L] * B if lens is None else lens, "permuted", seed)
     if name == "ragged_b128_h128_l1to32768":
         B = 128 if B is None else B
         hi = 32768 if L is None else L
