@@ -238,18 +238,21 @@ __global__ __launch_bounds__(XTHREADS, 1) void mha_prefill_kernel(MhaArgs a, int
     if (more) load(j + 1, nx);
     const lds_char* kst = (const lds_char*)smem + (j & 1) * X_STAGE;
     const lds_char* vst = kst + K_TILE;
+    // the two key blocks' accumulator chains alternate, so no MFMA waits on
+    // the one just before it
     f32x16 S[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) S[kb][v] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < XQK / 16; ++ks) {
+    for (int ks = 0; ks < XQK / 16; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const u32x4 kf = *(const __attribute__((address_space(3))) u32x4*)(
             kst + (32 * kb + r32) * K_STRIDE + 2 * (16 * ks + 8 * hf));
         S[kb] = mfma32(as_bf16x8(kf), qf[ks], S[kb]);
       }
-    }
     // online softmax in log2 units: the max is taken over the raw scores
     // (the scale is positive), exponentials as exp2(s * scale - m); keys past
     // the row's position or past Lc masked
@@ -298,9 +301,9 @@ __global__ __launch_bounds__(XTHREADS, 1) void mha_prefill_kernel(MhaArgs a, int
       P[kk] = as_bf16x8(w);
     }
 #pragma unroll
-    for (int cb = 0; cb < D_V / 32; ++cb)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int cb = 0; cb < D_V / 32; ++cb) {   // four accumulator chains in turn
         const lds_char* vp = vst + (32 * cb + r32) * VT_STRIDE + 2 * (16 * kk + 4 * hf);
         const u32x2 lo = *(const __attribute__((address_space(3))) u32x2*)vp;
         const u32x2 hi = *(const __attribute__((address_space(3))) u32x2*)(vp + 16);
