@@ -217,12 +217,61 @@ static void test_kvpe() {
   }
 }
 
+// The expanded-form prefill: gathered rows, expanded K and V^T in a workspace
+// on a 256-byte boundary, one length above max_len, one 0, block ids out of
+// the pool.
+static void test_expanded() {
+  for (int H : {16, 128}) {
+    const mla_dims d = dims_for(H);
+    const int B = 3, Lq = 4, max_len = 200, max_blocks = 4;
+    const int64_t nb = (int64_t)B * max_blocks;
+    const size_t N = (size_t)B * Lq;
+    Buf<uint16_t> qn(N * H * 128), qp(N * H * 64), pool(nb * 64 * 576), wuk((size_t)H * 128 * 512),
+        wuv((size_t)H * 128 * 512), o(N * H * 128);
+    Buf<int32_t> pos(N), table((size_t)B * max_blocks), lens(B);
+    Buf<float> lse(N * H);
+    for (int i = 0; i < B * max_blocks; ++i) table.p()[i] = (int32_t)((i * 5 + 1) % nb);
+    table.p()[2] = -1;
+    table.p()[max_blocks + 1] = (int32_t)nb;
+    const int32_t L[B] = {200, 0, 250};   // the last one above max_len
+    for (int b = 0; b < B; ++b) lens.p()[b] = L[b];
+    const size_t need = mla_prefill_expanded_workspace_size(&d, B, max_len);
+    EXPECT(need > 0 && need % 256 == 0);
+#ifdef PLANT_SHORT_WORKSPACE
+    const size_t have = need - 256;
+#else
+    const size_t have = need;
+#endif
+    void* ws = aligned_alloc(256, have);
+    auto call = [&](uint16_t* q, void* w, size_t wb, float* l, int lq, int ml) {
+      return mla_prefill_expanded(&d, q, qp.p(), pos.p(), pool.p(), nb, table.p(), max_blocks, lens.p(), B, lq, ml,
+                                  wuk.p(), wuv.p(), o.p(), l, w, wb, nullptr);
+    };
+    EXPECT(call(qn.p(), ws, need, lse.p(), Lq, max_len) == MLA_OK);
+    EXPECT(call(qn.p(), ws, need, nullptr, Lq, max_len) == MLA_OK);
+    EXPECT(call(qn.p(), ws, need - 16, lse.p(), Lq, max_len) == MLA_ERR_WORKSPACE);
+    EXPECT(call(qn.p(), nullptr, need, lse.p(), Lq, max_len) == MLA_ERR_WORKSPACE);
+    EXPECT(call(qn.p() + 1, ws, need, lse.p(), Lq, max_len) == MLA_ERR_INVALID_ARG);
+    EXPECT(call(qn.p(), (char*)ws + 16, need, lse.p(), Lq, max_len) == MLA_ERR_INVALID_ARG);
+    EXPECT(call(qn.p(), ws, need, (float*)((char*)lse.p() + 2), Lq, max_len) == MLA_ERR_INVALID_ARG);
+    EXPECT(call(qn.p(), ws, need, lse.p(), 0, max_len) == MLA_ERR_INVALID_ARG);
+    EXPECT(call(qn.p(), ws, need, lse.p(), Lq, (1 << 20) + 1) == MLA_ERR_UNSUPPORTED);
+    free(ws);
+  }
+  const mla_dims d = dims_for(128);
+  EXPECT(mla_prefill_expanded_workspace_size(&d, 0, 10) == 0);
+  EXPECT(mla_prefill_expanded_workspace_size(&d, 65536, 10) == 0);
+  EXPECT(mla_prefill_expanded_workspace_size(&d, 1, 0) == 0);
+  EXPECT(mla_prefill_expanded_workspace_size(&d, 65535, 1 << 20) > 0);   // sized in 64 bits
+}
+
 int main() {
   test_dims();
   test_append_absorb_out_up();
   test_linear();
   test_attention();
   test_kvpe();
+  test_expanded();
   if (g_fail) {
     fprintf(stderr, "sanitizer driver: %d expectation(s) failed\n", g_fail);
     return 1;

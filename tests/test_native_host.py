@@ -254,3 +254,40 @@ def test_no_alloc_attention_rejects_shapes_beyond_its_array(nat):
                                        null) == nat.MLA_ERR_WORKSPACE
     assert lib.mla_decode_attn_noalloc(ctypes.byref(d), null, ok, 4, ok, 2, ok, 1, 1, ok, null,
                                        null) == nat.MLA_ERR_INVALID_ARG
+
+
+def test_expanded_workspace_size_is_its_layout(nat):
+    """Gathered latent and rope rows, then the expanded K and V^T, each region
+    on a 256-byte boundary, for max_len rounded up to 32 rows per sequence."""
+    d = nat.mla_dims_default(128)
+    r256 = lambda n: (n + 255) // 256 * 256
+    for B, max_len in [(4, 1000), (1, 1), (3, 32), (2, 33), (7, 16896)]:
+        rows = B * ((max_len + 31) // 32 * 32)
+        want = r256(rows * 512 * 2) + r256(rows * 64 * 2) + 2 * r256(rows * 128 * 128 * 2)
+        assert nat.mla_prefill_expanded_workspace_size(d, B, max_len) == want, (B, max_len)
+    for B, max_len in [(0, 10), (65536, 10), (1, 0), (1, (1 << 20) + 1)]:
+        assert nat.mla_prefill_expanded_workspace_size(d, B, max_len) == 0, (B, max_len)
+
+
+def test_expanded_checks_arguments_on_the_host(nat):
+    lib = nat.lib()
+    d = nat.mla_dims_default(128)
+    P = ctypes.c_void_p
+    fake, null = P(0x1000), P(0)   # never dereferenced: the host checks fail first
+    need = nat.mla_prefill_expanded_workspace_size(d, 4, 1000)
+
+    def call(dims=d, q=fake, pool=fake, nb=16, mb=16, B=4, Lq=8, max_len=1000, o=fake, lse=null, ws=fake,
+             wsb=need):
+        return lib.mla_prefill_expanded(ctypes.byref(dims), q, fake, fake, pool, nb, fake, mb, fake, B, Lq, max_len,
+                                        fake, fake, o, lse, ws, wsb, null)
+
+    for kw in (dict(q=null), dict(pool=null), dict(o=null), dict(B=0), dict(Lq=0), dict(max_len=0), dict(nb=0),
+               dict(mb=0), dict(q=P(0x1008)), dict(o=P(0x1004)), dict(lse=P(0x1002)), dict(ws=P(0x1010))):
+        assert call(**kw) == nat.MLA_ERR_INVALID_ARG, kw
+    for kw in (dict(B=65536), dict(max_len=(1 << 20) + 1), dict(Lq=(1 << 20) + 1), dict(mb=(1 << 24) + 1)):
+        assert call(**kw) == nat.MLA_ERR_UNSUPPORTED, kw
+    assert call(wsb=need - 1) == nat.MLA_ERR_WORKSPACE
+    assert call(ws=null) == nat.MLA_ERR_WORKSPACE
+    bad = nat.mla_dims_default(128)
+    bad.d_c = 256
+    assert call(dims=bad) == nat.MLA_ERR_UNSUPPORTED
