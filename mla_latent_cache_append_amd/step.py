@@ -13,6 +13,21 @@ import torch
 
 from . import native as nat
 
+# Query tokens per sequence from which the expanded form (mla_prefill_expanded)
+# is faster than the absorbed calls: measured crossover ~295-340 at 16,384
+# cached tokens and 128 heads on MI355X. Both forms' costs grow with the keys
+# and the heads alike (expansion 2 L H 256 512 flops, attention 2 H Lq L 320,
+# against 2 H Lq L 1088 absorbed), so the crossover depends mostly on Lq.
+EXPANDED_FROM_LQ = 320
+
+
+def prefill_form(Lq: int, cache: str = "bf16") -> str:
+    """"expanded" for chunks of at least EXPANDED_FROM_LQ query tokens per
+    sequence over the paged bf16 pool, else "absorbed" (decode steps, short
+    chunks, and the FP8 and two-buffer caches, which only the absorbed calls
+    read)."""
+    return "expanded" if cache == "bf16" and Lq >= EXPANDED_FROM_LQ else "absorbed"
+
 
 class DecodeStep:
     """Buffers and arguments of one decode step for B sequences of Lq new tokens.
@@ -26,10 +41,17 @@ class DecodeStep:
     layout: ``pool`` is kv_cache [B, max_seq, 512], there is no block table,
     and the ``slots`` argument of ``append`` / ``__call__`` is each new
     token's sequence index (int32) instead of its pool slot.
+
+    ``form`` selects how the step attends: "absorbed" (absorb_q,
+    decode_attn, out_up), "expanded" (mla_prefill_expanded: per-head K and V
+    expanded from the cache, then multi-head attention; paged bf16 pool
+    only, sequences of at most ``max_len`` keys, a workspace allocated here)
+    or "auto" (``prefill_form(Lq)``). Both fill ``o`` and ``lse``; the
+    expanded form leaves ``q`` and ``o_lat`` unwritten.
     """
 
     def __init__(self, H: int, B: int, Lq: int, pool, block_table, seq_lens, w_uk, w_uv,
-                 device="cuda", pool_scale=None, pe_cache=None):
+                 device="cuda", pool_scale=None, pe_cache=None, form: str = "absorbed", max_len: int = 0):
         self.dims = nat.mla_dims_default(H)
         self.H, self.B, self.Lq, self.N = H, B, Lq, B * Lq
         self.pool, self.block_table, self.seq_lens = pool, block_table, seq_lens
@@ -43,6 +65,21 @@ class DecodeStep:
         self.o = torch.empty(N, H, nat.D_V, dtype=torch.bfloat16, device=device)
         ws = nat.mla_decode_workspace_size(self.dims, B, Lq)
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        cache = "fp8" if pool_scale is not None else "kvpe" if pe_cache is not None else "bf16"
+        self.form = prefill_form(Lq, cache) if form == "auto" else form
+        if self.form not in ("absorbed", "expanded"):
+            raise ValueError(f"form must be 'absorbed', 'expanded' or 'auto', not {form!r}")
+        self.max_len = int(max_len)
+        self.expanded_ws = None
+        if self.form == "expanded":
+            if cache != "bf16":
+                raise ValueError("the expanded form reads the paged bf16 pool only")
+            if self.max_len <= 0:
+                raise ValueError("the expanded form needs max_len (the longest sequence, in keys)")
+            xs = nat.mla_prefill_expanded_workspace_size(self.dims, B, self.max_len)
+            if xs == 0:
+                raise ValueError("shape not supported by the expanded form")
+            self.expanded_ws = torch.empty(xs, dtype=torch.uint8, device=device)
 
     def append(self, c_kv, k_pe, pos, slots):
         if self.pe_cache is not None:
@@ -64,7 +101,15 @@ class DecodeStep:
             nat.mla_decode_attn_fp8(self.dims, self.q, self.pool, self.pool_scale, self.block_table,
                                     self.seq_lens, self.Lq, self.o_lat, self.lse, self.workspace)
 
+    def attend_expanded(self, q_nope, q_pe, q_pos):
+        """The expanded form over the cache as it stands: o and lse."""
+        nat.mla_prefill_expanded(self.dims, q_nope, q_pe, q_pos, self.pool, self.block_table, self.seq_lens,
+                                 self.Lq, self.max_len, self.w_uk, self.w_uv, self.o, self.lse, self.expanded_ws)
+
     def attend(self, q_nope, q_pe, q_pos):
+        if self.form == "expanded":
+            self.attend_expanded(q_nope, q_pe, q_pos)
+            return
         nat.mla_absorb_q(self.dims, q_nope, q_pe, q_pos, self.w_uk, self.q)
         self.decode_attn()
         nat.mla_out_up(self.dims, self.o_lat, self.w_uv, self.o)
@@ -73,7 +118,7 @@ class DecodeStep:
         """Append the N new tokens (row n = b*Lq + i at position q_pos[n]), then
         attend: append and absorb share one launch (two launches for the
         two-buffer cache), then attention and out_up."""
-        if self.pe_cache is not None:
+        if self.pe_cache is not None or self.form == "expanded":
             self.append(c_kv, k_pe, q_pos, slots)
             self.attend(q_nope, q_pe, q_pos)
             return self.o

@@ -291,3 +291,16 @@ def test_expanded_checks_arguments_on_the_host(nat):
     bad = nat.mla_dims_default(128)
     bad.d_c = 256
     assert call(dims=bad) == nat.MLA_ERR_UNSUPPORTED
+
+
+def test_prefill_form_follows_the_measured_crossover():
+    """The step's form choice (host logic): the expanded form from the
+    measured crossover's query-token count on, over the paged bf16 pool only."""
+    from mla_latent_cache_append_amd import step
+    assert step.prefill_form(1) == "absorbed"
+    assert step.prefill_form(step.EXPANDED_FROM_LQ - 1) == "absorbed"
+    assert step.prefill_form(step.EXPANDED_FROM_LQ) == "expanded"
+    assert step.prefill_form(2048) == "expanded"
+    assert step.prefill_form(2048, "fp8") == "absorbed"
+    assert step.prefill_form(2048, "kvpe") == "absorbed"
+    assert 256 < step.EXPANDED_FROM_LQ < 512   # between the sweep's last absorbed-faster and first expanded-faster sizes
