@@ -416,7 +416,7 @@ def main():
         print(json.dumps(t))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 

@@ -77,7 +77,7 @@ def assert_parity(name: str, gpu, ref, max_rel=MAX_REL, mean_rel=MEAN_REL) -> di
 # ----------------------------------------------------------------- GPU side
 
 
-class GpuRun:
+class DeviceRun:
     """Fill the paged pool with every sequence's history through
     mla_cache_append, then run one decode step (append the Lq new tokens,
     absorb, attend, up-project) through the C ABI."""

@@ -68,7 +68,7 @@ def check_outputs(name, w, out, b, ref):
 def test_fp8_append_codes_and_scales():
     w = workloads.make("ragged_b128_h128_l1to32768", seed=11, B=4, lens=[1, 70, 200, 1031])
     _say(f"fp8 append {w.name} lens={list(w.lens)}")
-    run = hz.GpuRun(w, fp8=True)
+    run = hz.DeviceRun(w, fp8=True)
     run.run()
     for b in range(w.B):
         ref = hz.oracle_seq_fp8(w, b)
@@ -121,7 +121,7 @@ def test_fp8_decode_small(H, Lq, lens):
     w = workloads.Workload(f"fp8_h{H}_lq{Lq}", len(lens), H, Lq, lens,
                            "permuted" if H >= 64 else "contiguous", seed=100 + H + Lq)
     _say(f"fp8 decode step H={H} Lq={Lq} lens={lens}")
-    run = hz.GpuRun(w, fp8=True)
+    run = hz.DeviceRun(w, fp8=True)
     out = run.run()
     for b in range(w.B):
         ref = hz.oracle_seq_fp8(w, b)
@@ -133,7 +133,7 @@ def test_fp8_decode_small(H, Lq, lens):
 def test_fp8_zero_lengths_and_determinism(H):
     w = workloads.Workload("fp8_short", 4, H, 4, [0, 3, 5, 64], "contiguous", seed=19)
     _say(f"fp8 H={H} lens [0, 3, 5, 64] with Lq=4, run twice")
-    run = hz.GpuRun(w, fp8=True)
+    run = hz.DeviceRun(w, fp8=True)
     out = run.run()
     again = run.run()
     for k in ("o_lat", "o"):
@@ -148,7 +148,7 @@ def test_fp8_zero_lengths_and_determinism(H):
 def test_fp8_bad_block_id_poisons_only_its_sequence(H):
     w = workloads.Workload("fp8_poison", 3, H, 1, [100, 100, 100], "contiguous", seed=14)
     _say(f"fp8 H={H}: block id out of range in seq 1 and seq_len beyond the table in seq 2")
-    run = hz.GpuRun(w, fp8=True)
+    run = hz.DeviceRun(w, fp8=True)
     run.block_table[1, 1] = w.num_blocks
     run.seq_lens[2] = w.max_blocks * 64 + 1
     out = run.run()
@@ -166,7 +166,7 @@ def test_fp8_bad_block_id_poisons_only_its_sequence(H):
 def test_fp8_full_size_sampled(name):
     w = workloads.make(name, seed=0)
     _say(f"fp8 full size {name}: B={w.B} H={w.H} Lq={w.Lq} total keys={int(w.lens.sum())}")
-    run = hz.GpuRun(w, fp8=True)
+    run = hz.DeviceRun(w, fp8=True)
     out = run.run()
     for b in sorted({0, w.B // 2, w.B - 1, int(np.argmax(w.lens)), int(np.argmin(w.lens))}):
         ref = hz.oracle_seq_fp8(w, b)

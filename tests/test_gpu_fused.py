@@ -29,7 +29,7 @@ def test_fused_append_absorb_equals_separate_calls(H, lens, fp8):
     from mla_latent_cache_append_amd import native as nat
     w = workloads.Workload("fused", len(lens), H, 1, lens, "permuted", seed=21)
     print(f"\n[case] fused append+absorb: H={H} lens={lens} fp8={fp8}", flush=True)
-    run = hz.GpuRun(w, fp8=fp8)
+    run = hz.DeviceRun(w, fp8=fp8)
     ckv, kpe, qpos, slot = run.new
     qn, qp = hz.to_dev(run.q_nope), hz.to_dev(run.q_pe)
     st = run.step

@@ -32,7 +32,7 @@ def test_graph_replays_match_eager(H, lens, fp8, reps):
     rewrites the same cache rows and recomputes the same outputs)."""
     w = workloads.Workload("graph", len(lens), H, 1, lens, "permuted", seed=11)
     print(f"\n[case] graph replay: H={H} lens={lens} fp8={fp8} steps per graph={reps}", flush=True)
-    run = hz.GpuRun(w, fp8=fp8)
+    run = hz.DeviceRun(w, fp8=fp8)
     ckv, kpe, qpos, slot = run.new
     qn, qp = hz.to_dev(run.q_nope), hz.to_dev(run.q_pe)
     step = run.step

@@ -136,7 +136,7 @@ def test_v2lite_4k_full_size_matches_oracle_and_paged_pool():
     out = KvpeRun(w, 4096).step()
     for b in (0, 37, 63):
         hz.check_seq("kvpe v2lite 4k", w, out, b)
-    paged = hz.GpuRun(w).run()
+    paged = hz.DeviceRun(w).run()
     for k in ("q", "o_lat", "o"):
         assert np.array_equal(out[k], paged[k]), k
     assert np.array_equal(out["lse"], paged["lse"])
@@ -195,7 +195,7 @@ def test_v3_16k_full_size_matches_paged_pool():
     out = KvpeRun(w, 16384).step()
     for b in (0, 31):
         hz.check_seq("kvpe v3 16k", w, out, b)
-    paged = hz.GpuRun(w).run()
+    paged = hz.DeviceRun(w).run()
     for k in ("q", "o_lat", "o"):
         assert np.array_equal(out[k], paged[k]), k
     assert np.array_equal(out["lse"], paged["lse"])

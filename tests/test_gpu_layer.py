@@ -115,7 +115,7 @@ def test_layer_stack_error_growth():
     runs, steps, layers_f64, hists = [], [], [], []
     for l in range(n_layers):
         w = workloads.Workload(f"layer{l}", B, H, 1, lens, "permuted", seed=100 + l)
-        run = hz.GpuRun(w)
+        run = hz.DeviceRun(w)
         lw = workloads.layer_weights(100, l, H, d_model, d_cq)
         steps.append(LayerStep(run.step, **{k: hz.to_dev(v) for k, v in lw.items()}))
         runs.append(run)
@@ -155,7 +155,7 @@ def test_layer_graph_replays_match_eager(reps):
     from mla_latent_cache_append_amd.step import LayerStep
     H, d_model, d_cq = 16, 2048, 1536
     w = workloads.Workload("layer_graph", 3, H, 1, [70, 600, 1500], "permuted", seed=300)
-    run = hz.GpuRun(w)
+    run = hz.DeviceRun(w)
     lw = workloads.layer_weights(300, 0, H, d_model, d_cq)
     st = LayerStep(run.step, **{k: hz.to_dev(v) for k, v in lw.items()})
     h = hz.to_dev(workloads.hidden_states(300, w.B, d_model))

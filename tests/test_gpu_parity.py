@@ -35,7 +35,7 @@ def _lib():
 def test_append_latent_bit_exact_rope_within_ulp():
     w = workloads.make("ragged_b128_h128_l1to32768", seed=1, B=4, lens=[1, 70, 200, 1031])
     _say(f"append {w.name} lens={list(w.lens)}")
-    run = hz.GpuRun(w)
+    run = hz.DeviceRun(w)
     run.run()
     for b in range(w.B):
         L = int(w.lens[b])
@@ -86,7 +86,7 @@ def test_decode_step_small(H, Lq, lens):
     w = workloads.Workload(f"small_h{H}_lq{Lq}", len(lens), H, Lq, lens,
                            "permuted" if H >= 64 else "contiguous", seed=H + Lq)
     _say(f"decode step H={H} Lq={Lq} lens={lens}")
-    out = hz.GpuRun(w).run()
+    out = hz.DeviceRun(w).run()
     for b in range(w.B):
         hz.check_seq(w.name, w, out, b)
 
@@ -96,7 +96,7 @@ def test_many_short_sequences_multi_segment():
     lens = rng.integers(1, 300, size=300)
     w = workloads.Workload("many_h16", 300, 16, 1, lens, "permuted", seed=5)
     _say(f"decode step B=300 H=16 lens 1..300 (ranges span many sequences)")
-    out = hz.GpuRun(w).run()
+    out = hz.DeviceRun(w).run()
     for b in [0, 1, 2, 150, 298, 299, int(np.argmax(lens)), int(np.argmin(lens))]:
         hz.check_seq(w.name, w, out, b)
 
@@ -110,7 +110,7 @@ def test_many_short_sequences_multi_segment():
 def test_zero_and_short_lengths(H, Lq, lens):
     w = workloads.Workload("short", len(lens), H, Lq, lens, "contiguous", seed=9)
     _say(f"lens {lens} with Lq={Lq}, H={H}: empty sequences (and positions below 0)")
-    out = hz.GpuRun(w).run()
+    out = hz.DeviceRun(w).run()
     rows = Lq * H
     for b, L in enumerate(lens):
         if L == 0:
@@ -167,7 +167,7 @@ def test_tiny_prefill_then_decode_matches_one_shot():
 def test_determinism_bitwise():
     w = workloads.make("ragged_b128_h128_l1to32768", seed=3, B=6, L=3000)
     _say(f"determinism: two runs of {w.name} lens={list(w.lens)}")
-    run = hz.GpuRun(w)
+    run = hz.DeviceRun(w)
     a = run.run()
     b = run.run()
     for k in ("q", "o_lat", "o"):
@@ -178,7 +178,7 @@ def test_determinism_bitwise():
 def test_bad_block_id_and_length_poison_only_their_sequence():
     w = workloads.Workload("poison", 3, 16, 1, [100, 100, 100], "contiguous", seed=4)
     _say("block id out of range in seq 1 and seq_len beyond the table in seq 2")
-    run = hz.GpuRun(w)
+    run = hz.DeviceRun(w)
     run.block_table[1, 1] = w.num_blocks          # out of range
     run.seq_lens[2] = w.max_blocks * 64 + 1       # beyond the table
     out = run.run()
@@ -197,7 +197,7 @@ def test_bad_block_id_and_length_poison_only_their_sequence():
 def test_full_size_sampled(name):
     w = workloads.make(name, seed=0)
     _say(f"full size {name}: B={w.B} H={w.H} Lq={w.Lq} total keys={int(w.lens.sum())}")
-    out = hz.GpuRun(w).run()
+    out = hz.DeviceRun(w).run()
     picks = sorted({0, w.B - 1, int(np.argmax(w.lens)), int(np.argmin(w.lens)), w.B // 2})
     for b in picks:
         hz.check_seq(name, w, out, b)
@@ -211,6 +211,6 @@ def test_prefill_chunk_full_size_sampled(name):
     (the first, the last and two between), the GPU computes all of them."""
     w = workloads.make(name, seed=0)
     _say(f"prefill chunk {name}: B={w.B} H={w.H} Lq={w.Lq} total keys={int(w.lens.sum())}")
-    out = hz.GpuRun(w).run()
+    out = hz.DeviceRun(w).run()
     for b in (0, w.B - 1):
         hz.check_queries(name, w, out, b, [0, 1, w.Lq // 2 + 3, w.Lq - 1])

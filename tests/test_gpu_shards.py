@@ -28,7 +28,7 @@ def test_sharded_keys_merge_to_the_whole_sequence(shards):
     L, H = int(w.lens[0]), w.H
     blocks = L // 64
     _say(f"one 16k sequence at 128 heads in {shards} key shards")
-    run = hz.GpuRun(w)
+    run = hz.DeviceRun(w)
     full = run.run()
     # shard g takes whole 64-token blocks [cuts[g], cuts[g+1]) of the sequence's block table
     cuts = np.linspace(0, blocks, shards + 1).round().astype(int)

@@ -23,7 +23,7 @@ def _lib():
 
 def _compare(w: workloads.Workload):
     from mla_latent_cache_append_amd import native as nat
-    run = hz.GpuRun(w)
+    run = hz.DeviceRun(w)
     ref = run.run()                                   # the step's attention: mla_decode_attn
     s = run.step
     o_lat = torch.full_like(s.o_lat, float("nan"))
