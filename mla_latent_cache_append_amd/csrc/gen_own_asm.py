@@ -140,11 +140,11 @@ def vread(seq, j):
 
 
 # Two-buffer cache (PE = True below): the latent rows (1,024 bytes per token)
-# and the rope rows (128 bytes per token) sit in two arrays. Lines 0..7 of a
-# half tile read the latent array with the same instructions as the pool
-# (operands go / so / rs carry the 1,024-byte stride); line 8 reads the rope
-# array through its own offsets gp / sp and descriptor rp, at instruction
-# offset 0.
+# and the rope rows (128 bytes per token) sit in two arrays. The 1-KiB copies
+# of column groups 0..7 of a half tile read the latent array with the same
+# instructions as the pool (operands go / so / rs carry the 1,024-byte
+# stride); the copy of column group 8 reads the rope array through its own
+# offsets gp / sp and descriptor rp, at instruction offset 0.
 PE = False
 
 
