@@ -20,6 +20,7 @@
 #include <hipblaslt/hipblaslt.h>
 
 #include <mutex>
+#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -340,6 +341,21 @@ constexpr int MAX_DEVICES = 64;
 std::mutex lt_mu;
 hipblasLtHandle_t lt_handles[MAX_DEVICES];
 
+// The algorithm hipBLASLt's heuristic picked for each GEMM shape on each
+// device, so that repeated calls skip the query (about 15 us of host time per
+// GEMM). A handful of shapes per run: searched linearly, the oldest dropped
+// past LT_ALGOS.
+struct LtShape {
+  int dev, ta, tb;
+  int64_t m, n, k, lda, ldb, ldd;
+  bool operator==(const LtShape& o) const {
+    return dev == o.dev && ta == o.ta && tb == o.tb && m == o.m && n == o.n && k == o.k && lda == o.lda &&
+           ldb == o.ldb && ldd == o.ldd;
+  }
+};
+constexpr size_t LT_ALGOS = 64;
+std::vector<std::pair<LtShape, hipblasLtMatmulAlgo_t>> lt_algos;   // guarded by lt_mu
+
 hipError_t lt_handle(hipblasLtHandle_t* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -367,7 +383,11 @@ hipError_t lt_gemm(hipblasLtHandle_t handle, hipblasOperation_t ta, hipblasOpera
   const int64_t b_rows = tb == HIPBLAS_OP_N ? k : n, b_cols = tb == HIPBLAS_OP_N ? n : k;
   const float alpha = 1.f, beta = 0.f;
   hipblasLtMatmulHeuristicResult_t heur[1];
-  int found = 0;
+  int found = 0, dev = 0;
+  bool cached = false;
+  hipblasLtMatmulAlgo_t algo;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorUnknown;
+  const LtShape key{dev, (int)ta, (int)tb, m, n, k, lda, ldb, ldd};
   if (hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) goto done;
   if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) != HIPBLAS_STATUS_SUCCESS ||
       hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) != HIPBLAS_STATUS_SUCCESS)
@@ -376,12 +396,27 @@ hipError_t lt_gemm(hipblasLtHandle_t handle, hipblasOperation_t ta, hipblasOpera
       hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, b_rows, b_cols, ldb) != HIPBLAS_STATUS_SUCCESS ||
       hipblasLtMatrixLayoutCreate(&ld, HIP_R_16BF, m, n, ldd) != HIPBLAS_STATUS_SUCCESS)
     goto done;
-  if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) goto done;
-  if (hipblasLtMatmulAlgoGetHeuristic(handle, desc, la, lb, ld, ld, pref, 1, heur, &found) !=
-          HIPBLAS_STATUS_SUCCESS ||
-      found < 1)
-    goto done;
-  if (hipblasLtMatmul(handle, desc, &alpha, A, la, B, lb, &beta, D, ld, D, ld, &heur[0].algo, nullptr, 0, stream) ==
+  {
+    std::lock_guard<std::mutex> lock(lt_mu);
+    for (const auto& e : lt_algos)
+      if (e.first == key) {
+        algo = e.second;
+        cached = true;
+        break;
+      }
+  }
+  if (!cached) {
+    if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) goto done;
+    if (hipblasLtMatmulAlgoGetHeuristic(handle, desc, la, lb, ld, ld, pref, 1, heur, &found) !=
+            HIPBLAS_STATUS_SUCCESS ||
+        found < 1)
+      goto done;
+    algo = heur[0].algo;
+    std::lock_guard<std::mutex> lock(lt_mu);
+    if (lt_algos.size() >= LT_ALGOS) lt_algos.erase(lt_algos.begin());
+    lt_algos.emplace_back(key, algo);
+  }
+  if (hipblasLtMatmul(handle, desc, &alpha, A, la, B, lb, &beta, D, ld, D, ld, &algo, nullptr, 0, stream) ==
       HIPBLAS_STATUS_SUCCESS)
     err = hipSuccess;
 done:
