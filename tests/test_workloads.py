@@ -54,6 +54,19 @@ def test_query_positions_and_slots():
     assert np.all(s // 64 == np.repeat(w.block_table[1, :2], 64)[:100])
 
 
+def test_context_share_workload_is_an_eighth_of_the_128_head_batch():
+    """One GPU's share of the 128-head 16k batch when each sequence's keys are
+    split over 8 GPUs: the same batch and heads, 2,048 keys per sequence, and
+    a permuted block table that covers its pool."""
+    full = workloads.make("v3_b32_h128_l16384", seed=0)
+    share = workloads.make("v3share8_b32_h128_l2048", seed=0)
+    assert (share.B, share.H, share.Lq) == (full.B, full.H, full.Lq)
+    assert np.all(share.lens * 8 == full.lens)
+    assert share.num_blocks * 8 == full.num_blocks
+    used = share.block_table[share.block_table >= 0]
+    assert sorted(used.tolist()) == list(range(share.num_blocks))
+
+
 def test_prefill_chunk_workload_shape():
     w = workloads.make("chunk512_b4_h128_l16896", seed=0)
     assert (w.B, w.H, w.Lq, w.N) == (4, 128, 512, 2048)
