@@ -27,27 +27,29 @@ constexpr int AQ_CHUNKS = D_C / AQ_COLS;     // 4 workgroups per head
 // each) then hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int aq_swz(int j) { return 2 * (j & 3) + 8 * ((j >> 3) & 1); }
 
-// Each workgroup computes a [N x 128] column slice of q_lat for one head and
-// rotates a quarter of that head's rope pairs (q_pe[n][h], one pair per
-// thread and pass), so the rotation spreads over the whole grid.
+// Each workgroup computes a [tokens x 128] column slice of q_lat for one
+// head and rotates 64 (token, head) rows of q_pe, so the rotation spreads
+// over the whole grid.
 // W_UK[h] is stored [128 j][512 c] (rows of nn.Linear(d_c, H*d_nope).weight)
 // and the contraction runs over j, its row index: the MFMA A operand
 // (8 consecutive j of one column c) comes from two transposing LDS reads
 // (ds_read_b64_tr_b16) of the row-major slice.
 constexpr int AQ_LDS = D_NOPE * AQ_COLS * 2;   // 32 KiB weight slice
-// A pass's outputs (32 tokens x 128 columns) go through LDS on their way out,
-// so that 16 consecutive lanes store one token's 256 contiguous bytes (whole
-// 128-byte lines) rather than 32-byte pieces of 16 tokens. Rows are padded
-// to 272 bytes: the 16 tokens of one fragment write land on distinct banks.
-// The staging reuses the weight slice's LDS once its fragments are in registers.
-constexpr int AQ_OSTRIDE = AQ_COLS * 2 + 16;
-static_assert(32 * AQ_OSTRIDE <= AQ_LDS, "output staging fits in the weight slice's LDS");
-
-// Tokens per absorb workgroup: one workgroup per (head, column slice) sweeps
+// Tokens per absorb workgroup: one workgroup per (head, column slice) takes
 // a decode batch whole; a prefill-sized batch is split into runs of this many
 // tokens, each on its own workgroups (grid H * 4 * ceil(N / AQ_TPW)).
 constexpr int AQ_TPW = 256;
 __host__ __device__ constexpr int aq_runs(int N) { return (N + AQ_TPW - 1) / AQ_TPW; }
+// Within a run, wave w takes tokens 64 p + 16 w .. +15 in pass p: the four
+// waves read disjoint query rows, and each keeps the whole 128-column weight
+// slice in registers.
+constexpr int AQ_WT = 16;
+constexpr int AQ_PASSES = AQ_TPW / (4 * AQ_WT);
+// A pass's outputs (16 tokens x 128 columns) go through this wave's own
+// region of the LDS so that 16 lanes store one token's 256 contiguous bytes;
+// rows padded to 272 bytes.
+constexpr int AQ_OSTRIDE = AQ_COLS * 2 + 16;
+static_assert(4 * AQ_WT * AQ_OSTRIDE <= AQ_LDS, "output staging fits in the weight slice's LDS");
 
 __device__ __forceinline__ void absorb_q_block(
     int blk, char* wl, const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
@@ -72,71 +74,82 @@ __device__ __forceinline__ void absorb_q_block(
   __attribute__((address_space(3))) char* wls = (__attribute__((address_space(3))) char*)wl;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
-  // B = q_nope^T[K = j][N = token] of two 16-token blocks: lane (g, c) holds
-  // token n0 + 16 tb + c, rows 32 ks + 8 g .. +7. Lanes past the last token
-  // load a valid row; their columns are not stored.
-  bf16x8 bq[2][D_NOPE / 32], bn[2][D_NOPE / 32];
-  auto load_q = [&](bf16x8 (&dst)[2][D_NOPE / 32], int n0) {
+  // Every load of the workgroup is issued before the first wait: the rope
+  // pairs (with their positions and this lane's inverse frequency), the
+  // weight slice and this wave's query rows of all its passes.
+  //
+  // Rope: the run's (token, head) rows, head fastest, are dealt 64 to each
+  // of its 4H workgroups; thread (i = thread % 32, r = thread / 32) rotates
+  // pair i of rows r + 8 m (m < 8) of its workgroup's. At 64 heads or more a
+  // workgroup's rows are heads of one token, so each thread computes one
+  // angle for its eight pairs. Rows past the run's last one wrap round to
+  // its first rows and are stored again with the same values (every thread
+  // stores: a store behind a branch would leave the vector memory counter
+  // unknown to the compiler, whose next wait for a load would then also
+  // wait for these stores to complete).
+  constexpr int RP = AQ_TPW * (D_ROPE / 2) / (AQ_CHUNKS * 256);
+  const int ri = (int)threadIdx.x & (D_ROPE / 2 - 1);
+  const int rows = (n_end - n_begin) * H;
+  const int r0 = 64 * (h * AQ_CHUNKS + chunk) + ((int)threadIdx.x >> 5);
+  const double inv_freq = fr.f[ri];
+  uint32_t x[RP];
+  int ps[RP], rn[RP], rrow[RP];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int n = min(n0 + 16 * tb + c, n_end - 1);
-      const uint16_t* src = q_nope + ((int64_t)n * H + h) * D_NOPE + 8 * g;
+  for (int u = 0; u < RP; ++u) {
+    int R = r0 + 8 * u;
+    if (R >= rows) R %= rows;
+    const int t = R / H;
+    rn[u] = n_begin + t;
+    rrow[u] = (n_begin + t) * H + (R - t * H);   // (token, head) row of q_pe and q_out
+    x[u] = *(const uint32_t*)(q_pe + (int64_t)rrow[u] * D_ROPE + 2 * ri);
+    ps[u] = pos[rn[u]];
+  }
+  // the weight slice: 2048 chunks of 16 bytes, eight per thread
+  constexpr int PER = D_NOPE * (AQ_COLS / 8) / 256;
+  u32x4 v[PER];
 #pragma unroll
-      for (int ks = 0; ks < D_NOPE / 32; ++ks) dst[tb][ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
-    }
-  };
-  load_q(bq, n_begin);   // in flight together with the weight slice
+  for (int u = 0; u < PER; ++u) {
+    const int k = u * 256 + threadIdx.x, j = k >> 4, ch = k & 15;
+    v[u] = *(const u32x4*)(w + (int64_t)j * D_C + ch * 8);
+  }
+  // B = q_nope^T[K = j][N = token]: lane (g, c) holds token n0 + c, rows
+  // 32 ks + 8 g .. +7. Lanes past the last token load a valid row; their
+  // columns are stored over that token's with the same values.
+  bf16x8 bq[AQ_PASSES][D_NOPE / 32];
+#pragma unroll
+  for (int p = 0; p < AQ_PASSES; ++p) {
+    const int n = min(n_begin + 64 * p + 16 * wave + c, n_end - 1);
+    const uint16_t* src = q_nope + ((int64_t)n * H + h) * D_NOPE + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < D_NOPE / 32; ++ks) bq[p][ks] = as_bf16x8(*(const u32x4*)(src + 32 * ks));
+  }
+  __builtin_amdgcn_sched_barrier(0);
   {
-    // rope pairs p = (token p / 32, pair p % 32) of head h: q_out[n][h][512 + 2i .. +1];
-    // this slice takes every fourth group of 256, at most AQ_TPW / 32 per
-    // thread, with all the loads issued before the rotations
-    constexpr int RP = AQ_TPW * (D_ROPE / 2) / (AQ_CHUNKS * 256);
-    const int npairs = n_end * (D_ROPE / 2);
-    const int p0 = n_begin * (D_ROPE / 2) + chunk * 256 + (int)threadIdx.x;
-    uint32_t x[RP];
-    int ps[RP];
+    int n_prev = -1;
+    double cs = 1.0, sn = 0.0;
 #pragma unroll
     for (int u = 0; u < RP; ++u) {
-      const int p = min(p0 + u * AQ_CHUNKS * 256, npairs - 1);
-      const int n = p / (D_ROPE / 2), i = p % (D_ROPE / 2);
-      x[u] = *(const uint32_t*)(q_pe + ((int64_t)n * H + h) * D_ROPE + 2 * i);
-      ps[u] = pos[n];
-    }
-    // Every thread stores: one past the last pair rewrites the last pair
-    // with the same value. (A store behind a branch would leave the vector
-    // memory counter unknown to the compiler, whose next wait for a load
-    // would then also wait for these stores to complete.)
-#pragma unroll
-    for (int u = 0; u < RP; ++u) {
-      const int p = min(p0 + u * AQ_CHUNKS * 256, npairs - 1);
-      const int n = p / (D_ROPE / 2), i = p % (D_ROPE / 2);
-      *(uint32_t*)(q_out + ((int64_t)n * H + h) * D_K + D_C + 2 * i) = rope_pair_bf16(x[u], ps[u], fr.f[i]);
+      if (rn[u] != n_prev) {   // a new token: its angle
+        rope_cos_sin(ps[u], inv_freq, cs, sn);
+        n_prev = rn[u];
+      }
+      *(uint32_t*)(q_out + (int64_t)rrow[u] * D_K + D_C + 2 * ri) = rope_rotate_bf16(x[u], cs, sn);
     }
   }
-  {
-    // 2048 chunks of 16 bytes, eight per thread: all loads in flight before the LDS writes
-    constexpr int PER = D_NOPE * (AQ_COLS / 8) / 256;
-    u32x4 v[PER];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int k = u * 256 + threadIdx.x, j = k >> 4, ch = k & 15;
-      v[u] = *(const u32x4*)(w + (int64_t)j * D_C + ch * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int k = u * 256 + threadIdx.x, j = k >> 4, ch = k & 15;
-      *(__attribute__((address_space(3))) u32x4*)(wls + j * 256 + ((ch ^ aq_swz(j)) << 4)) = v[u];
-    }
+  for (int u = 0; u < PER; ++u) {
+    const int k = u * 256 + threadIdx.x, j = k >> 4, ch = k & 15;
+    *(__attribute__((address_space(3))) u32x4*)(wls + j * 256 + ((ch ^ aq_swz(j)) << 4)) = v[u];
   }
   __syncthreads();
 
-  // A = W^T[M = column][K = j]: this wave's two 16-column blocks
-  // (c0 + 32 wave + 16 cb + c), k-step ks covers j = 32 ks .. +31 and lane
-  // group g its rows 32 ks + 8 g .. +7.
-  bf16x8 af[2][D_NOPE / 32];
+  // A = W^T[M = column][K = j]: the eight 16-column blocks of the slice
+  // (c0 + 16 cb + c), k-step ks covers j = 32 ks .. +31 and lane group g its
+  // rows 32 ks + 8 g .. +7.
+  bf16x8 af[AQ_COLS / 16][D_NOPE / 32];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int col = 32 * wave + 16 * cb + 4 * (c & 3);   // first column of this lane's 8-byte piece
+  for (int cb = 0; cb < AQ_COLS / 16; ++cb) {
+    const int col = 16 * cb + 4 * (c & 3);   // first column of this lane's 8-byte piece
     const int ch = col >> 3, half = (col >> 2) & 1;
 #pragma unroll
     for (int ks = 0; ks < D_NOPE / 32; ++ks) {
@@ -147,45 +160,37 @@ __device__ __forceinline__ void absorb_q_block(
     }
   }
   __syncthreads();   // every wave holds its fragments: the slice's LDS becomes the output staging
-  // two 16-token blocks per pass; the next pass's query loads are issued
-  // before this pass's products
-  __attribute__((address_space(3))) char* ols = wls;
-  for (int n0 = n_begin; n0 < n_end; n0 += 32) {
-    const bool more = n0 + 32 < n_end;
-    if (more) load_q(bn, n0 + 32);
-    __builtin_amdgcn_sched_barrier(0);
-    if (n0 > n_begin) __syncthreads();   // the previous pass's rows have been stored
+  __attribute__((address_space(3))) char* ols = wls + wave * (AQ_WT * AQ_OSTRIDE);
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+  for (int p = 0; p < AQ_PASSES; ++p) {
+    const int n0 = n_begin + 64 * p + 16 * wave;
+    if (n0 >= n_end) break;   // wave-uniform
+    f32x4 acc[AQ_COLS / 16] = {};
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < D_NOPE / 32; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < D_NOPE / 32; ++ks) acc = mfma16x16x32(af[cb][ks], bq[tb][ks], acc);
-        // lane holds columns 32 wave + 16 cb + 4 g + i (i = 0..3) of token 16 tb + c of the pass
-        const u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-        *(__attribute__((address_space(3))) u32x2*)(ols + (16 * tb + c) * AQ_OSTRIDE +
-                                                     (32 * wave + 16 * cb + 4 * g) * 2) = out;
-      }
-    }
-    __syncthreads();
-    // 32 tokens x 16 chunks of 16 bytes: chunk k = 16 t + piece, two per
-    // thread. Rows past the last token hold that token's outputs (its query
-    // row was loaded for them) and are stored over it, unconditionally, with
-    // the same values.
+      for (int cb = 0; cb < AQ_COLS / 16; ++cb) acc[cb] = mfma16x16x32(af[cb][ks], bq[p][ks], acc[cb]);
+    // lane holds columns 16 cb + 4 g + i (i = 0..3) of token n0 + c
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int k = u * 256 + (int)threadIdx.x, t = k >> 4, piece = k & 15;
+    for (int cb = 0; cb < AQ_COLS / 16; ++cb)
+      *(__attribute__((address_space(3))) u32x2*)(ols + c * AQ_OSTRIDE + (16 * cb + 4 * g) * 2) =
+          u32x2{pack_bf16x2(acc[cb][0], acc[cb][1]), pack_bf16x2(acc[cb][2], acc[cb][3])};
+    // The LDS executes one wave's accesses in order: the reads below see the
+    // writes above, and the next pass's writes follow these reads.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 16 tokens x 16 chunks of 16 bytes, four per lane: lanes 16 r .. 16 r + 15 store token 4 u + r
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = 4 * u + g;
       const int n = min(n0 + t, n_end - 1);
-      *(u32x4*)(q_out + ((int64_t)n * H + h) * D_K + c0 + 8 * piece) =
-          *(const __attribute__((address_space(3))) u32x4*)(ols + t * AQ_OSTRIDE + 16 * piece);
+      *(u32x4*)(q_out + ((int64_t)n * H + h) * D_K + c0 + 8 * c) =
+          *(const __attribute__((address_space(3))) u32x4*)(ols + t * AQ_OSTRIDE + 16 * c);
     }
-    if (more) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int ks = 0; ks < D_NOPE / 32; ++ks) bq[tb][ks] = bn[tb][ks];
-    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
