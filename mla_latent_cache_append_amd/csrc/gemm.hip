@@ -242,8 +242,6 @@ hipError_t launch_append_absorb(const uint16_t* c_kv, const uint16_t* k_pe, cons
 }
 
 
-constexpr int OU_ROWS = 64;                 // W_UV rows (output features) per workgroup
-constexpr int OU_CHUNKS = D_V / OU_ROWS;    // 2 workgroups per head
 constexpr int OU_TOK = 32;                  // tokens per pass (two 16-token MFMA blocks)
 constexpr int OU_TPW = 256;                 // tokens per workgroup (runs of a prefill-sized batch)
 __host__ __device__ constexpr int ou_runs(int N) { return (N + OU_TPW - 1) / OU_TPW; }
@@ -254,22 +252,33 @@ __host__ __device__ constexpr int ou_runs(int N) { return (N + OU_TPW - 1) / OU_
 // of a pass are staged once per workgroup in LDS (32 rows x 1 KiB, 16-byte
 // chunk q of row t at slot q ^ (t & 15), so the 16 rows one fragment read
 // covers hit 16 distinct bank groups) instead of being loaded by every wave.
-__global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict__ o_lat,
-                                                     const uint16_t* __restrict__ w_uv,
-                                                     uint16_t* __restrict__ o, int N, int H) {
-  // o_lat rows of a pass, then its outputs (32 tokens x 64 features, rows
-  // padded to 144 bytes) on their way to whole-line stores
+// A workgroup takes OU_ROWS output rows (features) of one head: 64 (two
+// workgroups per head, four waves) when one workgroup per (run, head) would
+// not fill the 256 CUs, as at a decode step; else 128 (eight waves), so the
+// o_lat rows are staged once per head.
+template <int OU_ROWS>
+__global__ __launch_bounds__(4 * OU_ROWS) void out_up_kernel(const uint16_t* __restrict__ o_lat,
+                                                             const uint16_t* __restrict__ w_uv,
+                                                             uint16_t* __restrict__ o, int N, int H) {
+  constexpr int OU_CHUNKS = D_V / OU_ROWS;
+  constexpr int THREADS = 4 * OU_ROWS;
+  // o_lat rows of a pass, then its outputs (32 tokens x OU_ROWS features,
+  // rows padded by 16 bytes) on their way to whole-line stores
   constexpr int OSTRIDE = OU_ROWS * 2 + 16;
   __shared__ __attribute__((aligned(16))) char ol[OU_TOK * D_C * 2 + OU_TOK * OSTRIDE];
   typedef __attribute__((address_space(3))) char lchar;
   lchar* ols = (lchar*)ol;
   lchar* ost = ols + OU_TOK * D_C * 2;
-  // workgroup = (token run, head, half of the head's 128 output rows); the
-  // two halves read the same o_lat rows: ids 8 apart put them on one XCD
-  // (workgroups are dealt to the 8 XCDs round-robin) when the count allows
+  // workgroup = (token run, head, part of the head's 128 output rows); the
+  // two halves of 64 rows read the same o_lat rows: ids 8 apart put them on
+  // one XCD (workgroups are dealt to the 8 XCDs round-robin) when the count
+  // allows
   const int x = blockIdx.x;
   int half, item;
-  if (((H * ou_runs(N)) & 7) == 0) {
+  if (OU_CHUNKS == 1) {
+    half = 0;
+    item = x;
+  } else if (((H * ou_runs(N)) & 7) == 0) {
     half = (x >> 3) & 1;
     item = ((x >> 4) << 3) | (x & 7);
   } else {
@@ -286,12 +295,12 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
   const uint16_t* w = w_uv + ((int64_t)h * D_V + j0 + c) * D_C;
   // 2048 chunks of 16 bytes per pass, eight per thread; rows past the last
   // token repeat a valid row (their outputs are not stored)
-  constexpr int PER = OU_TOK * (D_C / 8) / 256;
+  constexpr int PER = OU_TOK * (D_C / 8) / THREADS;
   u32x4 v[PER];
   auto load_rows = [&](int n0) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int k = u * 256 + threadIdx.x, t = k >> 6, q = k & 63;
+      const int k = u * THREADS + threadIdx.x, t = k >> 6, q = k & 63;
       const int n = min(n0 + t, n_end - 1);
       v[u] = *(const u32x4*)(o_lat + ((int64_t)n * H + h) * D_C + 8 * q);
     }
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
     if (n0 > n_begin) __syncthreads();          // the previous pass has read its rows and stored its outputs
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int k = u * 256 + threadIdx.x, t = k >> 6, q = k & 63;
+      const int k = u * THREADS + threadIdx.x, t = k >> 6, q = k & 63;
       *(__attribute__((address_space(3))) u32x4*)(ols + t * 1024 + ((q ^ (t & 15)) << 4)) = v[u];
     }
     __syncthreads();
@@ -327,10 +336,11 @@ __global__ __launch_bounds__(256) void out_up_kernel(const uint16_t* __restrict_
     }
     __syncthreads();
     {
-      // 32 tokens x 8 chunks of 16 bytes, one per thread: 8 lanes store a token's 128 bytes
-      // (rows past the last token hold that token's outputs and are stored
-      // over it with the same values, so the store is unconditional)
-      const int t = (int)threadIdx.x >> 3, piece = (int)threadIdx.x & 7;
+      // 32 tokens x OU_ROWS / 8 chunks of 16 bytes, one per thread: OU_ROWS / 8
+      // lanes store a token's 2 * OU_ROWS bytes (rows past the last token hold
+      // that token's outputs and are stored over it with the same values, so
+      // the store is unconditional)
+      const int t = (int)threadIdx.x / (OU_ROWS / 8), piece = (int)threadIdx.x % (OU_ROWS / 8);
       const int n = min(n0 + t, n_end - 1);
       *(u32x4*)(o + ((int64_t)n * H + h) * D_V + (hc % OU_CHUNKS) * OU_ROWS + 8 * piece) =
           *(const __attribute__((address_space(3))) u32x4*)(ost + t * OSTRIDE + 16 * piece);
@@ -348,8 +358,10 @@ hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_pe, const i
 
 hipError_t launch_out_up(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int32_t N,
                          int32_t H, hipStream_t stream) {
-  hipLaunchKernelGGL(out_up_kernel, dim3(H * OU_CHUNKS * ou_runs(N)), dim3(256), 0, stream, o_lat, w_uv, o, N,
-                     H);
+  if (H * ou_runs(N) >= 256)
+    hipLaunchKernelGGL(out_up_kernel<128>, dim3(H * ou_runs(N)), dim3(512), 0, stream, o_lat, w_uv, o, N, H);
+  else
+    hipLaunchKernelGGL(out_up_kernel<64>, dim3(H * 2 * ou_runs(N)), dim3(256), 0, stream, o_lat, w_uv, o, N, H);
   return hipGetLastError();
 }
 
