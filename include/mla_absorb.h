@@ -336,6 +336,21 @@ int mla_cache_append_kvpe(const mla_dims* dims, const uint16_t* c_kv, const uint
                           int32_t B, int32_t max_seq, int32_t T, void* stream);
 
 /*
+ * mla_append_absorb_kvpe — mla_cache_append_kvpe and mla_absorb_q of one
+ * decode step in a single launch (as mla_append_absorb for the paged pool):
+ * new token n (c_kv[n], k_pe[n]) goes to [seq_idx[n]][pos[n]] of both
+ * arrays, and query n (q_nope[n], q_pe[n]) is absorbed at position pos[n].
+ * Results are bit-identical to the two separate calls; arguments, layouts,
+ * skipped tokens and errors as there (T = N; N above 2^22 gives
+ * MLA_ERR_UNSUPPORTED). Both parts only read their inputs and write disjoint
+ * outputs.
+ */
+int mla_append_absorb_kvpe(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                           const int32_t* seq_idx, uint16_t* kv_cache, uint16_t* pe_cache, int32_t B,
+                           int32_t max_seq, const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                           const uint16_t* w_uk, uint16_t* q_out, int32_t N, void* stream);
+
+/*
  * mla_decode_attn_kvpe — mla_decode_attn over the two-buffer cache: key t of
  * sequence b is C_t = [kv_cache[b][t] | pe_cache[b][t]] (the V3 reference
  * forms the score as the latent product plus the rope product, [AUDIT] §0).

@@ -254,6 +254,21 @@ int mla_cache_append_kvpe(const mla_dims* dims, const uint16_t* c_kv, const uint
                                                      (double)dims->rope_base, (hipStream_t)stream));
 }
 
+int mla_append_absorb_kvpe(const mla_dims* dims, const uint16_t* c_kv, const uint16_t* k_pe,
+                           const int32_t* seq_idx, uint16_t* kv_cache, uint16_t* pe_cache, int32_t B,
+                           int32_t max_seq, const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                           const uint16_t* w_uk, uint16_t* q_out, int32_t N, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!c_kv || !k_pe || !seq_idx || !kv_cache || !pe_cache || B <= 0 || max_seq <= 0 || !q_nope || !q_pe ||
+      !pos || !w_uk || !q_out || N <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (N > MAX_TOKENS) return MLA_ERR_UNSUPPORTED;
+  return launch_status(mla::launch_append_absorb_kvpe(c_kv, k_pe, seq_idx, kv_cache, pe_cache, B, max_seq, q_nope,
+                                                      q_pe, pos, w_uk, q_out, N, dims->num_heads,
+                                                      (double)dims->rope_base, (hipStream_t)stream));
+}
+
 int mla_decode_attn_kvpe(const mla_dims* dims, const uint16_t* q, const uint16_t* kv_cache,
                          const uint16_t* pe_cache, int32_t max_seq, const int32_t* seq_lens, int32_t B,
                          int32_t Lq, uint16_t* o_lat, float* lse, void* workspace, size_t workspace_bytes,

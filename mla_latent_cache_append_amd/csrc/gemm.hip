@@ -241,6 +241,33 @@ hipError_t launch_append_absorb(const uint16_t* c_kv, const uint16_t* k_pe, cons
   return hipGetLastError();
 }
 
+// The same for the two-buffer cache: the append part writes token j to
+// [seq_idx[j]][pos[j]] of kv_cache and pe_cache (as the two-buffer append
+// kernel), the absorb part is unchanged.
+__global__ __launch_bounds__(256) void append_absorb_kvpe_kernel(
+    const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe, const int32_t* __restrict__ seq_idx,
+    uint16_t* __restrict__ kv_cache, uint16_t* __restrict__ pe_cache, int B, int max_seq,
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe, const int32_t* __restrict__ pos,
+    const uint16_t* __restrict__ w_uk, uint16_t* __restrict__ q_out, int N, int H, RopeFreqs fr) {
+  __shared__ __attribute__((aligned(16))) char wl[AQ_LDS];
+  const int n_absorb = H * AQ_CHUNKS * aq_runs(N);
+  if ((int)blockIdx.x < n_absorb)
+    absorb_q_block(blockIdx.x, wl, q_nope, q_pe, pos, w_uk, q_out, N, H, fr);
+  else
+    append_token_kvpe(((int)blockIdx.x - n_absorb) * 4 + (int)(threadIdx.x >> 6), c_kv, k_pe, pos, seq_idx,
+                      kv_cache, pe_cache, B, max_seq, N, fr);
+}
+
+hipError_t launch_append_absorb_kvpe(const uint16_t* c_kv, const uint16_t* k_pe, const int32_t* seq_idx,
+                                     uint16_t* kv_cache, uint16_t* pe_cache, int32_t B, int32_t max_seq,
+                                     const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                                     const uint16_t* w_uk, uint16_t* q_out, int32_t N, int32_t H, double rope_base,
+                                     hipStream_t stream) {
+  const dim3 grid(H * AQ_CHUNKS * aq_runs(N) + (N + 3) / 4);
+  hipLaunchKernelGGL(append_absorb_kvpe_kernel, grid, dim3(256), 0, stream, c_kv, k_pe, seq_idx, kv_cache, pe_cache,
+                     B, max_seq, q_nope, q_pe, pos, w_uk, q_out, N, H, rope_freqs(rope_base));
+  return hipGetLastError();
+}
 
 constexpr int OU_TOK = 32;                  // tokens per pass (two 16-token MFMA blocks)
 constexpr int OU_TPW = 256;                 // tokens per workgroup (runs of a prefill-sized batch)

@@ -40,6 +40,13 @@ hipError_t launch_append_absorb(const uint16_t* c_kv, const uint16_t* k_pe, cons
                                 const uint16_t* q_pe, const int32_t* pos, const uint16_t* w_uk,
                                 uint16_t* q_out, int32_t N, int32_t H, double rope_base, hipStream_t stream);
 
+// the same into the two-buffer cache: new token n goes to [seq_idx[n]][pos[n]]
+hipError_t launch_append_absorb_kvpe(const uint16_t* c_kv, const uint16_t* k_pe, const int32_t* seq_idx,
+                                     uint16_t* kv_cache, uint16_t* pe_cache, int32_t B, int32_t max_seq,
+                                     const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                                     const uint16_t* w_uk, uint16_t* q_out, int32_t N, int32_t H, double rope_base,
+                                     hipStream_t stream);
+
 hipError_t launch_out_up(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int32_t N,
                          int32_t H, hipStream_t stream);
 

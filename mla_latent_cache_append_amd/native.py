@@ -67,6 +67,8 @@ _SIG = {
                                            _I32, _P, _P, _P, ctypes.c_size_t, _P]),
     "mla_cache_append_kvpe": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                              _P]),
+    "mla_append_absorb_kvpe": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P,
+                                              _P, _P, _I32, _P]),
     "mla_decode_attn_kvpe": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I32, _P, _I32, _I32, _P, _P,
                                             _P, ctypes.c_size_t, _P]),
     "mla_out_up": (ctypes.c_int, [ctypes.POINTER(MlaDims), _P, _P, _P, _I32, _P]),
@@ -328,6 +330,26 @@ def mla_cache_append_kvpe(dims: MlaDims, c_kv, k_pe, pos, seq_idx, kv_cache, pe_
     _ok("mla_cache_append_kvpe", lib().mla_cache_append_kvpe(
         ctypes.byref(dims), _ptr(c_kv), _ptr(k_pe), _ptr(pos), _ptr(seq_idx), _ptr(kv_cache), _ptr(pe_cache),
         kv_cache.shape[0], kv_cache.shape[1], T, _stream(stream)))
+
+
+def mla_append_absorb_kvpe(dims: MlaDims, c_kv, k_pe, seq_idx, kv_cache, pe_cache, q_nope, q_pe, pos, w_uk,
+                           q_out, stream=None):
+    """Append the N new tokens into the two-buffer cache and absorb the N
+    queries of the same tokens in one launch."""
+    N, H = q_nope.shape[0], dims.num_heads
+    _check("c_kv", c_kv, torch.bfloat16, (N, D_C))
+    _check("k_pe", k_pe, torch.bfloat16, (N, D_ROPE))
+    _check("seq_idx", seq_idx, torch.int32, (N,))
+    _check("q_nope", q_nope, torch.bfloat16, (N, H, D_NOPE))
+    _check("q_pe", q_pe, torch.bfloat16, (N, H, D_ROPE))
+    _check("pos", pos, torch.int32, (N,))
+    _check("w_uk", w_uk, torch.bfloat16, (H, D_NOPE, D_C))
+    _check("q_out", q_out, torch.bfloat16, (N, H, D_K))
+    _check_kvpe(kv_cache, pe_cache)
+    _ok("mla_append_absorb_kvpe", lib().mla_append_absorb_kvpe(
+        ctypes.byref(dims), _ptr(c_kv), _ptr(k_pe), _ptr(seq_idx), _ptr(kv_cache), _ptr(pe_cache),
+        kv_cache.shape[0], kv_cache.shape[1], _ptr(q_nope), _ptr(q_pe), _ptr(pos), _ptr(w_uk), _ptr(q_out), N,
+        _stream(stream)))
 
 
 def mla_decode_attn_kvpe(dims: MlaDims, q, kv_cache, pe_cache, seq_lens, Lq: int, o_lat, lse=None,

@@ -116,14 +116,17 @@ class DecodeStep:
 
     def __call__(self, c_kv, k_pe, q_nope, q_pe, q_pos, slots):
         """Append the N new tokens (row n = b*Lq + i at position q_pos[n]), then
-        attend: append and absorb share one launch (two launches for the
-        two-buffer cache), then attention and out_up."""
-        if self.pe_cache is not None or self.form == "expanded":
+        attend: append and absorb share one launch, then attention and out_up."""
+        if self.form == "expanded":
             self.append(c_kv, k_pe, q_pos, slots)
             self.attend(q_nope, q_pe, q_pos)
             return self.o
-        nat.mla_append_absorb(self.dims, c_kv, k_pe, slots, self.pool, q_nope, q_pe, q_pos, self.w_uk, self.q,
-                              pool_scale=self.pool_scale)
+        if self.pe_cache is not None:
+            nat.mla_append_absorb_kvpe(self.dims, c_kv, k_pe, slots, self.pool, self.pe_cache, q_nope, q_pe, q_pos,
+                                       self.w_uk, self.q)
+        else:
+            nat.mla_append_absorb(self.dims, c_kv, k_pe, slots, self.pool, q_nope, q_pe, q_pos, self.w_uk, self.q,
+                                  pool_scale=self.pool_scale)
         self.decode_attn()
         nat.mla_out_up(self.dims, self.o_lat, self.w_uv, self.o)
         return self.o

@@ -201,6 +201,13 @@ static void test_kvpe() {
            MLA_OK);
     EXPECT(mla_cache_append_kvpe(&d, ckv.p(), kpe.p(), pos.p(), sidx.p(), kv.p(), pe.p(), 0, max_seq, T, nullptr) ==
            MLA_ERR_INVALID_ARG);
+    {
+      Buf<uint16_t> qn((size_t)T * H * 128), qp((size_t)T * H * 64), wuk((size_t)H * 128 * 512), qo((size_t)T * H * 576);
+      EXPECT(mla_append_absorb_kvpe(&d, ckv.p(), kpe.p(), sidx.p(), kv.p(), pe.p(), B, max_seq, qn.p(), qp.p(), pos.p(),
+                                    wuk.p(), qo.p(), T, nullptr) == MLA_OK);
+      EXPECT(mla_append_absorb_kvpe(&d, ckv.p(), kpe.p(), sidx.p(), kv.p(), nullptr, B, max_seq, qn.p(), qp.p(),
+                                    pos.p(), wuk.p(), qo.p(), T, nullptr) == MLA_ERR_INVALID_ARG);
+    }
     const int32_t L[B] = {100, 0, 250};  // the last one above max_seq
     for (int b = 0; b < B; ++b) lens.p()[b] = L[b];
     const size_t need = mla_decode_workspace_size(&d, B, Lq);

@@ -116,6 +116,17 @@ hipError_t launch_append_absorb(const uint16_t* c_kv, const uint16_t* k_pe, cons
   return launch_absorb_q(q_nope, q_pe, pos, w_uk, q_out, N, H, rope_base, stream);
 }
 
+hipError_t launch_append_absorb_kvpe(const uint16_t* c_kv, const uint16_t* k_pe, const int32_t* seq_idx,
+                                     uint16_t* kv_cache, uint16_t* pe_cache, int32_t B, int32_t max_seq,
+                                     const uint16_t* q_nope, const uint16_t* q_pe, const int32_t* pos,
+                                     const uint16_t* w_uk, uint16_t* q_out, int32_t N, int32_t H, double rope_base,
+                                     hipStream_t stream) {
+  const hipError_t e = launch_cache_append_kvpe(c_kv, k_pe, pos, seq_idx, kv_cache, pe_cache, B, max_seq, N,
+                                                rope_base, stream);
+  if (e != hipSuccess) return e;
+  return launch_absorb_q(q_nope, q_pe, pos, w_uk, q_out, N, H, rope_base, stream);
+}
+
 hipError_t launch_out_up(const uint16_t* o_lat, const uint16_t* w_uv, uint16_t* o, int32_t N, int32_t H,
                          hipStream_t) {
   touch_read(o_lat, (size_t)N * H * D_C);

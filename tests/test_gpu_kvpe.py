@@ -218,3 +218,49 @@ def test_append_skips_outside_the_buffers():
     written = (kv != 0).any(dim=2)
     assert written.sum().item() == 1 and bool(written[1, 3])
     assert bool((pe != 0).any(dim=2)[1, 3]) and (pe != 0).any(dim=2).sum().item() == 1
+
+
+@pytest.mark.parametrize("H,lens,max_seq", [(128, [700, 33, 1500, 64], 1600), (16, [300, 1, 129, 64, 65], 320)],
+                         ids=lambda v: str(v))
+def test_fused_append_absorb_equals_separate_calls(H, lens, max_seq):
+    """mla_append_absorb_kvpe (append into both arrays and absorb in one
+    launch) against mla_cache_append_kvpe + mla_absorb_q from the same
+    starting cache: both arrays and the absorbed queries bit-identical, with
+    one token outside the sequences and one at a position past max_seq
+    (skipped by both)."""
+    from mla_latent_cache_append_amd import native as nat
+    w = workloads.Workload("kvpe_fused", len(lens), H, 1, lens, "contiguous", seed=23)
+    _say(f"two-buffer fused append+absorb: H={H} lens={lens} max_seq={max_seq}")
+    run = KvpeRun(w, max_seq)
+    ckv_n = np.zeros((w.N, 512), np.uint16)
+    kpe_n = np.zeros((w.N, 64), np.uint16)
+    for b in range(w.B):
+        ckv, kpe = w.seq_cache(b)
+        ckv_n[b], kpe_n[b] = ckv[-1], kpe[-1]
+    pos_n = w.query_positions().copy()
+    seq_n = np.arange(w.B, dtype=np.int32)
+    seq_n[1] = -1               # outside the sequences: skipped
+    pos_n[2] = max_seq          # past the buffers: skipped
+    ckv_d, kpe_d = hz.to_dev(ckv_n), hz.to_dev(kpe_n)
+    pos_d, seq_d = torch.from_numpy(pos_n.astype(np.int32)).cuda(), torch.from_numpy(seq_n).cuda()
+    q_nope, q_pe = w.queries(0)
+    qn, qp = hz.to_dev(q_nope), hz.to_dev(q_pe)
+    kv0, pe0 = run.kv.clone(), run.pe.clone()
+    nat.mla_cache_append_kvpe(run.dims, ckv_d, kpe_d, pos_d, seq_d, run.kv, run.pe)
+    nat.mla_absorb_q(run.dims, qn, qp, pos_d, run.w_uk, run.q)
+    torch.cuda.synchronize()
+    sep_kv, sep_pe, sep_q = run.kv.clone(), run.pe.clone(), run.q.clone()
+    run.kv.copy_(kv0)
+    run.pe.copy_(pe0)
+    run.q.fill_(float("nan"))
+    nat.mla_append_absorb_kvpe(run.dims, ckv_d, kpe_d, seq_d, run.kv, run.pe, qn, qp, pos_d, run.w_uk, run.q)
+    torch.cuda.synchronize()
+    assert torch.equal(run.q.view(torch.int16), sep_q.view(torch.int16))
+    assert torch.equal(run.kv.view(torch.int16), sep_kv.view(torch.int16))
+    assert torch.equal(run.pe.view(torch.int16), sep_pe.view(torch.int16))
+    # written rows: the valid new tokens' only
+    changed = ((run.kv.view(torch.int16) != kv0.view(torch.int16)).any(dim=2)
+               | (run.pe.view(torch.int16) != pe0.view(torch.int16)).any(dim=2)).nonzero().cpu().numpy()
+    expect = {(b, int(pos_n[b])) for b in range(w.B) if b not in (1, 2)}
+    assert {(int(b), int(p)) for b, p in changed} <= expect
+    print("  both arrays and the queries bit-identical to the separate calls", flush=True)

@@ -181,6 +181,13 @@ def test_fused_append_absorb_checks_arguments_on_the_host(nat):
                                  null) == nat.MLA_ERR_INVALID_ARG
     assert lib.mla_append_absorb_fp8(ctypes.byref(d), fake, fake, fake, fake, null, 4, fake, fake, fake, fake,
                                      fake, 2, null) == nat.MLA_ERR_INVALID_ARG
+    # two-buffer cache: null pe_cache, B = 0, N beyond 2^22
+    assert lib.mla_append_absorb_kvpe(ctypes.byref(d), fake, fake, fake, fake, null, 2, 8, fake, fake, fake, fake,
+                                      fake, 2, null) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_absorb_kvpe(ctypes.byref(d), fake, fake, fake, fake, fake, 0, 8, fake, fake, fake, fake,
+                                      fake, 2, null) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_absorb_kvpe(ctypes.byref(d), fake, fake, fake, fake, fake, 2, 8, fake, fake, fake, fake,
+                                      fake, (1 << 22) + 1, null) == nat.MLA_ERR_UNSUPPORTED
     d.block_size = 32
     assert lib.mla_append_absorb(ctypes.byref(d), fake, fake, fake, fake, 4, fake, fake, fake, fake, fake, 2,
                                  null) == nat.MLA_ERR_UNSUPPORTED
