@@ -1,9 +1,11 @@
 """absorb_q and out_up at prefill-sized token counts: the tokens are cut into
-256-token runs, each on its own workgroups, with the next 32-token pass
-prefetched and the outputs staged through LDS. Token counts that end inside a
-run and inside a pass check the tails; sampled tokens at run and pass edges
-are compared with the oracle (the per-head products of [AUDIT] §2.2 and §2.3),
-and every output element must have been written."""
+256-token runs, each on its own workgroups (absorb: each wave on its own
+16-token passes, the rope rows of a run dealt 64 to a workgroup; out_up:
+64- or 128-row workgroups by grid size), the outputs staged through LDS.
+Token counts that end inside a run and inside a pass check the tails, head
+counts below and above 8 the rope dealing; sampled tokens at run and pass
+edges are compared with the oracle (the per-head products of [AUDIT] §2.2
+and §2.3), and every output element must have been written."""
 
 import numpy as np
 import pytest
@@ -24,8 +26,9 @@ def _lib():
     native.lib()
 
 
-# (300, 21): 21 heads x 2 runs is not a multiple of 8, the plain workgroup order (no XCD grouping)
-@pytest.mark.parametrize("N,H", [(2085, 128), (257, 128), (256, 16), (300, 21)])
+# (300, 21) and (513, 7): heads x runs not a multiple of 8, the plain workgroup order (no XCD grouping);
+# (513, 7): rope rows of a workgroup span several tokens; (1000, 24): four runs, the last one partial
+@pytest.mark.parametrize("N,H", [(2085, 128), (257, 128), (256, 16), (300, 21), (513, 7), (1000, 24)])
 def test_absorb_and_out_up_in_token_runs(N, H):
     from mla_latent_cache_append_amd import native as nat
     print(f"\n[case] absorb_q / out_up N={N} H={H}", flush=True)
