@@ -29,6 +29,13 @@
  *     head_dim_k = 576; [TRACE] §3.1 the [B,T,576] projection).
  *   - A token at absolute position p of sequence b lives at slot
  *     block_table[b][p / 64] * 64 + p % 64.
+ *   - Alignment: the kernels move rows with 16-byte vector accesses. The
+ *     append, absorb and up-projection calls (and their fused and _fp8 /
+ *     _kvpe variants) return MLA_ERR_INVALID_ARG unless c_kv, the pool (or
+ *     kv_cache, or the FP8 codes and scales), q_nope, W_UK, the absorbed
+ *     queries, o_lat, W_UV and o are 16-byte aligned, k_pe, q_pe, pos,
+ *     seq_idx and pe_cache 4-byte aligned and slot_mapping 8-byte aligned;
+ *     the attention calls state theirs.
  */
 #ifndef MLA_ABSORB_H
 #define MLA_ABSORB_H

@@ -1,5 +1,6 @@
 // C ABI of libmla_absorb: argument checks on the host, then kernel launches on
 // the caller's stream. Declarations and their contracts: include/mla_absorb.h.
+#include <initializer_list>
 #include "mla_absorb.h"
 
 #include <math.h>
@@ -51,6 +52,18 @@ bool attn_aligned(const void* q, const void* pool, const void* pool_scale, const
          aligned(lse, 4) && aligned(workspace, 16);
 }
 
+// The append, absorb and up-projection kernels move bf16 rows (and FP8 code
+// rows) with 16-byte vector accesses, rope pairs and int32 indices with 4-byte
+// ones and slot numbers with 8-byte ones.
+bool rows_aligned(std::initializer_list<const void*> p16, std::initializer_list<const void*> p4,
+                  const void* p8 = nullptr) {
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return false;
+  for (const void* p : p4)
+    if (!aligned(p, 4)) return false;
+  return aligned(p8, 8);
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,6 +98,7 @@ int mla_cache_append(const mla_dims* dims, const uint16_t* c_kv, const uint16_t*
   if (st != MLA_OK) return st;
   if (!c_kv || !k_pe || !pos || !slot_mapping || !pool || num_blocks <= 0 || T <= 0)
     return MLA_ERR_INVALID_ARG;
+  if (!rows_aligned({c_kv, pool}, {k_pe, pos}, slot_mapping)) return MLA_ERR_INVALID_ARG;
   return launch_status(mla::launch_cache_append(c_kv, k_pe, pos, slot_mapping, pool, num_blocks, T,
                                                 (double)dims->rope_base, (hipStream_t)stream));
 }
@@ -95,6 +109,7 @@ int mla_absorb_q(const mla_dims* dims, const uint16_t* q_nope, const uint16_t* q
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (!q_nope || !q_pe || !pos || !w_uk || !q_out || N <= 0) return MLA_ERR_INVALID_ARG;
+  if (!rows_aligned({q_nope, w_uk, q_out}, {q_pe, pos})) return MLA_ERR_INVALID_ARG;
   if (N > MAX_TOKENS) return MLA_ERR_UNSUPPORTED;
   return launch_status(mla::launch_absorb_q(q_nope, q_pe, pos, w_uk, q_out, N, dims->num_heads,
                                             (double)dims->rope_base, (hipStream_t)stream));
@@ -187,6 +202,7 @@ int mla_append_absorb(const mla_dims* dims, const uint16_t* c_kv, const uint16_t
   if (!c_kv || !k_pe || !slot_mapping || !pool || num_blocks <= 0 || !q_nope || !q_pe || !pos || !w_uk ||
       !q_out || N <= 0)
     return MLA_ERR_INVALID_ARG;
+  if (!rows_aligned({c_kv, pool, q_nope, w_uk, q_out}, {k_pe, q_pe, pos}, slot_mapping)) return MLA_ERR_INVALID_ARG;
   if (N > MAX_TOKENS) return MLA_ERR_UNSUPPORTED;
   return launch_status(mla::launch_append_absorb(c_kv, k_pe, slot_mapping, pool, nullptr, num_blocks, q_nope,
                                                  q_pe, pos, w_uk, q_out, N, dims->num_heads,
@@ -203,6 +219,8 @@ int mla_append_absorb_fp8(const mla_dims* dims, const uint16_t* c_kv, const uint
   if (!c_kv || !k_pe || !slot_mapping || !pool8 || !pool_scale || num_blocks <= 0 || !q_nope || !q_pe ||
       !pos || !w_uk || !q_out || N <= 0)
     return MLA_ERR_INVALID_ARG;
+  if (!rows_aligned({c_kv, pool8, pool_scale, q_nope, w_uk, q_out}, {k_pe, q_pe, pos}, slot_mapping))
+    return MLA_ERR_INVALID_ARG;
   if (N > MAX_TOKENS) return MLA_ERR_UNSUPPORTED;
   return launch_status(mla::launch_append_absorb(c_kv, k_pe, slot_mapping, pool8, pool_scale, num_blocks,
                                                  q_nope, q_pe, pos, w_uk, q_out, N, dims->num_heads,
@@ -216,6 +234,7 @@ int mla_cache_append_fp8(const mla_dims* dims, const uint16_t* c_kv, const uint1
   if (st != MLA_OK) return st;
   if (!c_kv || !k_pe || !pos || !slot_mapping || !pool8 || !pool_scale || num_blocks <= 0 || T <= 0)
     return MLA_ERR_INVALID_ARG;
+  if (!rows_aligned({c_kv, pool8, pool_scale}, {k_pe, pos}, slot_mapping)) return MLA_ERR_INVALID_ARG;
   return launch_status(mla::launch_cache_append_fp8(c_kv, k_pe, pos, slot_mapping, pool8, pool_scale,
                                                     num_blocks, T, (double)dims->rope_base,
                                                     (hipStream_t)stream));
@@ -250,6 +269,7 @@ int mla_cache_append_kvpe(const mla_dims* dims, const uint16_t* c_kv, const uint
   if (st != MLA_OK) return st;
   if (!c_kv || !k_pe || !pos || !seq_idx || !kv_cache || !pe_cache || B <= 0 || max_seq <= 0 || T <= 0)
     return MLA_ERR_INVALID_ARG;
+  if (!rows_aligned({c_kv, kv_cache}, {k_pe, pos, seq_idx, pe_cache})) return MLA_ERR_INVALID_ARG;
   return launch_status(mla::launch_cache_append_kvpe(c_kv, k_pe, pos, seq_idx, kv_cache, pe_cache, B, max_seq, T,
                                                      (double)dims->rope_base, (hipStream_t)stream));
 }
@@ -262,6 +282,8 @@ int mla_append_absorb_kvpe(const mla_dims* dims, const uint16_t* c_kv, const uin
   if (st != MLA_OK) return st;
   if (!c_kv || !k_pe || !seq_idx || !kv_cache || !pe_cache || B <= 0 || max_seq <= 0 || !q_nope || !q_pe ||
       !pos || !w_uk || !q_out || N <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!rows_aligned({c_kv, kv_cache, q_nope, w_uk, q_out}, {k_pe, pos, seq_idx, pe_cache, q_pe}))
     return MLA_ERR_INVALID_ARG;
   if (N > MAX_TOKENS) return MLA_ERR_UNSUPPORTED;
   return launch_status(mla::launch_append_absorb_kvpe(c_kv, k_pe, seq_idx, kv_cache, pe_cache, B, max_seq, q_nope,
@@ -292,6 +314,7 @@ int mla_out_up(const mla_dims* dims, const uint16_t* o_lat, const uint16_t* w_uv
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (!o_lat || !w_uv || !o || N <= 0) return MLA_ERR_INVALID_ARG;
+  if (!rows_aligned({o_lat, w_uv, o}, {})) return MLA_ERR_INVALID_ARG;
   if (N > MAX_TOKENS) return MLA_ERR_UNSUPPORTED;
   return launch_status(
       mla::launch_out_up(o_lat, w_uv, o, N, dims->num_heads, (hipStream_t)stream));

@@ -170,6 +170,24 @@ def test_size_limits_return_unsupported(nat):
                                null) == nat.MLA_ERR_UNSUPPORTED
 
 
+def test_row_calls_reject_misaligned_pointers(nat):
+    """The append, absorb and up-projection calls move rows with 16-byte
+    vector accesses: a misaligned row pointer is refused before any launch."""
+    lib = nat.lib()
+    d = nat.mla_dims_default(16)
+    P = ctypes.c_void_p
+    a, m2, m4 = P(0x1000), P(0x1002), P(0x1004)
+    assert lib.mla_cache_append(ctypes.byref(d), m4, a, a, a, a, 4, 2, None) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(ctypes.byref(d), a, m2, a, a, a, 4, 2, None) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_cache_append(ctypes.byref(d), a, a, a, m4, a, 4, 2, None) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(ctypes.byref(d), a, a, a, a, m4, 2, None) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_out_up(ctypes.byref(d), a, m4, a, 2, None) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_absorb(ctypes.byref(d), a, a, a, a, 4, m4, a, a, a, a, 2,
+                                 None) == nat.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_absorb_kvpe(ctypes.byref(d), a, a, a, a, m2, 2, 8, a, a, a, a, a, 2,
+                                      None) == nat.MLA_ERR_INVALID_ARG
+
+
 def test_fused_append_absorb_checks_arguments_on_the_host(nat):
     lib = nat.lib()
     d = nat.mla_dims_default(16)
