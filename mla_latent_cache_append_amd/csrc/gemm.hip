@@ -118,6 +118,7 @@ __device__ __forceinline__ void absorb_q_block(
   bf16x8 bq[AQ_PASSES][D_NOPE / 32];
 #pragma unroll
   for (int p = 0; p < AQ_PASSES; ++p) {
+    if (n_begin + 64 * p + 16 * wave >= n_end) break;   // wave-uniform: no tokens from this pass on
     const int n = min(n_begin + 64 * p + 16 * wave + c, n_end - 1);
     const uint16_t* src = q_nope + ((int64_t)n * H + h) * D_NOPE + 8 * g;
 #pragma unroll
